@@ -1,0 +1,243 @@
+"""Benchmark: Engram forward tokens/s on one MI355X, with per-stage roofline fractions.
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over the batch: the hash for every
+layer, then per layer the row gather, the projection and the gate.  The
+inputs are resident in HBM before timing starts.  The timed region issues the
+same four C-ABI calls that engram_forward composes, on one stream, and
+records HIP events between the stages.  Each kernel's average duration
+therefore comes from the timed run itself.  engram_forward is then timed on
+its own for reference.
+
+Prints ONE JSON line: the headline metric, plus `roofline` for the dominant
+kernel (the bf16 MFMA projection), `stages` for every kernel, and
+`cpu_baseline` (the CPU oracle, timed on a bounded sample).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Engram forward tokens/s at T=8192 (1 GPU); % HBM roofline gather+gate, % MFMA GEMM"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published (no sparsity)
+CPU_SAMPLE_TOKENS = 2048       # one whole 2048-token sequence of the workload
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic(spec, token_mask) -> dict:
+    """Bytes (or FLOP) each stage must move per call, from the method's sizes."""
+    T, L, cols, hc, dim = spec.T, len(spec.layer_ids), spec.cols, spec.hc, spec.dim
+    live = T if token_mask is None else int((token_mask != 0).sum())
+    row_bytes = 84 if spec.fmt == "q2k" else 256 + 8
+    per_tok_rows = cols * 4 + cols * row_bytes + cols * 256 * 2
+    per_live_gate = 2 * hc * dim * 4 + (hc + 1) * dim * 2
+    mask_bytes = 0 if token_mask is None else T
+    return {
+        "hash": T * 4 + T * L * cols * 4,
+        "rows": T * per_tok_rows,                 # per layer
+        "project": 2.0 * T * spec.K * spec.N,     # FLOP per layer
+        "gate": live * per_live_gate + mask_bytes,  # per layer
+        "rows_per_token": per_tok_rows,
+        "gate_per_token": per_live_gate,
+    }
+
+
+def cpu_baseline(wl) -> dict:
+    """The oracle, as it stands, on the first CPU_SAMPLE_TOKENS tokens (one sequence)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    s = wl.spec
+    n = min(CPU_SAMPLE_TOKENS, s.T)
+    cu = np.array([0, n], dtype=np.int32)
+    sl = slice(0, n)
+    t0 = time.perf_counter()
+    oracle.forward(wl.h[sl], wl.cids[sl], cu, wl.hash_params, [l.as_dict() for l in wl.layers],
+                   s.eps, s.clamp, s.dot_scale,
+                   doc_ids=None if wl.doc_ids is None else wl.doc_ids[sl],
+                   token_mask=None if wl.token_mask is None else wl.token_mask[sl])
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} tokens (one sequence) of the {s.name} workload, whole "
+                      f"forward (hash, rows, projection, gate) in float64 numpy; {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the Engram forward here runs on a single "
+              "MI355X with no sharding or collectives (--gpus 1).", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads
+    from workloads.device import to_device
+    from gram_hash_memory_amd.build import LIB, build
+    if not os.path.exists(LIB):
+        build()
+    import gram_hash_memory_amd as eg
+
+    t0 = time.perf_counter()
+    wl = workloads.make_workload(args.config)
+    s = wl.spec
+    log(f"bench: inputs for config {args.config} ({s.name}) built in {time.perf_counter()-t0:.1f} s")
+    torch.cuda.set_device(0)
+    dw = to_device(wl, "cuda")
+    stream = torch.cuda.current_stream()
+    L = len(s.layer_ids)
+    fmt = eg.ENGRAM_ROWS_Q2K if s.fmt == "q2k" else eg.ENGRAM_ROWS_FP8_E4M3_E8M0
+    params = eg.HashParams.from_dict(wl.hash_params)
+    tokens = eg.Tokens(dw.cids, dw.cu_seqlens, dw.doc_ids, dw.token_mask, dw.lookback,
+                       dw.lookback_live)
+    layers = [eg.Layer(fmt, l.table, l.scales, l.wkv, l.q_weight, l.k_weight, s.hc, s.dim,
+                       s.cols) for l in dw.layers]
+    h = dw.h
+    ids = torch.empty((s.T, L, s.cols), dtype=torch.int32, device="cuda")
+    rows = torch.empty((s.T, s.K), dtype=torch.int16, device="cuda")
+    kv = torch.empty((s.T, s.N), dtype=torch.int16, device="cuda")
+    num_rows = [l.table.numel() // (84 if fmt == eg.ENGRAM_ROWS_Q2K else 256) for l in dw.layers]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        eg.engram_hash(params, tokens, ids, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        for l, dl in enumerate(dw.layers):
+            eg.engram_rows(fmt, dl.table, dl.scales, num_rows[l], ids.view(-1)[l * s.cols:],
+                           L * s.cols, s.cols, s.T, rows, None, stream)
+            if ev is not None:
+                ev[2 + 3 * l].record(stream)
+            eg.engram_project(rows, dl.wkv, kv, s.T, s.K, s.N, stream)
+            if ev is not None:
+                ev[3 + 3 * l].record(stream)
+            eg.engram_gate(h, kv, dl.q_weight, dl.k_weight, dw.token_mask, s.T, s.hc, s.dim,
+                           s.eps, s.clamp, s.dot_scale, stream)
+            if ev is not None:
+                ev[4 + 3 * l].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"bench: {args.warmup} warmup steps done; timing {args.steps} steps")
+
+    n_ev = 2 + 3 * L
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+
+    dur = {"hash": 0.0, "rows": 0.0, "project": 0.0, "gate": 0.0}
+    for ev in events:
+        dur["hash"] += ev[0].elapsed_time(ev[1])
+        for l in range(L):
+            dur["rows"] += ev[1 + 3 * l].elapsed_time(ev[2 + 3 * l])
+            dur["project"] += ev[2 + 3 * l].elapsed_time(ev[3 + 3 * l])
+            dur["gate"] += ev[3 + 3 * l].elapsed_time(ev[4 + 3 * l])
+    per_launch_ms = {"hash": dur["hash"] / args.steps}
+    for k in ("rows", "project", "gate"):
+        per_launch_ms[k] = dur[k] / (args.steps * L)
+
+    # engram_forward itself (same kernels), for reference
+    ws = torch.empty(eg.engram_workspace_bytes(s.T, L, s.cols, s.hc, s.dim), dtype=torch.uint8,
+                     device="cuda")
+    fe0, fe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    eg.engram_forward(params, tokens, layers, h, s.hc, s.dim, s.eps, s.clamp, s.dot_scale, ws,
+                      None, stream)
+    fe0.record(stream)
+    n_fwd = max(3, args.steps // 2)
+    for _ in range(n_fwd):
+        eg.engram_forward(params, tokens, layers, h, s.hc, s.dim, s.eps, s.clamp, s.dot_scale,
+                          ws, None, stream)
+    fe1.record(stream)
+    torch.cuda.synchronize()
+    forward_ms = fe0.elapsed_time(fe1) / n_fwd
+
+    alg = algorithmic(s, wl.token_mask)
+    gemm_tflops = alg["project"] / (per_launch_ms["project"] * 1e-3) / 1e12
+    rows_gbs = alg["rows"] / (per_launch_ms["rows"] * 1e-3) / 1e9
+    gate_gbs = alg["gate"] / (per_launch_ms["gate"] * 1e-3) / 1e9
+    hash_gbs = alg["hash"] / (per_launch_ms["hash"] * 1e-3) / 1e9
+    gg_bytes = alg["rows"] + alg["gate"]
+    gg_ms = per_launch_ms["rows"] + per_launch_ms["gate"]
+    gg_gbs = gg_bytes / (gg_ms * 1e-3) / 1e9
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    result = {
+        "metric": METRIC,
+        "value": s.T * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{s.name}: T={s.T} ({len(s.seq_lens)}x{s.seq_lens[0]}), "
+                               f"{L} layer(s), {s.cols} cols, {s.fmt} table "
+                               f"{s.num_rows} rows, dim={s.dim}, hc={s.hc}, "
+                               f"{s.id_dist} ids",
+                   "T": s.T, "K": s.K, "N": s.N, "row_format": s.fmt},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "gemm_nt_kernel (engram_project)",
+                     "per_launch_ms": round(per_launch_ms["project"], 4)},
+        "stages": {
+            "hash": {"ms": round(per_launch_ms["hash"], 4), "bound": "alu",
+                     "hbm_gbs": round(hash_gbs, 1)},
+            "rows": {"ms": round(per_launch_ms["rows"], 4), "bound": "hbm",
+                     "achieved_gbs": round(rows_gbs, 1),
+                     "frac": round(rows_gbs / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": alg["rows"]},
+            "project": {"ms": round(per_launch_ms["project"], 4), "bound": "mfma",
+                        "achieved_tflops": round(gemm_tflops, 1),
+                        "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4)},
+            "gate": {"ms": round(per_launch_ms["gate"], 4), "bound": "hbm",
+                     "achieved_gbs": round(gate_gbs, 1),
+                     "frac": round(gate_gbs / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": alg["gate"]},
+            "gather_plus_gate": {"ms": round(gg_ms, 4), "achieved_gbs": round(gg_gbs, 1),
+                                 "frac": round(gg_gbs / HBM_PEAK_GBS, 4)},
+            "engram_forward_ms": round(forward_ms, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

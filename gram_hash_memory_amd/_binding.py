@@ -1,0 +1,229 @@
+"""ctypes binding of libengram.so, with the C entry points' names.
+
+Argument marshalling only: every stage runs in the library's HIP kernels.
+Device buffers are torch tensors on the GPU; the binding passes their data
+pointers and the current torch stream (or the stream given).  Before each
+call it checks that every device tensor is on the GPU, contiguous, of the
+right dtype and large enough for the sizes passed.  The C library cannot see
+buffer sizes, and a short buffer would make a kernel read out of bounds.
+
+The library is loaded after torch, so it binds to the HIP runtime that torch
+already loaded (both name the same soname), and torch streams are valid in it.
+If libengram.so has not been built, importing this module raises ImportError:
+there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import c_char_p, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
+
+import numpy as np
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libengram.so")
+
+ENGRAM_OK, ENGRAM_ERR_ARG, ENGRAM_ERR_UNSUPPORTED, ENGRAM_ERR_HIP = 0, 1, 2, 3
+ENGRAM_ROWS_Q2K, ENGRAM_ROWS_FP8_E4M3_E8M0 = 0, 1
+HEAD_DIM, Q2K_ROW_BYTES, FP8_ROW_BYTES, FP8_SCALE_BYTES = 256, 84, 256, 8
+
+EXPORTS = ("engram_hash", "engram_rows", "engram_project", "engram_gate",
+           "engram_workspace_bytes", "engram_forward", "engram_last_error")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m gram_hash_memory_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class _HashParams(ctypes.Structure):
+    _fields_ = [("n_layers", c_int32), ("max_ngram", c_int32), ("n_heads", c_int32),
+                ("pad_id", c_int32), ("multipliers", c_void_p), ("primes", c_void_p),
+                ("offsets", c_void_p)]
+
+
+class _Tokens(ctypes.Structure):
+    _fields_ = [("T", c_int32), ("n_seqs", c_int32), ("lookback_depth", c_int32),
+                ("cids", c_void_p), ("cu_seqlens", c_void_p), ("doc_ids", c_void_p),
+                ("token_mask", c_void_p), ("lookback", c_void_p), ("lookback_live", c_void_p)]
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [("fmt", c_int), ("num_rows", c_int64), ("table", c_void_p),
+                ("scales", c_void_p), ("wkv", c_void_p), ("q_weight", c_void_p),
+                ("k_weight", c_void_p)]
+
+
+_P = ctypes.POINTER
+_lib.engram_hash.argtypes = [_P(_HashParams), _P(_Tokens), c_void_p, c_void_p]
+_lib.engram_rows.argtypes = [c_int, c_void_p, c_void_p, c_int64, c_void_p, c_int64, c_int32,
+                             c_int32, c_void_p, c_void_p, c_void_p]
+_lib.engram_project.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                c_void_p]
+_lib.engram_gate.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                             c_int32, c_int32, c_float, c_float, c_float, c_void_p]
+_lib.engram_workspace_bytes.argtypes = [c_int32, c_int32, c_int32, c_int32, c_int32]
+_lib.engram_workspace_bytes.restype = c_size_t
+_lib.engram_forward.argtypes = [_P(_HashParams), _P(_Tokens), _P(_Layer), c_void_p, c_int32,
+                                c_int32, c_float, c_float, c_float, c_void_p, c_size_t,
+                                c_void_p, c_void_p]
+_lib.engram_last_error.restype = c_char_p
+for _name in ("engram_hash", "engram_rows", "engram_project", "engram_gate", "engram_forward"):
+    getattr(_lib, _name).restype = c_int
+
+
+class EngramError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"engram status {status}: {message}")
+        self.status = status
+
+
+def engram_last_error() -> str:
+    return (_lib.engram_last_error() or b"").decode()
+
+
+def _check(status: int) -> None:
+    if status != ENGRAM_OK:
+        raise EngramError(status, engram_last_error())
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _dptr(t, dtype, min_numel: int = 0, name: str = "tensor"):
+    """Device pointer of a contiguous GPU tensor with at least min_numel elements."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {min_numel}")
+    return t.data_ptr()
+
+
+class HashParams:
+    """engram_hash_params: host tables, kept alive as long as this object."""
+
+    def __init__(self, multipliers, primes, offsets, max_ngram: int, n_heads: int, pad_id: int):
+        self.multipliers = np.ascontiguousarray(multipliers, dtype=np.int64)
+        self.primes = np.ascontiguousarray(primes, dtype=np.int64)
+        self.offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+        self.n_layers = int(self.primes.shape[0])
+        self.max_ngram, self.n_heads, self.pad_id = int(max_ngram), int(n_heads), int(pad_id)
+        self.cols = (self.max_ngram - 1) * self.n_heads
+        if self.multipliers.shape != (self.n_layers, self.max_ngram) or \
+                self.primes.shape != (self.n_layers, self.cols) or \
+                self.offsets.shape != (self.n_layers, self.cols):
+            raise ValueError("hash table shapes do not match n_layers/max_ngram/n_heads")
+        self.c = _HashParams(self.n_layers, self.max_ngram, self.n_heads, self.pad_id,
+                             self.multipliers.ctypes.data, self.primes.ctypes.data,
+                             self.offsets.ctypes.data)
+
+    @classmethod
+    def from_dict(cls, d: dict) -> "HashParams":
+        return cls(d["multipliers"], d["primes"], d["offsets"], d["max_ngram"], d["n_heads"],
+                   d["pad_id"])
+
+
+class Tokens:
+    """engram_tokens over GPU tensors (kept alive as long as this object)."""
+
+    def __init__(self, cids, cu_seqlens, doc_ids=None, token_mask=None, lookback=None,
+                 lookback_live=None):
+        self.T = int(cids.numel())
+        self.n_seqs = int(cu_seqlens.numel()) - 1
+        self.depth = 0 if lookback is None else int(lookback.shape[1])
+        if lookback is not None and lookback.shape[0] != self.n_seqs:
+            raise ValueError("lookback must have one row per sequence")
+        self._keep = (cids, cu_seqlens, doc_ids, token_mask, lookback, lookback_live)
+        self.c = _Tokens(self.T, self.n_seqs, self.depth,
+                         _dptr(cids, torch.int32, self.T, "cids"),
+                         _dptr(cu_seqlens, torch.int32, self.n_seqs + 1, "cu_seqlens"),
+                         _dptr(doc_ids, torch.int32, self.T, "doc_ids"),
+                         _dptr(token_mask, torch.uint8, self.T, "token_mask"),
+                         _dptr(lookback, torch.int32, self.n_seqs * self.depth, "lookback"),
+                         _dptr(lookback_live, torch.uint8, self.n_seqs * self.depth,
+                               "lookback_live"))
+        self.token_mask = token_mask
+
+
+def engram_hash(params: HashParams, tokens: Tokens, ids: torch.Tensor, stream=None) -> None:
+    """Stage 1: ids int32 [T, n_layers, cols] from the token batch."""
+    p = _dptr(ids, torch.int32, tokens.T * params.n_layers * params.cols, "ids")
+    _check(_lib.engram_hash(ctypes.byref(params.c), ctypes.byref(tokens.c), p, _stream(stream)))
+
+
+def engram_rows(fmt: int, table, scales, num_rows: int, ids, ids_token_stride: int, cols: int,
+                T: int, rows, bad_ids=None, stream=None) -> None:
+    """Stage 2: bf16 rows [T, cols*256] (int16 tensor of bf16 bits) from ids."""
+    row_bytes = Q2K_ROW_BYTES if fmt == ENGRAM_ROWS_Q2K else FP8_ROW_BYTES
+    need_ids = 0 if T <= 0 else (T - 1) * ids_token_stride + cols
+    _check(_lib.engram_rows(
+        int(fmt), _dptr(table, torch.uint8, num_rows * row_bytes, "table"),
+        _dptr(scales, torch.uint8, num_rows * FP8_SCALE_BYTES, "scales"), int(num_rows),
+        _dptr(ids, torch.int32, need_ids, "ids"), int(ids_token_stride), int(cols), int(T),
+        _dptr(rows, torch.int16, T * cols * HEAD_DIM, "rows"),
+        _dptr(bad_ids, torch.int32, 1, "bad_ids"), _stream(stream)))
+
+
+def engram_project(rows, wkv, kv, T: int, K: int, N: int, stream=None) -> None:
+    """Stage 3: kv [T, N] = rows [T, K] x wkv [N, K]^T (bf16 bits in int16 tensors)."""
+    _check(_lib.engram_project(_dptr(rows, torch.int16, T * K, "rows"),
+                               _dptr(wkv, torch.int16, N * K, "wkv"),
+                               _dptr(kv, torch.int16, T * N, "kv"), int(T), int(K), int(N),
+                               _stream(stream)))
+
+
+def engram_gate(h, kv, q_weight, k_weight, token_mask, T: int, hc: int, dim: int, eps: float,
+                clamp: float, dot_scale: float, stream=None) -> None:
+    """Stage 4: update fp32 h [T, hc, dim] in place."""
+    _check(_lib.engram_gate(_dptr(h, torch.float32, T * hc * dim, "h"),
+                            _dptr(kv, torch.int16, T * (hc + 1) * dim, "kv"),
+                            _dptr(q_weight, torch.int16, hc * dim, "q_weight"),
+                            _dptr(k_weight, torch.int16, hc * dim, "k_weight"),
+                            _dptr(token_mask, torch.uint8, T, "token_mask"), int(T), int(hc),
+                            int(dim), float(eps), float(clamp), float(dot_scale),
+                            _stream(stream)))
+
+
+def engram_workspace_bytes(T: int, n_layers: int, cols: int, hc: int, dim: int) -> int:
+    return int(_lib.engram_workspace_bytes(T, n_layers, cols, hc, dim))
+
+
+class Layer:
+    """engram_layer over GPU tensors (kept alive as long as this object)."""
+
+    def __init__(self, fmt: int, table, scales, wkv, q_weight, k_weight, hc: int, dim: int,
+                 cols: int):
+        row_bytes = Q2K_ROW_BYTES if fmt == ENGRAM_ROWS_Q2K else FP8_ROW_BYTES
+        self.num_rows = int(table.numel()) // row_bytes
+        self._keep = (table, scales, wkv, q_weight, k_weight)
+        self.c = _Layer(int(fmt), self.num_rows,
+                        _dptr(table, torch.uint8, self.num_rows * row_bytes, "table"),
+                        _dptr(scales, torch.uint8, self.num_rows * FP8_SCALE_BYTES, "scales"),
+                        _dptr(wkv, torch.int16, (hc + 1) * dim * cols * HEAD_DIM, "wkv"),
+                        _dptr(q_weight, torch.int16, hc * dim, "q_weight"),
+                        _dptr(k_weight, torch.int16, hc * dim, "k_weight"))
+
+
+def engram_forward(params: HashParams, tokens: Tokens, layers, h, hc: int, dim: int,
+                   eps: float, clamp: float, dot_scale: float, workspace,
+                   bad_ids=None, stream=None) -> None:
+    """Whole forward on h (fp32 [T, hc, dim], in place); workspace is a uint8 GPU tensor."""
+    if len(layers) != params.n_layers:
+        raise ValueError("one Layer per hashed layer is required")
+    arr = (_Layer * len(layers))(*[l.c for l in layers])
+    need = engram_workspace_bytes(tokens.T, params.n_layers, params.cols, hc, dim)
+    ws = _dptr(workspace, torch.uint8, need, "workspace")
+    _check(_lib.engram_forward(ctypes.byref(params.c), ctypes.byref(tokens.c), arr,
+                               _dptr(h, torch.float32, tokens.T * hc * dim, "h"), int(hc),
+                               int(dim), float(eps), float(clamp), float(dot_scale), ws,
+                               int(workspace.numel()) if workspace is not None else 0,
+                               _dptr(bad_ids, torch.int32, 1, "bad_ids"), _stream(stream)))

@@ -1,0 +1,281 @@
+// C ABI of libengram.so: host-side validation and dispatch (see include/engram.h).
+//
+// Every entry point checks all of its arguments before queuing anything, so
+// ENGRAM_ERR_ARG and ENGRAM_ERR_UNSUPPORTED mean that nothing reached the GPU.
+// ENGRAM_ERR_HIP reports a failed launch; in engram_forward, stages queued
+// before the failing one may still run.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "common.hpp"
+
+namespace {
+
+thread_local char g_error[512] = "";
+
+engram_status fail(engram_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof(g_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+engram_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ENGRAM_OK;
+  return fail(ENGRAM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define REQUIRE(cond, ...)                                   \
+  do {                                                       \
+    if (!(cond)) return fail(ENGRAM_ERR_ARG, __VA_ARGS__);   \
+  } while (0)
+#define REQUIRE_SUP(cond, ...)                                       \
+  do {                                                               \
+    if (!(cond)) return fail(ENGRAM_ERR_UNSUPPORTED, __VA_ARGS__);   \
+  } while (0)
+
+constexpr int64_t kInt32Max = 2147483647;
+
+engram_status check_hash_params(const engram_hash_params *p, engram::HashTables *tab) {
+  REQUIRE(p, "engram_hash_params is NULL");
+  REQUIRE_SUP(p->n_layers >= 1 && p->n_layers <= ENGRAM_MAX_LAYERS,
+              "n_layers=%d outside 1..%d", p->n_layers, ENGRAM_MAX_LAYERS);
+  REQUIRE_SUP(p->max_ngram >= 2 && p->max_ngram <= ENGRAM_MAX_NGRAM,
+              "max_ngram=%d outside 2..%d", p->max_ngram, ENGRAM_MAX_NGRAM);
+  REQUIRE(p->n_heads >= 1, "n_heads=%d < 1", p->n_heads);
+  const int64_t cols = int64_t(p->max_ngram - 1) * p->n_heads;
+  REQUIRE_SUP(cols <= ENGRAM_MAX_COLS, "(max_ngram-1)*n_heads=%lld > %d", (long long)cols,
+              ENGRAM_MAX_COLS);
+  REQUIRE(p->multipliers && p->primes && p->offsets, "hash table pointer is NULL");
+  std::memset(tab, 0, sizeof(*tab));
+  tab->n_layers = p->n_layers;
+  tab->max_ngram = p->max_ngram;
+  tab->n_heads = p->n_heads;
+  tab->pad_id = p->pad_id;
+  for (int l = 0; l < p->n_layers; ++l) {
+    for (int k = 0; k < p->max_ngram; ++k)
+      tab->mult[l][k] = uint64_t(p->multipliers[int64_t(l) * p->max_ngram + k]);
+    for (int c = 0; c < cols; ++c) {
+      const int64_t pr = p->primes[int64_t(l) * cols + c];
+      const int64_t of = p->offsets[int64_t(l) * cols + c];
+      REQUIRE(pr >= 1 && pr <= kInt32Max, "primes[%d][%d]=%lld outside [1, 2^31)", l, c,
+              (long long)pr);
+      REQUIRE(of >= 0 && of + pr <= kInt32Max + 1, "offsets[%d][%d]+primes exceeds 2^31", l,
+              c);
+      tab->prime[l][c] = uint32_t(pr);
+      tab->offset[l][c] = uint32_t(of);
+    }
+  }
+  return ENGRAM_OK;
+}
+
+engram_status check_tokens(const engram_tokens *t, int max_ngram) {
+  REQUIRE(t, "engram_tokens is NULL");
+  REQUIRE(t->T >= 0, "T=%d < 0", t->T);
+  if (t->T == 0) return ENGRAM_OK;
+  REQUIRE(t->n_seqs >= 1, "n_seqs=%d < 1", t->n_seqs);
+  REQUIRE(t->cids && t->cu_seqlens, "cids or cu_seqlens is NULL");
+  REQUIRE(aligned(t->cids, 4) && aligned(t->cu_seqlens, 4), "cids/cu_seqlens misaligned");
+  REQUIRE(!t->doc_ids || aligned(t->doc_ids, 4), "doc_ids misaligned");
+  REQUIRE(t->lookback_depth >= 0 && t->lookback_depth <= max_ngram - 1,
+          "lookback_depth=%d outside 0..max_ngram-1=%d", t->lookback_depth, max_ngram - 1);
+  REQUIRE(!t->lookback || aligned(t->lookback, 4), "lookback misaligned");
+  REQUIRE(!(t->lookback_live && !t->lookback), "lookback_live given without lookback");
+  return ENGRAM_OK;
+}
+
+engram_status check_rows_shape(engram_row_format fmt, int64_t num_rows, int64_t stride,
+                               int32_t cols, int32_t T) {
+  REQUIRE(fmt == ENGRAM_ROWS_Q2K || fmt == ENGRAM_ROWS_FP8_E4M3_E8M0, "unknown row format %d",
+          int(fmt));
+  REQUIRE(T >= 0, "T=%d < 0", T);
+  REQUIRE(cols >= 1, "cols=%d < 1", cols);
+  REQUIRE(num_rows >= 1, "num_rows=%lld < 1", (long long)num_rows);
+  REQUIRE(stride >= cols, "ids_token_stride=%lld < cols=%d", (long long)stride, cols);
+  return ENGRAM_OK;
+}
+
+engram_status check_rows_ptrs(engram_row_format fmt, const uint8_t *table, const uint8_t *scales,
+                              const int32_t *ids, const uint16_t *rows, const int32_t *bad_ids) {
+  REQUIRE(table && ids && rows, "table, ids or rows is NULL");
+  REQUIRE(aligned(ids, 4), "ids misaligned");
+  REQUIRE(aligned(rows, 16), "rows must be 16-byte aligned");
+  REQUIRE(!bad_ids || aligned(bad_ids, 4), "bad_ids misaligned");
+  if (fmt == ENGRAM_ROWS_Q2K) {
+    REQUIRE(aligned(table, 4), "Q2_K table must be 4-byte aligned");
+  } else {
+    REQUIRE(scales, "FP8 rows need scales");
+    REQUIRE(aligned(table, 16), "FP8 table must be 16-byte aligned");
+  }
+  return ENGRAM_OK;
+}
+
+engram_status check_project_shape(int32_t T, int32_t K, int32_t N) {
+  REQUIRE(T >= 0, "T=%d < 0", T);
+  REQUIRE(K > 0 && K % 64 == 0, "K=%d must be a positive multiple of 64", K);
+  REQUIRE(N > 0, "N=%d must be positive", N);
+  return ENGRAM_OK;
+}
+
+engram_status check_project_ptrs(const uint16_t *a, const uint16_t *w, const uint16_t *c) {
+  REQUIRE(a && w && c, "rows, wkv or kv is NULL");
+  REQUIRE(aligned(a, 16) && aligned(w, 16) && aligned(c, 16),
+          "GEMM operands must be 16-byte aligned");
+  return ENGRAM_OK;
+}
+
+engram_status check_gate_shape(int32_t T, int32_t hc, int32_t dim, float eps, float clamp) {
+  REQUIRE(T >= 0, "T=%d < 0", T);
+  REQUIRE_SUP(hc >= 1 && hc <= ENGRAM_MAX_HC, "hc=%d outside 1..%d", hc, ENGRAM_MAX_HC);
+  REQUIRE_SUP(dim >= 8 && dim <= ENGRAM_MAX_DIM && dim % 8 == 0,
+              "dim=%d must be a multiple of 8 in 8..%d", dim, ENGRAM_MAX_DIM);
+  REQUIRE(eps >= 0.f && clamp >= 0.f, "eps and clamp must be >= 0");
+  return ENGRAM_OK;
+}
+
+engram_status check_gate_ptrs(const float *h, const uint16_t *kv, const uint16_t *qw,
+                              const uint16_t *kw) {
+  REQUIRE(h && kv && qw && kw, "h, kv, q_weight or k_weight is NULL");
+  REQUIRE(aligned(h, 16) && aligned(kv, 16) && aligned(qw, 16) && aligned(kw, 16),
+          "gate operands must be 16-byte aligned");
+  return ENGRAM_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+const char *engram_last_error(void) { return g_error; }
+
+engram_status engram_hash(const engram_hash_params *params, const engram_tokens *tokens,
+                          int32_t *ids, hipStream_t stream) {
+  engram::HashTables tab;
+  engram_status st = check_hash_params(params, &tab);
+  if (st != ENGRAM_OK) return st;
+  if ((st = check_tokens(tokens, params->max_ngram)) != ENGRAM_OK) return st;
+  if (tokens->T == 0) return ENGRAM_OK;
+  REQUIRE(ids && aligned(ids, 4), "ids is NULL or misaligned");
+  return hip_status(engram::launch_hash(tab, *tokens, ids, stream), "engram_hash launch");
+}
+
+engram_status engram_rows(engram_row_format fmt, const uint8_t *table, const uint8_t *scales,
+                          int64_t num_rows, const int32_t *ids, int64_t ids_token_stride,
+                          int32_t cols, int32_t T, uint16_t *rows, int32_t *bad_ids,
+                          hipStream_t stream) {
+  engram_status st = check_rows_shape(fmt, num_rows, ids_token_stride, cols, T);
+  if (st != ENGRAM_OK) return st;
+  if (T == 0) return ENGRAM_OK;
+  if ((st = check_rows_ptrs(fmt, table, scales, ids, rows, bad_ids)) != ENGRAM_OK) return st;
+  return hip_status(engram::launch_rows(fmt, table, scales, num_rows, ids, ids_token_stride,
+                                        cols, T, rows, bad_ids, stream),
+                    "engram_rows launch");
+}
+
+engram_status engram_project(const uint16_t *rows, const uint16_t *wkv, uint16_t *kv, int32_t T,
+                             int32_t K, int32_t N, hipStream_t stream) {
+  engram_status st = check_project_shape(T, K, N);
+  if (st != ENGRAM_OK) return st;
+  if (T == 0) return ENGRAM_OK;
+  if ((st = check_project_ptrs(rows, wkv, kv)) != ENGRAM_OK) return st;
+  return hip_status(engram::launch_project(rows, wkv, kv, T, K, N, stream),
+                    "engram_project launch");
+}
+
+engram_status engram_gate(float *h, const uint16_t *kv, const uint16_t *q_weight,
+                          const uint16_t *k_weight, const uint8_t *token_mask, int32_t T,
+                          int32_t hc, int32_t dim, float eps, float clamp, float dot_scale,
+                          hipStream_t stream) {
+  engram_status st = check_gate_shape(T, hc, dim, eps, clamp);
+  if (st != ENGRAM_OK) return st;
+  if (T == 0) return ENGRAM_OK;
+  if ((st = check_gate_ptrs(h, kv, q_weight, k_weight)) != ENGRAM_OK) return st;
+  return hip_status(engram::launch_gate(h, kv, q_weight, k_weight, token_mask, T, hc, dim, eps,
+                                        clamp, dot_scale, stream),
+                    "engram_gate launch");
+}
+
+size_t engram_workspace_bytes(int32_t T, int32_t n_layers, int32_t cols, int32_t hc,
+                              int32_t dim) {
+  if (T < 0 || n_layers < 0 || cols < 0 || hc < 0 || dim < 0) return 0;
+  const size_t t = size_t(T);
+  return align256(t * n_layers * cols * sizeof(int32_t)) +
+         align256(t * cols * ENGRAM_HEAD_DIM * sizeof(uint16_t)) +
+         align256(t * (size_t(hc) + 1) * dim * sizeof(uint16_t));
+}
+
+engram_status engram_forward(const engram_hash_params *params, const engram_tokens *tokens,
+                             const engram_layer *layers, float *h, int32_t hc, int32_t dim,
+                             float eps, float clamp, float dot_scale, void *workspace,
+                             size_t workspace_bytes, int32_t *bad_ids, hipStream_t stream) {
+  engram::HashTables tab;
+  engram_status st = check_hash_params(params, &tab);
+  if (st != ENGRAM_OK) return st;
+  if ((st = check_tokens(tokens, params->max_ngram)) != ENGRAM_OK) return st;
+  REQUIRE(layers, "layers is NULL");
+  const int32_t T = tokens->T, L = params->n_layers;
+  const int32_t cols = (params->max_ngram - 1) * params->n_heads;
+  const int32_t K = cols * ENGRAM_HEAD_DIM;
+  const int64_t N64 = int64_t(hc + 1) * dim;
+  REQUIRE_SUP(N64 <= kInt32Max, "(hc+1)*dim too large");
+  const int32_t N = int32_t(N64);
+  if ((st = check_gate_shape(T, hc, dim, eps, clamp)) != ENGRAM_OK) return st;
+  for (int l = 0; l < L; ++l) {
+    const engram_layer &ly = layers[l];
+    if ((st = check_rows_shape(ly.fmt, ly.num_rows, int64_t(L) * cols, cols, T)) != ENGRAM_OK)
+      return fail(st, "layer %d: %s", l, engram_last_error());
+    int64_t max_row = 0;
+    for (int c = 0; c < cols; ++c)
+      max_row = std::max<int64_t>(max_row, int64_t(tab.offset[l][c]) + tab.prime[l][c]);
+    REQUIRE(max_row <= ly.num_rows, "layer %d: offsets + primes reach row %lld > num_rows %lld",
+            l, (long long)max_row, (long long)ly.num_rows);
+  }
+  if (T == 0) return ENGRAM_OK;
+  const size_t need = engram_workspace_bytes(T, L, cols, hc, dim);
+  REQUIRE(workspace && aligned(workspace, 256), "workspace is NULL or not 256-byte aligned");
+  REQUIRE(workspace_bytes >= need, "workspace_bytes=%zu < required %zu", workspace_bytes, need);
+
+  char *ws = static_cast<char *>(workspace);
+  int32_t *ids = reinterpret_cast<int32_t *>(ws);
+  ws += align256(size_t(T) * L * cols * sizeof(int32_t));
+  uint16_t *rows = reinterpret_cast<uint16_t *>(ws);
+  ws += align256(size_t(T) * K * sizeof(uint16_t));
+  uint16_t *kv = reinterpret_cast<uint16_t *>(ws);
+
+  for (int l = 0; l < L; ++l) {
+    const engram_layer &ly = layers[l];
+    if ((st = check_rows_ptrs(ly.fmt, ly.table, ly.scales, ids, rows, bad_ids)) != ENGRAM_OK ||
+        (st = check_project_ptrs(rows, ly.wkv, kv)) != ENGRAM_OK ||
+        (st = check_gate_ptrs(h, kv, ly.q_weight, ly.k_weight)) != ENGRAM_OK)
+      return fail(st, "layer %d: %s", l, engram_last_error());
+  }
+
+  if ((st = hip_status(engram::launch_hash(tab, *tokens, ids, stream), "hash launch")) !=
+      ENGRAM_OK)
+    return st;
+  for (int l = 0; l < L; ++l) {
+    const engram_layer &ly = layers[l];
+    if ((st = hip_status(engram::launch_rows(ly.fmt, ly.table, ly.scales, ly.num_rows,
+                                             ids + l * cols, int64_t(L) * cols, cols, T, rows,
+                                             bad_ids, stream),
+                         "rows launch")) != ENGRAM_OK)
+      return st;
+    if ((st = hip_status(engram::launch_project(rows, ly.wkv, kv, T, K, N, stream),
+                         "project launch")) != ENGRAM_OK)
+      return st;
+    if ((st = hip_status(engram::launch_gate(h, kv, ly.q_weight, ly.k_weight,
+                                             tokens->token_mask, T, hc, dim, eps, clamp,
+                                             dot_scale, stream),
+                         "gate launch")) != ENGRAM_OK)
+      return st;
+  }
+  return ENGRAM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// Internal declarations shared by the HIP sources of libengram.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "engram.h"
+
+namespace engram {
+
+// ---------------------------------------------------------------- bf16 / vectors
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bits, round to nearest even (gfx950: v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// Two fp32 -> packed bf16 pair (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------- hash params
+
+// Hash tables as kernel arguments (copied from the host arrays at each call).
+struct HashTables {
+  uint64_t mult[ENGRAM_MAX_LAYERS][ENGRAM_MAX_NGRAM];
+  uint32_t prime[ENGRAM_MAX_LAYERS][ENGRAM_MAX_COLS];
+  uint32_t offset[ENGRAM_MAX_LAYERS][ENGRAM_MAX_COLS];
+  int32_t n_layers, max_ngram, n_heads, pad_id;
+};
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipGetLastError() after queuing its kernel(s); arguments are
+// validated by the caller (api.cpp).
+
+hipError_t launch_hash(const HashTables &tab, const engram_tokens &tok, int32_t *ids,
+                       hipStream_t stream);
+
+hipError_t launch_rows(engram_row_format fmt, const uint8_t *table, const uint8_t *scales,
+                       int64_t num_rows, const int32_t *ids, int64_t ids_token_stride,
+                       int32_t cols, int32_t T, uint16_t *rows, int32_t *bad_ids,
+                       hipStream_t stream);
+
+hipError_t launch_project(const uint16_t *a, const uint16_t *w, uint16_t *c, int32_t M,
+                          int32_t K, int32_t N, hipStream_t stream);
+
+hipError_t launch_gate(float *h, const uint16_t *kv, const uint16_t *qw, const uint16_t *kw,
+                       const uint8_t *mask, int32_t T, int32_t hc, int32_t dim, float eps,
+                       float clamp, float dot_scale, hipStream_t stream);
+
+}  // namespace engram

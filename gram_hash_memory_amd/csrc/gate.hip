@@ -1,0 +1,178 @@
+// Stage 4: the Engram gate, in place on the fp32 highway.
+//
+// [spark engram_v41 page, overview stage 4]: normalised dot of stream and
+// key, signed square root, sigmoid, h += gate * value on the fp32 [T, hc, H]
+// highway.  [NeMo engram page, _engram_gate_core / compile_engram_gate]: the
+// three hidden-dim reductions (stream RMS, key RMS, stream-key dot) are
+// fused into one pass over the fp32 streams; masked tokens keep their
+// streams.  [vLLM engram page, Engram]: one key per stream plus a shared
+// value; clamp 1e-6 before the square root.
+//
+// One workgroup per token.  Every thread loads its 8-wide slices of all hc
+// streams into registers, together with the matching key and value slices.
+// It accumulates the 3*hc partial sums, and the sums are reduced with wave
+// shuffles plus one LDS exchange.  Each thread then derives the hc gates and
+// writes x + g * v from the registers, so h is read once and written once
+// and the shared value once per token (not once per stream).  Masked tokens
+// return before touching memory, which leaves them bit-for-bit unchanged.
+#include "common.hpp"
+
+namespace engram {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kVec = 8;                       // elements per thread per chunk
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(const u32x4 w, float *f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_lo(w[i]);
+    f[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+
+template <int HC, int NCH>
+__global__ __launch_bounds__(kThreads) void gate_kernel(
+    float *__restrict__ h, const uint16_t *__restrict__ kv, const uint16_t *__restrict__ qw,
+    const uint16_t *__restrict__ kw, const uint8_t *__restrict__ mask, int32_t dim,
+    float eps, float clamp, float dot_scale) {
+  const int64_t t = blockIdx.x;
+  if (mask && mask[t] == 0) return;
+  __shared__ float red[kWaves][3 * HC];
+
+  float *ht = h + t * HC * int64_t(dim);
+  const uint16_t *kvt = kv + t * (HC + 1) * int64_t(dim);
+
+  float x[HC][NCH][kVec];
+  float ssx[HC], ssk[HC], dot[HC];
+#pragma unroll
+  for (int s = 0; s < HC; ++s) ssx[s] = ssk[s] = dot[s] = 0.f;
+
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int i0 = (threadIdx.x + c * kThreads) * kVec;
+    if (i0 < dim) {
+#pragma unroll
+      for (int s = 0; s < HC; ++s) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(ht + s * dim + i0);
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(ht + s * dim + i0 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[s][c][e] = a[e];
+          x[s][c][4 + e] = b[e];
+        }
+        float key[kVec], q[kVec], k[kVec];
+        bf16x8_to_f32(*reinterpret_cast<const u32x4 *>(kvt + s * dim + i0), key);
+        bf16x8_to_f32(*reinterpret_cast<const u32x4 *>(qw + s * dim + i0), q);
+        bf16x8_to_f32(*reinterpret_cast<const u32x4 *>(kw + s * dim + i0), k);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+          const float xv = x[s][c][e];
+          ssx[s] += xv * xv;
+          ssk[s] += key[e] * key[e];
+          dot[s] += (xv * q[e]) * (key[e] * k[e]);
+        }
+      }
+    }
+  }
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int s = 0; s < HC; ++s) {
+    const float a = wave_sum(ssx[s]), b = wave_sum(ssk[s]), d = wave_sum(dot[s]);
+    if (lane == 0) {
+      red[wave][3 * s] = a;
+      red[wave][3 * s + 1] = b;
+      red[wave][3 * s + 2] = d;
+    }
+  }
+  __syncthreads();
+
+  float g[HC];
+  const float inv_dim = 1.0f / float(dim);
+#pragma unroll
+  for (int s = 0; s < HC; ++s) {
+    float a = 0.f, b = 0.f, d = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      a += red[w][3 * s];
+      b += red[w][3 * s + 1];
+      d += red[w][3 * s + 2];
+    }
+    const float rx = 1.0f / sqrtf(a * inv_dim + eps);
+    const float rk = 1.0f / sqrtf(b * inv_dim + eps);
+    const float av = dot_scale * d * rx * rk;
+    const float mag = sqrtf(fmaxf(fabsf(av), clamp));
+    const float z = av > 0.f ? mag : (av < 0.f ? -mag : 0.f);
+    g[s] = 1.0f / (1.0f + expf(-z));
+  }
+
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int i0 = (threadIdx.x + c * kThreads) * kVec;
+    if (i0 < dim) {
+      float v[kVec];
+      bf16x8_to_f32(*reinterpret_cast<const u32x4 *>(kvt + HC * dim + i0), v);
+#pragma unroll
+      for (int s = 0; s < HC; ++s) {
+        f32x4 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = x[s][c][e] + g[s] * v[e];
+          b[e] = x[s][c][4 + e] + g[s] * v[4 + e];
+        }
+        *reinterpret_cast<f32x4 *>(ht + s * dim + i0) = a;
+        *reinterpret_cast<f32x4 *>(ht + s * dim + i0 + 4) = b;
+      }
+    }
+  }
+}
+
+template <int HC>
+hipError_t launch_hc(float *h, const uint16_t *kv, const uint16_t *qw, const uint16_t *kw,
+                     const uint8_t *mask, int32_t T, int32_t dim, float eps, float clamp,
+                     float dot_scale, hipStream_t stream) {
+  const int nch = (dim + kThreads * kVec - 1) / (kThreads * kVec);
+  const dim3 grid(T), block(kThreads);
+  switch (nch) {
+    case 1:
+      hipLaunchKernelGGL((gate_kernel<HC, 1>), grid, block, 0, stream, h, kv, qw, kw, mask,
+                         dim, eps, clamp, dot_scale);
+      break;
+    case 2:
+      hipLaunchKernelGGL((gate_kernel<HC, 2>), grid, block, 0, stream, h, kv, qw, kw, mask,
+                         dim, eps, clamp, dot_scale);
+      break;
+    default:
+      hipLaunchKernelGGL((gate_kernel<HC, 4>), grid, block, 0, stream, h, kv, qw, kw, mask,
+                         dim, eps, clamp, dot_scale);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gate(float *h, const uint16_t *kv, const uint16_t *qw, const uint16_t *kw,
+                       const uint8_t *mask, int32_t T, int32_t hc, int32_t dim, float eps,
+                       float clamp, float dot_scale, hipStream_t stream) {
+  switch (hc) {
+    case 1: return launch_hc<1>(h, kv, qw, kw, mask, T, dim, eps, clamp, dot_scale, stream);
+    case 2: return launch_hc<2>(h, kv, qw, kw, mask, T, dim, eps, clamp, dot_scale, stream);
+    case 3: return launch_hc<3>(h, kv, qw, kw, mask, T, dim, eps, clamp, dot_scale, stream);
+    case 4: return launch_hc<4>(h, kv, qw, kw, mask, T, dim, eps, clamp, dot_scale, stream);
+    case 5: return launch_hc<5>(h, kv, qw, kw, mask, T, dim, eps, clamp, dot_scale, stream);
+    case 6: return launch_hc<6>(h, kv, qw, kw, mask, T, dim, eps, clamp, dot_scale, stream);
+    case 7: return launch_hc<7>(h, kv, qw, kw, mask, T, dim, eps, clamp, dot_scale, stream);
+    default: return launch_hc<8>(h, kv, qw, kw, mask, T, dim, eps, clamp, dot_scale, stream);
+  }
+}
+
+}  // namespace engram

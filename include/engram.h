@@ -1,0 +1,234 @@
+/*
+ * engram.h -- C ABI of libengram.so: the DeepSeek-V4.1 Engram forward on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The forward has four stages: n-gram hash, quantised row gather and dequant,
+ * bf16 projection, gate.  Each runs as a hand-written HIP kernel.  The stages
+ * are described on three public pages:
+ *   [spark] "Module engram_v41" (spark_model layers API docs): the overview's
+ *           four numbered stages and the ENGRAM_ROW_BYTES constant;
+ *   [NeMo]  "nemo_automodel.components.models.deepseek_v41.engram":
+ *           DeepseekV41NgramHash.forward, DeepseekV41Engram.forward,
+ *           _engram_gate_core, compile_engram_gate;
+ *   [vLLM]  "vllm.models.deepseek_v41.common.engram": Engram,
+ *           EngramLayout, NgramHashState.forward, ParallelEngramEmbedding,
+ *           _engram_lookup_kernel, compute_hash_multipliers.
+ *
+ * Conventions for every entry point:
+ *   - Memory.  The caller allocates every device buffer and keeps it alive
+ *     until the queued work has finished.  The library allocates nothing and
+ *     keeps no state between calls.  Small hash tables are passed as HOST
+ *     arrays; they are read during the call and copied into kernel arguments.
+ *   - Asynchrony.  Work is queued on `stream` (NULL = the legacy default
+ *     stream) and the call returns without synchronising.
+ *   - Errors.  All arguments are validated on the host before anything is
+ *     launched: ENGRAM_ERR_ARG and ENGRAM_ERR_UNSUPPORTED mean nothing was
+ *     queued.  ENGRAM_ERR_HIP means a launch failed (in engram_forward the
+ *     stages queued before it may still run).  After any non-OK status
+ *     engram_last_error() returns a message for the calling thread.
+ *     The library does not read device memory to validate it: the contents
+ *     of cu_seqlens and similar arrays are the caller's promise (the kernels
+ *     still keep every access inside the buffers whose sizes are passed).
+ *   - Empty input.  T == 0 returns ENGRAM_OK and queues nothing.
+ *   - bf16 values are stored as uint16_t bit patterns (the upper half of an
+ *     IEEE binary32).  Every conversion to bf16 rounds to nearest, ties to even.
+ *   - Alignment.  Every device pointer must be 16-byte aligned, except
+ *     `table` (4 bytes for Q2_K, 16 for FP8) and the byte masks (any alignment).
+ *   - Concurrency.  Calls on different streams are independent.  Calls that
+ *     write the same buffers must be ordered by the caller.
+ */
+#ifndef ENGRAM_H
+#define ENGRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The library is built with hidden visibility; only these entry points are exported. */
+#if defined(ENGRAM_BUILDING_LIBRARY)
+#define ENGRAM_API __attribute__((visibility("default")))
+#else
+#define ENGRAM_API
+#endif
+
+typedef enum engram_status {
+  ENGRAM_OK = 0,
+  ENGRAM_ERR_ARG = 1,          /* invalid argument: null, misaligned, bad size     */
+  ENGRAM_ERR_UNSUPPORTED = 2,  /* valid for the method, beyond this build's limits */
+  ENGRAM_ERR_HIP = 3           /* a HIP launch or runtime call failed             */
+} engram_status;
+
+typedef enum engram_row_format {
+  ENGRAM_ROWS_Q2K = 0,             /* one 84-byte Q2_K super-block per row        */
+  ENGRAM_ROWS_FP8_E4M3_E8M0 = 1    /* 256 e4m3fn bytes + 8 e8m0 bytes per row     */
+} engram_row_format;
+
+#define ENGRAM_HEAD_DIM 256        /* values per table row                         */
+#define ENGRAM_Q2K_ROW_BYTES 84    /* [spark] ENGRAM_ROW_BYTES                     */
+#define ENGRAM_FP8_ROW_BYTES 256
+#define ENGRAM_FP8_SCALE_BYTES 8   /* one e8m0 byte per 32 values                  */
+#define ENGRAM_MAX_LAYERS 4        /* engram layers hashed in one call             */
+#define ENGRAM_MAX_NGRAM 8         /* orders 2..max_ngram                          */
+#define ENGRAM_MAX_COLS 64         /* (max_ngram - 1) * n_heads per layer          */
+#define ENGRAM_MAX_HC 8            /* hyper-connection streams                     */
+#define ENGRAM_MAX_DIM 8192        /* hidden size                                  */
+
+/* Hash-table metadata of all engram layers ([vLLM] EngramLayout and
+ * compute_hash_multipliers; the spark page ships them as checkpoint
+ * metadata).  HOST pointers, read during the call.
+ *   multipliers [n_layers][max_ngram]: entry k multiplies the token k
+ *              positions back (k = 0: the current token); any int64.
+ *   primes     [n_layers][cols]: bucket size of column c, in [1, 2^31).
+ *   offsets    [n_layers][cols]: first row of column c, >= 0, with
+ *              offsets + primes <= 2^31 so that every id fits int32.
+ *   Column c = (n - 2) * n_heads + j holds order n (2..max_ngram), head j.
+ *   pad_id: compressed id that stands in for absent or blocked history.
+ */
+typedef struct engram_hash_params {
+  int32_t n_layers;            /* 1..ENGRAM_MAX_LAYERS                            */
+  int32_t max_ngram;           /* 2..ENGRAM_MAX_NGRAM                             */
+  int32_t n_heads;             /* >= 1, (max_ngram - 1) * n_heads <= MAX_COLS     */
+  int32_t pad_id;
+  const int64_t *multipliers;
+  const int64_t *primes;
+  const int64_t *offsets;
+} engram_hash_params;
+
+/* A batch of tokens: T positions split into n_seqs chunks.  DEVICE pointers.
+ *   cids [T]: compressed token ids (the pages hash compressed ids; the
+ *        token map that produces them is outside this library).
+ *   cu_seqlens [n_seqs + 1]: chunk s is positions cu[s] .. cu[s+1]-1;
+ *        cu[0] = 0, nondecreasing, cu[n_seqs] = T.
+ *   doc_ids [T] or NULL: document of each position; 0 marks padding
+ *        ([NeMo] DeepseekV41NgramHash.forward sequence_ids).
+ *   token_mask [T] or NULL: 0 marks image/padding positions.  They block
+ *        lookback through them, and the gate leaves them unchanged.
+ *   lookback [n_seqs][lookback_depth] or NULL: the ids just before each
+ *        chunk, oldest first, so lookback[s][depth-1] directly precedes
+ *        position cu[s] ([vLLM] module docstring, NgramHashState.forward).
+ *   lookback_live: same shape or NULL (all live); 0 = unusable entry.
+ */
+typedef struct engram_tokens {
+  int32_t T;
+  int32_t n_seqs;              /* >= 1 when T > 0                                 */
+  int32_t lookback_depth;      /* 0..max_ngram-1                                  */
+  const int32_t *cids;
+  const int32_t *cu_seqlens;
+  const int32_t *doc_ids;
+  const uint8_t *token_mask;
+  const int32_t *lookback;
+  const uint8_t *lookback_live;
+} engram_tokens;
+
+/* One engram layer's resident weights.  DEVICE pointers.
+ *   Q2K: table [num_rows][84], scales NULL.
+ *   FP8: table [num_rows][256] e4m3fn codes, scales [num_rows][8] e8m0 bytes.
+ *   wkv [(hc+1)*dim][cols*256] bf16, row-major (the projection's weight;
+ *        output o = sum_k rows[k] * wkv[o][k]).
+ *   q_weight, k_weight [hc][dim] bf16 (learned branch-norm weights).
+ */
+typedef struct engram_layer {
+  engram_row_format fmt;
+  int64_t num_rows;
+  const uint8_t *table;
+  const uint8_t *scales;
+  const uint16_t *wkv;
+  const uint16_t *q_weight;
+  const uint16_t *k_weight;
+} engram_layer;
+
+/* Stage 1 -- n-gram hash ([spark] overview stage 1; [vLLM] EngramLayout,
+ * NgramHashState.forward; [NeMo] DeepseekV41NgramHash.forward).
+ * For every position t, layer l, order n and head j (column c):
+ *   tok_0 = cids[t]; tok_k = the id k positions back if that position and
+ *     every position between it and t is live, else pad_id.  A position is
+ *     live if it lies in t's chunk or in its lookback, is not masked, and
+ *     (when doc_ids is given) has the same non-zero document as t.  A padding
+ *     position (doc 0) has no history.  A dead lookback entry is not live.
+ *   mix_n = XOR over k < n of (uint64)tok_k * (uint64)multipliers[l][k]
+ *     (64-bit wrapping products; within 0 <= id < vocab none wrap).
+ *   ids[t][l][c] = offsets[l][c] + mix_n mod primes[l][c].
+ * Output ids: DEVICE int32 [T][n_layers][cols], fully overwritten.
+ */
+ENGRAM_API engram_status engram_hash(const engram_hash_params *params, const engram_tokens *tokens,
+                          int32_t *ids, hipStream_t stream);
+
+/* Stage 2 -- row gather + dequant to bf16 ([spark] overview stage 2,
+ * ENGRAM_ROW_BYTES; [vLLM] _engram_lookup_kernel, bf16 mode).
+ *   ids: DEVICE int32; row r of token t is ids[t * ids_token_stride + r],
+ *        r < cols (pass ids + l * cols and stride n_layers * cols to use
+ *        layer l of engram_hash's output).
+ *   rows: DEVICE bf16 [T][cols * 256]; rows[t][r*256 + i] is value i of
+ *        table row ids[t][r], fully overwritten.
+ *   Q2_K value i of a block: bytes 0..15 hold (min << 4 | scale) per 16
+ *     values, bytes 16..79 the 2-bit quants (value i: byte
+ *     16 + 32*(i/128) + i%32, bits 2*((i%128)/32)), bytes 80..81 fp16 d,
+ *     82..83 fp16 dmin; y = d*scale*q - dmin*min in fp32, then bf16.
+ *     This equals the exact value whenever d and dmin are within 2^6 of
+ *     each other.
+ *   FP8 value i: e4m3fn code times 2^(scales[row][i/32] - 127) (the byte is
+ *     placed in the binary32 exponent field, so byte 0 gives 0), then bf16.
+ *   An id outside [0, num_rows) yields a zero row; if bad_ids (DEVICE int32,
+ *   nullable) is given, it is atomically incremented once per such row.
+ */
+ENGRAM_API engram_status engram_rows(engram_row_format fmt, const uint8_t *table, const uint8_t *scales,
+                          int64_t num_rows, const int32_t *ids, int64_t ids_token_stride,
+                          int32_t cols, int32_t T, uint16_t *rows, int32_t *bad_ids,
+                          hipStream_t stream);
+
+/* Stage 3 -- projection kv = rows x wkv^T ([spark] overview stage 3; [vLLM]
+ * Engram, the wkv linear without bias).
+ *   rows DEVICE bf16 [T][K], wkv DEVICE bf16 [N][K], kv DEVICE bf16 [T][N],
+ *   all row-major; K % 64 == 0.  Products accumulate in fp32 on the matrix
+ *   cores and each output is rounded to bf16 once.
+ */
+ENGRAM_API engram_status engram_project(const uint16_t *rows, const uint16_t *wkv, uint16_t *kv,
+                             int32_t T, int32_t K, int32_t N, hipStream_t stream);
+
+/* Stage 4 -- gate, in place on the fp32 highway ([spark] overview stage 4;
+ * [NeMo] _engram_gate_core, compile_engram_gate; [vLLM] Engram).
+ *   h DEVICE fp32 [T][hc][dim], updated in place.
+ *   kv DEVICE bf16 [T][(hc+1)*dim]: hc keys (stream-major), then the shared value.
+ *   q_weight, k_weight DEVICE bf16 [hc][dim].  token_mask DEVICE [T] or NULL.
+ *   For each token t with a non-zero mask and each stream s, in fp32:
+ *     a = dot_scale * sum_i (x_i q_i)(key_i k_i) / (rms(x) rms(key)),
+ *         rms(v) = sqrt(mean(v^2) + eps), x = h[t][s], key = key s of t;
+ *     z = sign(a) * sqrt(max(|a|, clamp));  g = 1 / (1 + exp(-z));
+ *     h[t][s][i] += g * value[i].
+ *   Masked tokens are not written, so they stay unchanged bit for bit.
+ *   Limits: 1 <= hc <= ENGRAM_MAX_HC, 8 <= dim <= ENGRAM_MAX_DIM, dim % 8 == 0.
+ */
+ENGRAM_API engram_status engram_gate(float *h, const uint16_t *kv, const uint16_t *q_weight,
+                          const uint16_t *k_weight, const uint8_t *token_mask, int32_t T,
+                          int32_t hc, int32_t dim, float eps, float clamp, float dot_scale,
+                          hipStream_t stream);
+
+/* Bytes of device workspace engram_forward needs for this shape: the ids,
+ * one layer's rows and one layer's kv, each 256-byte aligned. */
+ENGRAM_API size_t engram_workspace_bytes(int32_t T, int32_t n_layers, int32_t cols, int32_t hc,
+                              int32_t dim);
+
+/* The whole forward ([spark] overview, stages 1-4): hash every layer once,
+ * then for each layer in order: rows -> projection -> gate on the same h.
+ *   layers: HOST array [params->n_layers] of DEVICE-pointer descriptors.
+ *   workspace: DEVICE, at least engram_workspace_bytes(...) bytes, 256-byte
+ *   aligned; its contents are scratch.  Every other argument is as for the
+ *   per-stage calls; the gate mask is tokens->token_mask.  Validation also
+ *   checks offsets + primes <= num_rows for every layer.
+ */
+ENGRAM_API engram_status engram_forward(const engram_hash_params *params, const engram_tokens *tokens,
+                             const engram_layer *layers, float *h, int32_t hc, int32_t dim,
+                             float eps, float clamp, float dot_scale, void *workspace,
+                             size_t workspace_bytes, int32_t *bad_ids, hipStream_t stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+ENGRAM_API const char *engram_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ENGRAM_H */

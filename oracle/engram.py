@@ -204,7 +204,7 @@ def project(rows_bits, wkv_bits) -> np.ndarray:
 # --------------------------------------------------------------------------- gate
 
 def gate(h, kv_bits, q_weight_bits, k_weight_bits, token_mask, eps, clamp,
-         dot_scale) -> np.ndarray:
+         dot_scale, return_preact=False):
     """Gate the shared value into every stream; returns new fp32 h [T, hc, dim].
 
     [spark] stage 4, [vLLM] Engram, [NeMo] _engram_gate_core.  For each
@@ -218,6 +218,7 @@ def gate(h, kv_bits, q_weight_bits, k_weight_bits, token_mask, eps, clamp,
         h[t,s] <- x + g * value
     Masked tokens keep their streams bit for bit (reading A17).  Everything
     runs in float64; the result is rounded to fp32 once (reading A19).
+    With return_preact, also returns a [T, hc] (the scaled normalised dot).
     """
     h = np.asarray(h, dtype=np.float32)
     T, hc, dim = h.shape
@@ -236,6 +237,8 @@ def gate(h, kv_bits, q_weight_bits, k_weight_bits, token_mask, eps, clamp,
     if token_mask is not None:
         keep = ~np.asarray(token_mask, dtype=bool)
         new[keep] = h[keep]
+    if return_preact:
+        return new, a
     return new
 
 

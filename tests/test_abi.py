@@ -1,0 +1,199 @@
+"""C-ABI checks that need no GPU: exports, workspace sizes, host-side validation.
+
+The validation cases pass arguments that the host checks must reject before
+any launch.  They run only where no GPU device node exists: there, even a
+validation bug could only end in a failed launch (no device), never in a
+kernel touching a bogus pointer.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "engram.h")
+NO_GPU = not os.path.exists("/dev/kfd")
+
+
+@pytest.fixture(scope="module")
+def eg():
+    from gram_hash_memory_amd.build import LIB, build
+    if not os.path.exists(LIB):
+        build()
+    import gram_hash_memory_amd
+    return gram_hash_memory_amd
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"ENGRAM_API\s+[\w\s\*]+?\b(engram_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls_and_helpers():
+    names = declared_functions()
+    for want in ("engram_hash", "engram_rows", "engram_project", "engram_gate",
+                 "engram_forward", "engram_workspace_bytes", "engram_last_error"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(eg):
+    lib = ctypes.CDLL(eg.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(eg.EXPORTS)
+
+
+def test_library_exports_nothing_else(eg):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", eg.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    ours = {line.split()[-1] for line in out.splitlines()
+            if " T " in line and "engram" in line.lower()}
+    assert ours == set(declared_functions())
+
+
+def test_workspace_bytes(eg):
+    def a256(x):
+        return (x + 255) // 256 * 256
+    T, L, cols, hc, dim = 8192, 1, 24, 4, 4096
+    want = a256(T * L * cols * 4) + a256(T * cols * 256 * 2) + a256(T * (hc + 1) * dim * 2)
+    assert eg.engram_workspace_bytes(T, L, cols, hc, dim) == want
+    assert eg.engram_workspace_bytes(0, 1, 24, 4, 4096) == 0
+    assert eg.engram_workspace_bytes(-1, 1, 24, 4, 4096) == 0
+
+
+# ------------------------------------------------------------ raw C validation
+
+class _HP(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("max_ngram", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("pad_id", ctypes.c_int32),
+                ("multipliers", ctypes.c_void_p), ("primes", ctypes.c_void_p),
+                ("offsets", ctypes.c_void_p)]
+
+
+class _TK(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("n_seqs", ctypes.c_int32),
+                ("lookback_depth", ctypes.c_int32), ("cids", ctypes.c_void_p),
+                ("cu_seqlens", ctypes.c_void_p), ("doc_ids", ctypes.c_void_p),
+                ("token_mask", ctypes.c_void_p), ("lookback", ctypes.c_void_p),
+                ("lookback_live", ctypes.c_void_p)]
+
+
+FAKE = 0x10000      # aligned, never dereferenced by the host checks
+
+
+def _raw(eg):
+    lib = ctypes.CDLL(eg.LIB_PATH)
+    lib.engram_last_error.restype = ctypes.c_char_p
+    lib.engram_hash.argtypes = [ctypes.POINTER(_HP), ctypes.POINTER(_TK), ctypes.c_void_p,
+                                ctypes.c_void_p]
+    lib.engram_rows.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.engram_project.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int32] * 3 + [ctypes.c_void_p]
+    lib.engram_gate.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int32] * 3 +
+                                [ctypes.c_float] * 3 + [ctypes.c_void_p])
+    return lib
+
+
+def _tables(L=1, N=4, H=2):
+    cols = (N - 1) * H
+    m = np.ones((L, N), np.int64)
+    p = np.full((L, cols), 7, np.int64)
+    o = (np.arange(cols, dtype=np.int64) * 7)[None].repeat(L, 0)
+    return m, p, o
+
+
+def _hp(m, p, o, L=1, N=4, H=2, pad=0):
+    return _HP(L, N, H, pad, m.ctypes.data, p.ctypes.data, o.ctypes.data)
+
+
+@pytest.mark.skipif(not NO_GPU, reason="validation-rejection cases run only without a GPU")
+class TestValidation:
+    def test_hash_rejects(self, eg):
+        lib = _raw(eg)
+        m, p, o = _tables()
+        tk = _TK(16, 1, 0, FAKE, FAKE, None, None, None, None)
+        assert lib.engram_hash(None, ctypes.byref(tk), FAKE, None) == eg.ENGRAM_ERR_ARG
+        cases = [
+            (_hp(m, p, o, L=5), eg.ENGRAM_ERR_UNSUPPORTED, "n_layers"),
+            (_hp(m, p, o, N=1), eg.ENGRAM_ERR_UNSUPPORTED, "max_ngram"),
+            (_hp(m, p, o, N=9), eg.ENGRAM_ERR_UNSUPPORTED, "max_ngram"),
+            (_hp(m, p, o, H=0), eg.ENGRAM_ERR_ARG, "n_heads"),
+        ]
+        for hp, st, msg in cases:
+            assert lib.engram_hash(ctypes.byref(hp), ctypes.byref(tk), FAKE, None) == st
+            assert msg in lib.engram_last_error().decode()
+        bad_p = p.copy()
+        bad_p[0, 3] = 0
+        hp = _hp(m, bad_p, o)
+        assert lib.engram_hash(ctypes.byref(hp), ctypes.byref(tk), FAKE, None) == eg.ENGRAM_ERR_ARG
+        assert "primes" in lib.engram_last_error().decode()
+        big_o = o.copy()
+        big_o[0, 5] = 2**31 - 3
+        hp = _hp(m, p, big_o)
+        assert lib.engram_hash(ctypes.byref(hp), ctypes.byref(tk), FAKE, None) == eg.ENGRAM_ERR_ARG
+        hp = _hp(m, p, o)
+        for bad in (_TK(16, 0, 0, FAKE, FAKE, None, None, None, None),
+                    _TK(16, 1, 4, FAKE, FAKE, None, None, FAKE, None),      # depth > N-1
+                    _TK(16, 1, 0, None, FAKE, None, None, None, None),
+                    _TK(16, 1, 0, FAKE + 2, FAKE, None, None, None, None),  # misaligned
+                    _TK(16, 1, 2, FAKE, FAKE, None, None, None, FAKE),      # live w/o lookback
+                    _TK(-1, 1, 0, FAKE, FAKE, None, None, None, None)):
+            assert lib.engram_hash(ctypes.byref(hp), ctypes.byref(bad), FAKE, None) == eg.ENGRAM_ERR_ARG
+        assert lib.engram_hash(ctypes.byref(hp), ctypes.byref(tk), None, None) == eg.ENGRAM_ERR_ARG
+        empty = _TK(0, 0, 0, None, None, None, None, None, None)
+        assert lib.engram_hash(ctypes.byref(hp), ctypes.byref(empty), None, None) == eg.ENGRAM_OK
+
+    def test_rows_rejects(self, eg):
+        lib = _raw(eg)
+        Q, F = eg.ENGRAM_ROWS_Q2K, eg.ENGRAM_ROWS_FP8_E4M3_E8M0
+        ok = dict(fmt=Q, table=FAKE, scales=None, nrows=100, ids=FAKE, stride=24, cols=24, T=8,
+                  rows=FAKE, bad=None)
+
+        def call(**kw):
+            a = dict(ok, **kw)
+            return lib.engram_rows(a["fmt"], a["table"], a["scales"], a["nrows"], a["ids"],
+                                   a["stride"], a["cols"], a["T"], a["rows"], a["bad"], None)
+        for kw in (dict(fmt=7), dict(nrows=0), dict(cols=0), dict(stride=23), dict(T=-1),
+                   dict(table=None), dict(ids=None), dict(rows=None), dict(rows=FAKE + 8),
+                   dict(table=FAKE + 2), dict(ids=FAKE + 1), dict(bad=FAKE + 2),
+                   dict(fmt=F, scales=None), dict(fmt=F, scales=FAKE, table=FAKE + 4)):
+            assert call(**kw) == eg.ENGRAM_ERR_ARG, kw
+        assert call(T=0, table=None, ids=None, rows=None) == eg.ENGRAM_OK
+
+    def test_project_rejects(self, eg):
+        lib = _raw(eg)
+        for args in ((FAKE, FAKE, FAKE, 8, 100, 64),       # K not a multiple of 64
+                     (FAKE, FAKE, FAKE, 8, 0, 64),
+                     (FAKE, FAKE, FAKE, 8, 64, 0),
+                     (FAKE, FAKE, FAKE, -1, 64, 64),
+                     (None, FAKE, FAKE, 8, 64, 64),
+                     (FAKE, FAKE + 8, FAKE, 8, 64, 64)):
+            assert lib.engram_project(*args, None) == eg.ENGRAM_ERR_ARG, args
+        assert lib.engram_project(None, None, None, 0, 64, 64, None) == eg.ENGRAM_OK
+
+    def test_gate_rejects(self, eg):
+        lib = _raw(eg)
+        ok = [FAKE, FAKE, FAKE, FAKE, None, 8, 4, 4096, 1e-6, 1e-6, 1 / 64]
+        for i, v, st in ((6, 9, eg.ENGRAM_ERR_UNSUPPORTED), (6, 0, eg.ENGRAM_ERR_UNSUPPORTED),
+                         (7, 100, eg.ENGRAM_ERR_UNSUPPORTED), (7, 16384, eg.ENGRAM_ERR_UNSUPPORTED),
+                         (5, -1, eg.ENGRAM_ERR_ARG), (8, -1.0, eg.ENGRAM_ERR_ARG),
+                         (0, None, eg.ENGRAM_ERR_ARG), (1, FAKE + 4, eg.ENGRAM_ERR_ARG)):
+            a = list(ok)
+            a[i] = v
+            assert lib.engram_gate(*a, None) == st, (i, v)
+        a = list(ok)
+        a[5] = 0
+        a[0] = None
+        assert lib.engram_gate(*a, None) == eg.ENGRAM_OK
+
+
+def test_binding_refuses_host_tensors(eg):
+    import torch
+    h = torch.zeros(4, 2, 8)
+    with pytest.raises(TypeError):
+        eg.engram_gate(h, h, h, h, None, 4, 2, 8, 1e-6, 1e-6, 0.3, stream=0)

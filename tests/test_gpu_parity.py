@@ -1,0 +1,334 @@
+"""GPU parity: every stage of the HIP path against the CPU oracle, through the C ABI.
+
+Bars:
+* hash ids and dequantised rows: bit-exact on every workload;
+* projection: |kv_gpu - kv_oracle| <= one bf16 ulp + K * 2^-24 * sum|a||b|
+  (fp32 accumulation on the GPU, one rounding of the exact sum in the oracle);
+* gate and whole forward: |h_gpu - h_oracle| <= 1e-2 * max(1, |h_oracle|)
+  per element.  The gate stage, fed the oracle's own kv, must also match within
+  1e-4 * max(1, |h|) wherever the pre-activation |a| > 1e-2: outside the steep
+  region of the signed square root, fp32 reductions over dim elements stay
+  far inside that.  Masked tokens must be bit-for-bit unchanged.
+
+Full-size workloads are checked on all outputs where the oracle is cheap
+(ids, rows) and on a sample of tokens otherwise (kv, h), at the exact launch
+configuration the benchmark uses.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads.device import to_device, tensor
+
+pytestmark = pytest.mark.gpu
+
+CONFIGS = [0, 1, 2, 3, 4]
+_host, _dev, _ids = {}, {}, {}
+
+
+@pytest.fixture(scope="module")
+def eg():
+    import os
+    from gram_hash_memory_amd.build import LIB, build
+    if not os.path.exists(LIB):
+        build()
+    import gram_hash_memory_amd
+    torch.cuda.set_device(0)
+    return gram_hash_memory_amd
+
+
+def host(c):
+    if c not in _host:
+        _host[c] = workloads.make_workload(c)
+    return _host[c]
+
+
+def dev(c):
+    if c not in _dev:
+        _dev[c] = to_device(host(c), "cuda")
+    return _dev[c]
+
+
+def oracle_ids(c):
+    if c not in _ids:
+        wl = host(c)
+        hp = wl.hash_params
+        _ids[c] = oracle.hash_ids(wl.cids, wl.cu_seqlens, hp["multipliers"], hp["primes"],
+                                  hp["offsets"], hp["max_ngram"], hp["n_heads"], hp["pad_id"],
+                                  doc_ids=wl.doc_ids, token_mask=wl.token_mask,
+                                  lookback=wl.lookback, lookback_live=wl.lookback_live)
+    return _ids[c]
+
+
+def binding_objs(eg, c):
+    wl, dw = host(c), dev(c)
+    s = wl.spec
+    params = eg.HashParams.from_dict(wl.hash_params)
+    tokens = eg.Tokens(dw.cids, dw.cu_seqlens, dw.doc_ids, dw.token_mask, dw.lookback,
+                       dw.lookback_live)
+    fmt = eg.ENGRAM_ROWS_Q2K if s.fmt == "q2k" else eg.ENGRAM_ROWS_FP8_E4M3_E8M0
+    layers = [eg.Layer(fmt, l.table, l.scales, l.wkv, l.q_weight, l.k_weight, s.hc, s.dim,
+                       s.cols) for l in dw.layers]
+    return params, tokens, layers, fmt
+
+
+def sample_tokens(wl, n=96, seed=0):
+    T = wl.spec.T
+    if T <= 128:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    pick = {0, 1, 2, T - 1, T - 2}
+    pick.update(int(c) for c in wl.cu_seqlens[1:-1])             # chunk starts
+    if wl.token_mask is not None:
+        pick.update(np.flatnonzero(wl.token_mask == 0)[:8].tolist())
+    pick.update(rng.choice(T, n, replace=False).tolist())
+    return np.array(sorted(pick))
+
+
+def gpu_rows(eg, c, layer, fmt):
+    wl, dw = host(c), dev(c)
+    s = wl.spec
+    ids = torch.empty((s.T, len(s.layer_ids), s.cols), dtype=torch.int32, device="cuda")
+    params, tokens, _, _ = binding_objs(eg, c)
+    eg.engram_hash(params, tokens, ids)
+    rows = torch.empty((s.T, s.K), dtype=torch.int16, device="cuda")
+    L = dw.layers[layer]
+    num_rows = L.table.numel() // (84 if fmt == eg.ENGRAM_ROWS_Q2K else 256)
+    eg.engram_rows(fmt, L.table, L.scales, num_rows, ids.view(-1)[layer * s.cols:],
+                   len(s.layer_ids) * s.cols, s.cols, s.T, rows)
+    return ids, rows
+
+
+def bf16_ulp(x):
+    x = np.maximum(np.abs(x), 2.0 ** -126)
+    return np.ldexp(1.0, np.floor(np.log2(x)).astype(np.int64) - 7)
+
+
+# ------------------------------------------------------------------------- hash
+
+@pytest.mark.parametrize("c", CONFIGS)
+def test_hash_bit_exact(eg, c):
+    wl = host(c)
+    s = wl.spec
+    params, tokens, _, _ = binding_objs(eg, c)
+    ids = torch.full((s.T, len(s.layer_ids), s.cols), -7, dtype=torch.int32, device="cuda")
+    eg.engram_hash(params, tokens, ids)
+    got = ids.cpu().numpy()
+    want = oracle_ids(c)
+    assert np.array_equal(got, want), f"{(got != want).sum()} ids differ"
+
+
+# ------------------------------------------------------------------------- rows
+
+@pytest.mark.parametrize("c", CONFIGS)
+def test_rows_bit_exact(eg, c):
+    wl = host(c)
+    s = wl.spec
+    _, _, _, fmt = binding_objs(eg, c)
+    want_ids = oracle_ids(c)
+    for layer in range(len(s.layer_ids)):
+        _, rows = gpu_rows(eg, c, layer, fmt)
+        got = rows.cpu().numpy().view(np.uint16)
+        L = wl.layers[layer]
+        if s.fmt == "q2k":
+            want = oracle.rows_q2k(L.table, want_ids[:, layer])
+        else:
+            want = oracle.rows_fp8(L.table, L.scales, want_ids[:, layer])
+        assert np.array_equal(got, want), f"layer {layer}: {(got != want).sum()} values differ"
+
+
+def test_rows_out_of_range_ids_and_counter(eg):
+    # Ids outside [0, num_rows) read as zero rows and bump the counter once each.
+    wl = host(0)
+    dw = dev(0)
+    table = dw.layers[0].table
+    R = table.numel() // 84
+    ids_np = np.array([[5, -1, R, R - 1], [2**31 - 1, 0, -(2**31), 7], [3, 3, 3, 3]],
+                      dtype=np.int32)
+    ids = tensor(ids_np, "cuda")
+    rows = torch.full((3, 4 * 256), 0x5555, dtype=torch.int16, device="cuda")
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    eg.engram_rows(eg.ENGRAM_ROWS_Q2K, table, None, R, ids, 4, 4, 3, rows, bad)
+    want = oracle.rows_q2k(wl.layers[0].table, ids_np)
+    assert np.array_equal(rows.cpu().numpy().view(np.uint16), want)
+    assert bad.item() == 4
+
+
+@pytest.mark.parametrize("T", [1, 3, 33])
+def test_rows_ragged_token_counts_and_fp8_small(eg, T):
+    rng = np.random.default_rng(T)
+    R, cols = 50, 5
+    vals = np.clip(rng.standard_normal((R, 256)).astype(np.float32), -448, 448)
+    codes = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    scales = rng.integers(119, 128, (R, 8)).astype(np.uint8)
+    ids_np = rng.integers(-2, R + 2, (T, cols)).astype(np.int32)
+    rows = torch.empty((T, cols * 256), dtype=torch.int16, device="cuda")
+    eg.engram_rows(eg.ENGRAM_ROWS_FP8_E4M3_E8M0, tensor(codes, "cuda"), tensor(scales, "cuda"),
+                   R, tensor(ids_np, "cuda"), cols, cols, T, rows)
+    want = oracle.rows_fp8(codes, scales, ids_np)
+    assert np.array_equal(rows.cpu().numpy().view(np.uint16), want)
+
+
+# ------------------------------------------------------------------- projection
+
+def _check_kv(got_bits, rows_bits, wkv_bits):
+    want = oracle.bf16_value(oracle.project(rows_bits, wkv_bits))
+    got = oracle.bf16_value(got_bits)
+    a, b = oracle.bf16_value(rows_bits), oracle.bf16_value(wkv_bits)
+    K = a.shape[1]
+    bound = bf16_ulp(np.maximum(np.abs(want), np.abs(got))) + K * 2.0 ** -24 * (np.abs(a) @ np.abs(b).T)
+    err = np.abs(got - want)
+    assert (err <= bound).all(), f"max err/bound {np.max(err / bound):.3f}"
+    return float(np.mean(got == want))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (300, 520, 512), (257, 256, 1536),
+                                   (512, 768, 192)])
+def test_project_ragged_shapes_full_compare(eg, M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    a = oracle.bf16_bits(oracle.bf16_round(rng.standard_normal((M, K))))
+    b = oracle.bf16_bits(oracle.bf16_round(0.02 * rng.standard_normal((N, K))))
+    kv = torch.full((M, N), 0x7777, dtype=torch.int16, device="cuda")
+    eg.engram_project(tensor(a, "cuda"), tensor(b, "cuda"), kv, M, K, N)
+    exact = _check_kv(kv.cpu().numpy().view(np.uint16), a, b)
+    assert exact > 0.9
+
+
+@pytest.mark.parametrize("c", CONFIGS)
+def test_project_workloads_sampled(eg, c):
+    wl = host(c)
+    s = wl.spec
+    _, _, _, fmt = binding_objs(eg, c)
+    for layer in range(len(s.layer_ids)):
+        _, rows = gpu_rows(eg, c, layer, fmt)
+        kv = torch.empty((s.T, s.N), dtype=torch.int16, device="cuda")
+        eg.engram_project(rows, dev(c).layers[layer].wkv, kv, s.T, s.K, s.N)
+        pick = sample_tokens(wl)
+        rows_np = rows.cpu().numpy().view(np.uint16)[pick]
+        got = kv.cpu().numpy().view(np.uint16)[pick]
+        _check_kv(got, rows_np, wl.layers[layer].wkv)
+
+
+# ------------------------------------------------------------------------- gate
+
+@pytest.mark.parametrize("c", CONFIGS)
+def test_gate_with_oracle_kv(eg, c):
+    # Feed the oracle's kv (same bits) so that only the gate arithmetic differs.
+    wl = host(c)
+    s = wl.spec
+    pick = sample_tokens(wl)
+    L = wl.layers[0]
+    ids = oracle_ids(c)[pick, 0]
+    rows = (oracle.rows_q2k(L.table, ids) if s.fmt == "q2k"
+            else oracle.rows_fp8(L.table, L.scales, ids))
+    kv = oracle.project(rows, L.wkv)
+    h0 = wl.h[pick]
+    mask = None if wl.token_mask is None else wl.token_mask[pick]
+    want, a = oracle.gate(h0, kv, L.q_weight, L.k_weight, mask, s.eps, s.clamp, s.dot_scale,
+                          return_preact=True)
+    h = tensor(h0, "cuda")
+    eg.engram_gate(h, tensor(kv, "cuda"), dev(c).layers[0].q_weight, dev(c).layers[0].k_weight,
+                   None if mask is None else tensor(mask, "cuda"), len(pick), s.hc, s.dim,
+                   s.eps, s.clamp, s.dot_scale)
+    got = h.cpu().numpy()
+    err = np.abs(got - want) / np.maximum(1.0, np.abs(want))
+    assert err.max() <= 1e-2
+    steady = np.abs(a) > 1e-2
+    assert err[steady].max() <= 1e-4, f"max err away from a=0: {err[steady].max():.2e}"
+    if mask is not None:
+        off = mask == 0
+        assert np.array_equal(got[off].view(np.uint32), h0[off].view(np.uint32))
+
+
+def test_gate_value_zero_and_all_masked_are_identity(eg):
+    rng = np.random.default_rng(11)
+    T, hc, dim = 40, 3, 264
+    h0 = rng.standard_normal((T, hc, dim)).astype(np.float32)
+    kv = oracle.bf16_bits(oracle.bf16_round(0.1 * rng.standard_normal((T, (hc + 1) * dim))))
+    kv[:, hc * dim:] = 0
+    w = oracle.bf16_bits(oracle.bf16_round(1 + 0.1 * rng.standard_normal((hc, dim))))
+    h = tensor(h0, "cuda")
+    eg.engram_gate(h, tensor(kv, "cuda"), tensor(w, "cuda"), tensor(w, "cuda"), None, T, hc,
+                   dim, 1e-6, 1e-6, dim ** -0.5)
+    assert np.array_equal(h.cpu().numpy().view(np.uint32), h0.view(np.uint32))
+    kv[:, hc * dim:] = oracle.bf16_bits(np.ones((T, dim)))
+    h = tensor(h0, "cuda")
+    eg.engram_gate(h, tensor(kv, "cuda"), tensor(w, "cuda"), tensor(w, "cuda"),
+                   torch.zeros(T, dtype=torch.uint8, device="cuda"), T, hc, dim, 1e-6, 1e-6,
+                   dim ** -0.5)
+    assert np.array_equal(h.cpu().numpy().view(np.uint32), h0.view(np.uint32))
+
+
+@pytest.mark.parametrize("hc,dim", [(1, 8), (2, 200), (5, 2056), (8, 8192)])
+def test_gate_shapes(eg, hc, dim):
+    rng = np.random.default_rng(hc * dim)
+    T = 5
+    h0 = rng.standard_normal((T, hc, dim)).astype(np.float32)
+    kv = oracle.bf16_bits(oracle.bf16_round(0.125 * rng.standard_normal((T, (hc + 1) * dim))))
+    q = oracle.bf16_bits(oracle.bf16_round(1 + 0.1 * rng.standard_normal((hc, dim))))
+    k = oracle.bf16_bits(oracle.bf16_round(1 + 0.1 * rng.standard_normal((hc, dim))))
+    want = oracle.gate(h0, kv, q, k, None, 1e-6, 1e-6, dim ** -0.5)
+    h = tensor(h0, "cuda")
+    eg.engram_gate(h, tensor(kv, "cuda"), tensor(q, "cuda"), tensor(k, "cuda"), None, T, hc,
+                   dim, 1e-6, 1e-6, dim ** -0.5)
+    err = np.abs(h.cpu().numpy() - want) / np.maximum(1.0, np.abs(want))
+    assert err.max() <= 1e-2
+
+
+# ---------------------------------------------------------------------- forward
+
+@pytest.mark.parametrize("c", CONFIGS)
+def test_forward_against_oracle(eg, c):
+    wl = host(c)
+    s = wl.spec
+    params, tokens, layers, _ = binding_objs(eg, c)
+    h = dev(c).h.clone()
+    ws = torch.empty(eg.engram_workspace_bytes(s.T, len(s.layer_ids), s.cols, s.hc, s.dim),
+                     dtype=torch.uint8, device="cuda")
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    eg.engram_forward(params, tokens, layers, h, s.hc, s.dim, s.eps, s.clamp, s.dot_scale, ws,
+                      bad)
+    got = h.cpu().numpy()
+    assert bad.item() == 0
+    pick = sample_tokens(wl)
+    ids = oracle_ids(c)[pick]
+    want = wl.h[pick]
+    for l, L in enumerate(wl.layers):
+        rows = (oracle.rows_q2k(L.table, ids[:, l]) if s.fmt == "q2k"
+                else oracle.rows_fp8(L.table, L.scales, ids[:, l]))
+        kv = oracle.project(rows, L.wkv)
+        mask = None if wl.token_mask is None else wl.token_mask[pick]
+        want = oracle.gate(want, kv, L.q_weight, L.k_weight, mask, s.eps, s.clamp, s.dot_scale)
+    err = np.abs(got[pick] - want) / np.maximum(1.0, np.abs(want))
+    print(f"config {c}: max rel err {err.max():.3e} over {len(pick)} tokens", flush=True)
+    assert err.max() <= 1e-2
+    if wl.token_mask is not None:
+        off = np.flatnonzero(wl.token_mask == 0)
+        assert np.array_equal(got[off].view(np.uint32), wl.h[off].view(np.uint32))
+
+
+def test_forward_empty_batch(eg):
+    wl = host(0)
+    s = wl.spec
+    params = eg.HashParams.from_dict(wl.hash_params)
+    e32 = torch.empty(0, dtype=torch.int32, device="cuda")
+    tokens = eg.Tokens(e32, torch.zeros(1, dtype=torch.int32, device="cuda"))
+    _, _, layers, _ = binding_objs(eg, 0)
+    h = torch.empty((0, s.hc, s.dim), dtype=torch.float32, device="cuda")
+    eg.engram_forward(params, tokens, layers, h, s.hc, s.dim, s.eps, s.clamp, s.dot_scale,
+                      torch.empty(0, dtype=torch.uint8, device="cuda"))
+    ids = torch.empty(0, dtype=torch.int32, device="cuda")
+    eg.engram_hash(params, tokens, ids)
+    torch.cuda.synchronize()
+
+
+def test_binding_rejects_short_buffers(eg):
+    wl = host(0)
+    s = wl.spec
+    params, tokens, _, _ = binding_objs(eg, 0)
+    short = torch.empty(s.T * s.cols - 1, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        eg.engram_hash(params, tokens, short)
