@@ -10,12 +10,11 @@
 //
 // Tiling (gfx950: 160 KB LDS per CU, 4 SIMDs): a 256 x 256 output tile per
 // workgroup of 4 waves in a 2 x 2 grid.  Each wave owns 128 x 128 = 4 x 4
-// MFMA tiles, whose 256 fp32 accumulators live in AGPRs.  K advances 64 at a
-// time through two LDS stages of 64 KB each (A and B tiles, 256 rows x 128 B).
-// The next stage's global loads are in flight while the current stage is
-// multiplied.  Inside a row, each 16-byte chunk sits at position
-// chunk ^ (row & 7), so the 8 lanes of a ds_read_b128 phase hit 8 distinct
-// chunks and never the same banks.
+// MFMA tiles, whose 256 fp32 accumulators live in AGPRs.  A and B tiles
+// stream through a ring of LDS stages that are filled straight from global
+// memory (buffer_load ... lds, no VGPR staging), several stages ahead of the
+// matrix cores.  Fragment reads from LDS are interleaved one-for-two with
+// the MFMAs, and the chunk swizzle keeps them free of bank conflicts.
 //
 // Tile order: the hardware deals workgroups round-robin to the 8 XCDs, each of
 // which has its own L2.  The block id is remapped so that every XCD gets a
@@ -26,16 +25,56 @@
 namespace engram {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256;
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 constexpr int kGroupM = 8;
 constexpr int kNumXcd = 8;
-constexpr int kChunks = BK / 8;                         // 16-byte chunks per tile row
-constexpr int kLoadsPerThread = BM * kChunks / kThreads;  // per operand, per stage
-constexpr int kStageElems = (BM + BN) * BK;             // bf16 elements per stage
+// sched_group_barrier instruction classes.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmemRead = 0x020;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedDsWrite = 0x200;
 
+// s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4 (left at max), lgkmcnt 11:8.
+constexpr int waitcnt(int vm, int lgkm) {
+  return (vm & 15) | (((vm >> 4) & 3) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
+// LDS layout of one operand tile: BM rows of BK bf16, in 16-byte chunks.
+// gfx950's LDS serves a ds_read_b128 16 lanes per cycle across 64 banks.
+// Our fragment reads hit 16 consecutive rows at one logical chunk.  The
+// chunk is stored at (logical chunk) ^ key(row), and the key makes those 16
+// rows land on 16 distinct 16-byte bank groups:
+//   BK = 64 (8 chunks, 128 B rows): the bank group is (row % 2, chunk), so key
+//     = (row & 7) ^ ((row >> 3) & 1) is a bijection on the 8 even and on the
+//     8 odd rows;
+//   BK = 32 (4 chunks, 64 B rows): the bank group is (row % 4, chunk), so key
+//     = (row >> 2) & 3 is a bijection on each residue class mod 4.
+template <int BK>
+__device__ __forceinline__ int swz_key(int row) {
+  if constexpr (BK == 64) return (row & 7) ^ ((row >> 3) & 1);
+  else return (row >> 2) & 3;
+}
+// Workgroup barrier for the K pipeline.  __syncthreads() carries a release
+// fence, which makes the compiler wait for ALL outstanding loads (vmcnt(0)),
+// the LDS-DMA loads of later stages included, and that would serialise the
+// prefetch.  Instead: wait explicitly for what this stage needs (the
+// s_waitcnt immediate kImm), then a bare s_barrier.  LDS has no cache, so a DMA write
+// is visible to every wave once it has been counted down.  The empty asm
+// statements stop the compiler from moving LDS accesses across the barrier.
+template <int kImm>
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt(kImm);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int BK>
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * BK + ((chunk ^ (row & 7)) << 3);
+  return row * BK + ((chunk ^ swz_key<BK>(row)) << 3);
 }
 
 __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int &tm,
@@ -53,48 +92,65 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
   tn = in_group / gsize;
 }
 
+// Raw buffer resource over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  const int32_t n = int32_t(bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : (bytes < 0 ? 0 : bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
+}
+
+// One 256 x 256 output tile per workgroup.  K streams through two LDS stages
+// (BK = 64 each) fed from two register stages: slice s is requested from
+// global memory (raw buffer loads into VGPRs) two iterations before it is
+// multiplied, written to LDS one iteration before, and read back as MFMA
+// fragments while it is multiplied.  Plain loads plus ds_write move about a
+// third more data into LDS per unit time than gfx950's LDS-DMA loads do
+// here, and the VGPRs they need are free: the accumulators sit in AGPRs.
 __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
     int M, int N, int K, int tiles_m, int tiles_n) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  constexpr int BK = 64;
+  constexpr int kStageElems = (BM + BN) * BK;      // bf16 elements per LDS stage
+  constexpr int kChunks = BK / 8;                  // 16-byte chunks per tile row
+  constexpr int kRowStep = kThreads / kChunks;     // rows covered per load round
+  constexpr int kLoads = BM / kRowStep;            // loads per operand per thread
+  constexpr int kKsub = BK / 16;                   // MFMA k sub-steps per stage
+  extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
 
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  // Global -> LDS mapping: thread owns chunk (tid % 8) of rows tid/8 + 32 i.
-  const int lchunk = tid & (kChunks - 1);
-  const int lrow = tid / kChunks;
-  const uint16_t *a_src[kLoadsPerThread];
-  const uint16_t *b_src[kLoadsPerThread];
-#pragma unroll
-  for (int i = 0; i < kLoadsPerThread; ++i) {
-    const int r = lrow + i * (kThreads / kChunks);
-    const int ar = min(m0 + r, M - 1), br = min(n0 + r, N - 1);   // ragged edges: clamp
-    a_src[i] = A + int64_t(ar) * K + lchunk * 8;
-    b_src[i] = B + int64_t(br) * K + lchunk * 8;
-  }
+  // Global -> VGPR: thread owns logical chunk (tid % 8) of rows tid/8 + 32 i.
+  // The buffer resources start at the tile's first row, so rows past M (or N)
+  // read as zeros.
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + int64_t(m0) * K, int64_t(M - m0) * K * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + int64_t(n0) * K, int64_t(N - n0) * K * 2);
+  const int lrow = tid / kChunks, lchunk = tid % kChunks;
+  const uint32_t voff = uint32_t(lrow * K + lchunk * 8) * 2;
+  const uint32_t row_step = uint32_t(kRowStep * K) * 2;
 
-  u32x4 ra[kLoadsPerThread], rb[kLoadsPerThread];
-  auto load_global = [&](int k0) {
+  u32x4 ga[2][kLoads], gb[2][kLoads];
+  auto load_global = [&](int set, int k0) {
 #pragma unroll
-    for (int i = 0; i < kLoadsPerThread; ++i) {
-      ra[i] = *reinterpret_cast<const u32x4 *>(a_src[i] + k0);
-      rb[i] = *reinterpret_cast<const u32x4 *>(b_src[i] + k0);
+    for (int i = 0; i < kLoads; ++i) {
+      const int soff = int(i * row_step) + k0 * 2;
+      ga[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, voff, soff, 0));
+      gb[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, voff, soff, 0));
     }
   };
-  auto store_lds = [&](int stage) {
+  auto store_lds = [&](int set, int stage) {
     uint16_t *sa = smem + stage * kStageElems;
     uint16_t *sb = sa + BM * BK;
 #pragma unroll
-    for (int i = 0; i < kLoadsPerThread; ++i) {
-      const int r = lrow + i * (kThreads / kChunks);
-      *reinterpret_cast<u32x4 *>(sa + swz(r, lchunk)) = ra[i];
-      *reinterpret_cast<u32x4 *>(sb + swz(r, lchunk)) = rb[i];
+    for (int i = 0; i < kLoads; ++i) {
+      const int r = lrow + i * kRowStep;
+      *reinterpret_cast<u32x4 *>(sa + swz<BK>(r, lchunk)) = ga[set][i];
+      *reinterpret_cast<u32x4 *>(sb + swz<BK>(r, lchunk)) = gb[set][i];
     }
   };
 
@@ -114,35 +170,92 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     const int chunk = 2 * ks + fhalf;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      fa[slot][i] = *reinterpret_cast<const bf16x8 *>(sa + swz(wm * 128 + i * 32 + frow, chunk));
+      fa[slot][i] =
+          *reinterpret_cast<const bf16x8 *>(sa + swz<BK>(wm * 128 + i * 32 + frow, chunk));
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      fb[slot][j] = *reinterpret_cast<const bf16x8 *>(sb + swz(wn * 128 + j * 32 + frow, chunk));
+      fb[slot][j] =
+          *reinterpret_cast<const bf16x8 *>(sb + swz<BK>(wn * 128 + j * 32 + frow, chunk));
+  };
+  auto mfma_block = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j],
+                                                            acc[i][j], 0, 0, 0);
+  };
+  // Scheduling patterns for one sub-step (16 MFMAs, 8 fragment reads), with
+  // the global loads (16) or the LDS writes (16) of the pipeline spread over it.
+  auto sched_reads = [&]() {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+    }
+  };
+  auto sched_reads_vmem = [&]() {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+    }
+  };
+  auto sched_reads_dswrite = [&]() {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+    }
   };
 
+  // One iteration multiplies slice kt from LDS stage kt % 2 and
+  //  - requests slice kt + 2 into register set kt % 2 (sub-step 0),
+  //  - waits for slice kt + 1 (issued one iteration earlier, so vmcnt may
+  //    keep the 2 * kLoads newer loads in flight) and writes it to LDS stage
+  //    (kt + 1) % 2 (sub-step 2).  That stage was last read in iteration
+  //    kt - 1, and every wave passed the barrier after it,
+  //  - waits for its LDS traffic and meets the other waves at the barrier,
+  //    after which stage (kt + 1) % 2 is complete,
+  //  - reads the first fragments of slice kt + 1 while the last sub-step of
+  //    slice kt multiplies.
+  // Requests past the end re-read the final K slice (in bounds, never used).
   const int nk = K / BK;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
+  auto iteration = [&](int kt, const int set) {
+    const int stage = set;                          // kt % 2, as a compile-time value
+    load_global(set, min(kt + 2, nk - 1) * BK);
+    load_frags(stage, 1, 1);
+    mfma_block(0);
+    sched_reads_vmem();
+    load_frags(stage, 2, 0);
+    mfma_block(1);
+    sched_reads();
+    __builtin_amdgcn_s_waitcnt(waitcnt(2 * kLoads, 15));
+    store_lds(set ^ 1, stage ^ 1);
+    load_frags(stage, 3, 1);
+    mfma_block(0);
+    sched_reads_dswrite();
+    stage_barrier<waitcnt(2 * kLoads, 0)>();
+    load_frags(stage ^ 1, 0, 0);
+    mfma_block(1);
+    sched_reads();
+  };
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int stage = kt & 1;
-    if (kt + 1 < nk) load_global((kt + 1) * BK);
-    load_frags(stage, 0, 0);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < BK / 16) load_frags(stage, ks + 1, cur ^ 1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j],
-                                                              acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store_lds(stage ^ 1);
-    __syncthreads();
+  load_global(0, 0);
+  load_global(1, min(1, nk - 1) * BK);
+  __builtin_amdgcn_s_waitcnt(waitcnt(2 * kLoads, 15));
+  store_lds(0, 0);
+  stage_barrier<waitcnt(2 * kLoads, 0)>();
+  load_frags(0, 0, 0);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    iteration(kt, 0);
+    iteration(kt + 1, 1);
   }
+  if (kt < nk) iteration(kt, 0);
+  __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
 
   // Epilogue: accumulator r of a 32x32 tile is row 8*(r/4) + 4*(lane/32) + r%4,
   // column lane % 32.
@@ -165,13 +278,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
 hipError_t launch_project(const uint16_t *a, const uint16_t *w, uint16_t *c, int32_t M,
                           int32_t K, int32_t N, hipStream_t stream) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const size_t lds = 2 * kStageElems * sizeof(uint16_t);
+  const size_t lds = size_t(2) * (BM + BN) * 64 * sizeof(uint16_t);
+  const void *fn = reinterpret_cast<const void *>(&gemm_nt_kernel);
   // Set on every call: the attribute is per device, and the call is cheap.
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_nt_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gemm_nt_kernel, dim3(tiles_m * tiles_n), dim3(kThreads), lds, stream,
-                     a, w, c, M, N, K, tiles_m, tiles_n);
+  hipLaunchKernelGGL(gemm_nt_kernel, dim3(tiles_m * tiles_n), dim3(kThreads), lds, stream, a,
+                     w, c, M, N, K, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
