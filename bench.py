@@ -31,7 +31,28 @@ sys.path.insert(0, ROOT)
 METRIC = "Engram forward tokens/s at T=8192 (1 GPU); % HBM roofline gather+gate, % MFMA GEMM"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published (no sparsity)
-CPU_SAMPLE_TOKENS = 2048       # one whole 2048-token sequence of the workload
+CPU_SAMPLE_TOKENS = 8192       # whole sequences of the workload, up to this many tokens
+
+
+def profiled_traffic(profile: str) -> int | None:
+    """HBM bytes per launch from a committed rocprofv3 summary, or None.
+
+    The summary records the FETCH_SIZE + WRITE_SIZE bytes (copy-calibrated)
+    and the sha256 of the kernel source it was taken on; a different source
+    today means the number is stale, so none is reported.
+    """
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", profile)
+    try:
+        text = open(path).read()
+        traffic = int(re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M).group(1))
+        src = re.search(r"^source: (\S+)$", text, re.M).group(1)
+        sha = re.search(r"^source_sha256: ([0-9a-f]+)$", text, re.M).group(1)
+        now = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
+    except (OSError, AttributeError, ValueError):
+        return None
+    return traffic if now == sha else None
 
 
 def log(msg: str) -> None:
@@ -57,7 +78,7 @@ def algorithmic(spec, token_mask) -> dict:
 
 
 def cpu_baseline(wl) -> dict:
-    """The oracle, as it stands, on the first CPU_SAMPLE_TOKENS tokens (one sequence)."""
+    """The oracle, as it stands, on the workload's first whole sequences (<= CPU_SAMPLE_TOKENS)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -65,17 +86,20 @@ def cpu_baseline(wl) -> dict:
     except Exception:
         threads = len(os.sched_getaffinity(0))
     s = wl.spec
-    n = min(CPU_SAMPLE_TOKENS, s.T)
-    cu = np.array([0, n], dtype=np.int32)
+    cu = [int(c) for c in wl.cu_seqlens]
+    n_seq = max(1, max(i for i in range(1, len(cu)) if cu[i] <= CPU_SAMPLE_TOKENS or i == 1))
+    n = cu[n_seq]
     sl = slice(0, n)
+    opt = lambda a: None if a is None else a[sl]
     t0 = time.perf_counter()
-    oracle.forward(wl.h[sl], wl.cids[sl], cu, wl.hash_params, [l.as_dict() for l in wl.layers],
-                   s.eps, s.clamp, s.dot_scale,
-                   doc_ids=None if wl.doc_ids is None else wl.doc_ids[sl],
-                   token_mask=None if wl.token_mask is None else wl.token_mask[sl])
+    oracle.forward(wl.h[sl], wl.cids[sl], np.array(cu[:n_seq + 1], dtype=np.int32),
+                   wl.hash_params, [l.as_dict() for l in wl.layers], s.eps, s.clamp,
+                   s.dot_scale, doc_ids=opt(wl.doc_ids), token_mask=opt(wl.token_mask),
+                   lookback=None if wl.lookback is None else wl.lookback[:n_seq],
+                   lookback_live=None if wl.lookback_live is None else wl.lookback_live[:n_seq])
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {n} tokens (one sequence) of the {s.name} workload, whole "
+            "sample": f"first {n} tokens ({n_seq} sequences) of the {s.name} workload, whole "
                       f"forward (hash, rows, projection, gate) in float64 numpy; {dt:.1f} s"}
 
 
@@ -86,6 +110,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES (for scaling "
+                         "the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the Engram forward here runs on a single "
@@ -93,6 +120,14 @@ def main() -> int:
         return 2
 
     import torch
+    if args.calibrate_copy:
+        src = torch.ones(args.calibrate_copy, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": args.calibrate_copy}), flush=True)
+        return 0
     import workloads
     from workloads.device import to_device
     from gram_hash_memory_amd.build import LIB, build
@@ -190,6 +225,9 @@ def main() -> int:
     gg_gbs = gg_bytes / (gg_ms * 1e-3) / 1e9
     ms_per_step = elapsed * 1e3 / args.steps
 
+    def prof(name):
+        return profiled_traffic(name) if args.config == 2 else None
+
     result = {
         "metric": METRIC,
         "value": s.T * args.steps / elapsed,
@@ -210,23 +248,27 @@ def main() -> int:
                    "T": s.T, "K": s.K, "N": s.N, "row_format": s.fmt},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": prof("gemm_nt_prefill_T8192.md"),
                      "kernel": "gemm_nt_kernel (engram_project)",
                      "per_launch_ms": round(per_launch_ms["project"], 4)},
         "stages": {
             "hash": {"ms": round(per_launch_ms["hash"], 4), "bound": "alu",
-                     "hbm_gbs": round(hash_gbs, 1)},
+                     "hbm_gbs": round(hash_gbs, 1),
+                     "traffic": prof("hash_prefill_T8192.md")},
             "rows": {"ms": round(per_launch_ms["rows"], 4), "bound": "hbm",
                      "achieved_gbs": round(rows_gbs, 1),
                      "frac": round(rows_gbs / HBM_PEAK_GBS, 4),
-                     "bytes_per_launch": alg["rows"]},
+                     "bytes_per_launch": alg["rows"],
+                     "traffic": prof("rows_q2k_prefill_T8192.md")},
             "project": {"ms": round(per_launch_ms["project"], 4), "bound": "mfma",
                         "achieved_tflops": round(gemm_tflops, 1),
                         "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4)},
             "gate": {"ms": round(per_launch_ms["gate"], 4), "bound": "hbm",
                      "achieved_gbs": round(gate_gbs, 1),
                      "frac": round(gate_gbs / HBM_PEAK_GBS, 4),
-                     "bytes_per_launch": alg["gate"]},
+                     "bytes_per_launch": alg["gate"],
+                     "traffic": prof("gate_prefill_T8192.md")},
             "gather_plus_gate": {"ms": round(gg_ms, 4), "achieved_gbs": round(gg_gbs, 1),
                                  "frac": round(gg_gbs / HBM_PEAK_GBS, 4)},
             "engram_forward_ms": round(forward_ms, 4),
