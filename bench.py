@@ -5,10 +5,12 @@
 A step is one pass of the whole hot path over the batch: the hash for every
 layer, then per layer the row gather, the projection and the gate.  The
 inputs are resident in HBM before timing starts.  The timed region issues the
-same four C-ABI calls that engram_forward composes, on one stream, and
-records HIP events between the stages.  Each kernel's average duration
-therefore comes from the timed run itself.  engram_forward is then timed on
-its own for reference.
+same C-ABI calls that engram_forward makes, in its order, on one stream, and
+records HIP events between them, so each kernel's average duration comes from
+the timed run itself.  For Q2_K tables that is engram_project_q2k (row gather
+and projection fused into one kernel); the two-kernel path it replaces
+(engram_rows, engram_project) is timed after the steps for comparison, as is
+engram_forward itself.
 
 Prints ONE JSON line: the headline metric, plus `roofline` for the dominant
 kernel (the bf16 MFMA projection), `stages` for every kernel, and
@@ -31,6 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "Engram forward tokens/s at T=8192 (1 GPU); % HBM roofline gather+gate, % MFMA GEMM"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published (no sparsity)
+Q2K_FUSED_MAX_BYTES = 2147483504   # engram.h: ENGRAM_Q2K_FUSED_MAX_BYTES
 CPU_SAMPLE_TOKENS = 8192       # whole sequences of the workload, up to this many tokens
 
 
@@ -130,9 +133,8 @@ def main() -> int:
         return 0
     import workloads
     from workloads.device import to_device
-    from gram_hash_memory_amd.build import LIB, build
-    if not os.path.exists(LIB):
-        build()
+    import __graft_entry__
+    __graft_entry__._ensure_built()
     import gram_hash_memory_amd as eg
 
     t0 = time.perf_counter()
@@ -154,33 +156,53 @@ def main() -> int:
     rows = torch.empty((s.T, s.K), dtype=torch.int16, device="cuda")
     kv = torch.empty((s.T, s.N), dtype=torch.int16, device="cuda")
     num_rows = [l.table.numel() // (84 if fmt == eg.ENGRAM_ROWS_Q2K else 256) for l in dw.layers]
+    # The fused Q2_K rows+projection kernel, as engram_forward picks it.
+    fused = fmt == eg.ENGRAM_ROWS_Q2K and all(n * 84 <= Q2K_FUSED_MAX_BYTES for n in num_rows)
+
+    def layer_ids(l):
+        return ids.view(-1)[l * s.cols:]
+
+    def rows_call(l):
+        dl = dw.layers[l]
+        eg.engram_rows(fmt, dl.table, dl.scales, num_rows[l], layer_ids(l), L * s.cols, s.cols,
+                       s.T, rows, None, stream)
+
+    def project_call(l):
+        eg.engram_project(rows, dw.layers[l].wkv, kv, s.T, s.K, s.N, stream)
+
+    def fused_call(l):
+        dl = dw.layers[l]
+        eg.engram_project_q2k(dl.table, num_rows[l], layer_ids(l), L * s.cols, s.cols, dl.wkv,
+                              kv, s.T, s.N, None, stream)
+
+    def gate_call(l):
+        dl = dw.layers[l]
+        eg.engram_gate(h, kv, dl.q_weight, dl.k_weight, dw.token_mask, s.T, s.hc, s.dim, s.eps,
+                       s.clamp, s.dot_scale, stream)
+
+    # One step = the launches engram_forward makes, in its order.
+    plan = [("hash", lambda: eg.engram_hash(params, tokens, ids, stream))]
+    for l in range(L):
+        if fused:
+            plan.append(("rows_project", lambda l=l: fused_call(l)))
+        else:
+            plan += [("rows", lambda l=l: rows_call(l)), ("project", lambda l=l: project_call(l))]
+        plan.append(("gate", lambda l=l: gate_call(l)))
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        eg.engram_hash(params, tokens, ids, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        for l, dl in enumerate(dw.layers):
-            eg.engram_rows(fmt, dl.table, dl.scales, num_rows[l], ids.view(-1)[l * s.cols:],
-                           L * s.cols, s.cols, s.T, rows, None, stream)
+        for i, (_, fn) in enumerate(plan):
+            fn()
             if ev is not None:
-                ev[2 + 3 * l].record(stream)
-            eg.engram_project(rows, dl.wkv, kv, s.T, s.K, s.N, stream)
-            if ev is not None:
-                ev[3 + 3 * l].record(stream)
-            eg.engram_gate(h, kv, dl.q_weight, dl.k_weight, dw.token_mask, s.T, s.hc, s.dim,
-                           s.eps, s.clamp, s.dot_scale, stream)
-            if ev is not None:
-                ev[4 + 3 * l].record(stream)
+                ev[i + 1].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"bench: {args.warmup} warmup steps done; timing {args.steps} steps")
 
-    n_ev = 2 + 3 * L
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(plan) + 1)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -189,44 +211,91 @@ def main() -> int:
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
 
-    dur = {"hash": 0.0, "rows": 0.0, "project": 0.0, "gate": 0.0}
+    total, count = {}, {}
     for ev in events:
-        dur["hash"] += ev[0].elapsed_time(ev[1])
-        for l in range(L):
-            dur["rows"] += ev[1 + 3 * l].elapsed_time(ev[2 + 3 * l])
-            dur["project"] += ev[2 + 3 * l].elapsed_time(ev[3 + 3 * l])
-            dur["gate"] += ev[3 + 3 * l].elapsed_time(ev[4 + 3 * l])
-    per_launch_ms = {"hash": dur["hash"] / args.steps}
-    for k in ("rows", "project", "gate"):
-        per_launch_ms[k] = dur[k] / (args.steps * L)
+        for i, (name, _) in enumerate(plan):
+            total[name] = total.get(name, 0.0) + ev[i].elapsed_time(ev[i + 1])
+            count[name] = count.get(name, 0) + 1
+    per_launch_ms = {k: total[k] / count[k] for k in total}
 
-    # engram_forward itself (same kernels), for reference
+    def time_alone(fn, n):
+        """Average ms of n back-to-back launches of fn (outside the timed steps)."""
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    n_ref = max(3, args.steps // 2)
+    if fused:
+        # The two-kernel path the fused kernel replaces, for comparison (the
+        # row gather is also a C-ABI entry point of its own).
+        per_launch_ms["rows"] = time_alone(lambda: rows_call(0), n_ref)
+        per_launch_ms["project"] = time_alone(lambda: project_call(0), n_ref)
     ws = torch.empty(eg.engram_workspace_bytes(s.T, L, s.cols, s.hc, s.dim), dtype=torch.uint8,
                      device="cuda")
-    fe0, fe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    eg.engram_forward(params, tokens, layers, h, s.hc, s.dim, s.eps, s.clamp, s.dot_scale, ws,
-                      None, stream)
-    fe0.record(stream)
-    n_fwd = max(3, args.steps // 2)
-    for _ in range(n_fwd):
-        eg.engram_forward(params, tokens, layers, h, s.hc, s.dim, s.eps, s.clamp, s.dot_scale,
-                          ws, None, stream)
-    fe1.record(stream)
-    torch.cuda.synchronize()
-    forward_ms = fe0.elapsed_time(fe1) / n_fwd
+    forward_ms = time_alone(lambda: eg.engram_forward(params, tokens, layers, h, s.hc, s.dim,
+                                                      s.eps, s.clamp, s.dot_scale, ws, None,
+                                                      stream), n_ref)
 
     alg = algorithmic(s, wl.token_mask)
-    gemm_tflops = alg["project"] / (per_launch_ms["project"] * 1e-3) / 1e12
-    rows_gbs = alg["rows"] / (per_launch_ms["rows"] * 1e-3) / 1e9
-    gate_gbs = alg["gate"] / (per_launch_ms["gate"] * 1e-3) / 1e9
-    hash_gbs = alg["hash"] / (per_launch_ms["hash"] * 1e-3) / 1e9
-    gg_bytes = alg["rows"] + alg["gate"]
+
+    def tflops(ms):
+        return alg["project"] / (ms * 1e-3) / 1e12
+
+    def gbs(nbytes, ms):
+        return nbytes / (ms * 1e-3) / 1e9
+
     gg_ms = per_launch_ms["rows"] + per_launch_ms["gate"]
-    gg_gbs = gg_bytes / (gg_ms * 1e-3) / 1e9
+    gg_gbs = gbs(alg["rows"] + alg["gate"], gg_ms)
     ms_per_step = elapsed * 1e3 / args.steps
 
     def prof(name):
         return profiled_traffic(name) if args.config == 2 else None
+
+    if fused:
+        dom_name, dom_kernel = "rows_project", "gemm_q2k_kernel (engram_project_q2k)"
+        dom_prof = "gemm_q2k_prefill_T8192.md"
+    else:
+        dom_name, dom_kernel = "project", "gemm_nt_kernel (engram_project)"
+        dom_prof = "gemm_nt_prefill_T8192.md"
+    dom_tf = tflops(per_launch_ms[dom_name])
+    stages = {
+        "hash": {"ms": round(per_launch_ms["hash"], 4), "bound": "alu",
+                 "hbm_gbs": round(gbs(alg["hash"], per_launch_ms["hash"]), 1),
+                 "traffic": prof("hash_prefill_T8192.md")},
+    }
+    if fused:
+        stages["rows_project"] = {
+            "ms": round(per_launch_ms["rows_project"], 4), "bound": "mfma",
+            "achieved_tflops": round(dom_tf, 1), "frac": round(dom_tf / BF16_PEAK_TFLOPS, 4),
+            "traffic": prof(dom_prof)}
+    rows_gbs = gbs(alg["rows"], per_launch_ms["rows"])
+    proj_tf = tflops(per_launch_ms["project"])
+    stages["rows"] = {"ms": round(per_launch_ms["rows"], 4), "bound": "hbm",
+                      "achieved_gbs": round(rows_gbs, 1),
+                      "frac": round(rows_gbs / HBM_PEAK_GBS, 4),
+                      "bytes_per_launch": alg["rows"],
+                      "traffic": prof("rows_q2k_prefill_T8192.md"),
+                      "in_step": not fused}
+    stages["project"] = {"ms": round(per_launch_ms["project"], 4), "bound": "mfma",
+                         "achieved_tflops": round(proj_tf, 1),
+                         "frac": round(proj_tf / BF16_PEAK_TFLOPS, 4),
+                         "traffic": prof("gemm_nt_prefill_T8192.md"),
+                         "in_step": not fused}
+    gate_gbs = gbs(alg["gate"], per_launch_ms["gate"])
+    stages["gate"] = {"ms": round(per_launch_ms["gate"], 4), "bound": "hbm",
+                      "achieved_gbs": round(gate_gbs, 1),
+                      "frac": round(gate_gbs / HBM_PEAK_GBS, 4),
+                      "bytes_per_launch": alg["gate"],
+                      "traffic": prof("gate_prefill_T8192.md")}
+    stages["gather_plus_gate"] = {"ms": round(gg_ms, 4), "achieved_gbs": round(gg_gbs, 1),
+                                  "frac": round(gg_gbs / HBM_PEAK_GBS, 4),
+                                  "kernels": "engram_rows + engram_gate"}
+    stages["engram_forward_ms"] = round(forward_ms, 4)
 
     result = {
         "metric": METRIC,
@@ -246,33 +315,13 @@ def main() -> int:
                                f"{s.num_rows} rows, dim={s.dim}, hc={s.hc}, "
                                f"{s.id_dist} ids",
                    "T": s.T, "K": s.K, "N": s.N, "row_format": s.fmt},
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1),
+        "roofline": {"bound": "mfma", "achieved": round(dom_tf, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": prof("gemm_nt_prefill_T8192.md"),
-                     "kernel": "gemm_nt_kernel (engram_project)",
-                     "per_launch_ms": round(per_launch_ms["project"], 4)},
-        "stages": {
-            "hash": {"ms": round(per_launch_ms["hash"], 4), "bound": "alu",
-                     "hbm_gbs": round(hash_gbs, 1),
-                     "traffic": prof("hash_prefill_T8192.md")},
-            "rows": {"ms": round(per_launch_ms["rows"], 4), "bound": "hbm",
-                     "achieved_gbs": round(rows_gbs, 1),
-                     "frac": round(rows_gbs / HBM_PEAK_GBS, 4),
-                     "bytes_per_launch": alg["rows"],
-                     "traffic": prof("rows_q2k_prefill_T8192.md")},
-            "project": {"ms": round(per_launch_ms["project"], 4), "bound": "mfma",
-                        "achieved_tflops": round(gemm_tflops, 1),
-                        "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4)},
-            "gate": {"ms": round(per_launch_ms["gate"], 4), "bound": "hbm",
-                     "achieved_gbs": round(gate_gbs, 1),
-                     "frac": round(gate_gbs / HBM_PEAK_GBS, 4),
-                     "bytes_per_launch": alg["gate"],
-                     "traffic": prof("gate_prefill_T8192.md")},
-            "gather_plus_gate": {"ms": round(gg_ms, 4), "achieved_gbs": round(gg_gbs, 1),
-                                 "frac": round(gg_gbs / HBM_PEAK_GBS, 4)},
-            "engram_forward_ms": round(forward_ms, 4),
-        },
+                     "frac": round(dom_tf / BF16_PEAK_TFLOPS, 4),
+                     "traffic": prof(dom_prof),
+                     "kernel": dom_kernel,
+                     "per_launch_ms": round(per_launch_ms[dom_name], 4)},
+        "stages": stages,
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")

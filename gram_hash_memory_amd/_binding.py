@@ -28,11 +28,11 @@ ENGRAM_OK, ENGRAM_ERR_ARG, ENGRAM_ERR_UNSUPPORTED, ENGRAM_ERR_HIP = 0, 1, 2, 3
 ENGRAM_ROWS_Q2K, ENGRAM_ROWS_FP8_E4M3_E8M0 = 0, 1
 HEAD_DIM, Q2K_ROW_BYTES, FP8_ROW_BYTES, FP8_SCALE_BYTES = 256, 84, 256, 8
 
-EXPORTS = ("engram_hash", "engram_rows", "engram_project", "engram_gate",
+EXPORTS = ("engram_hash", "engram_rows", "engram_project", "engram_project_q2k", "engram_gate",
            "engram_workspace_bytes", "engram_forward", "engram_last_error")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m gram_hash_memory_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built; run `python gram_hash_memory_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
 
 
@@ -60,6 +60,8 @@ _lib.engram_rows.argtypes = [c_int, c_void_p, c_void_p, c_int64, c_void_p, c_int
                              c_int32, c_void_p, c_void_p, c_void_p]
 _lib.engram_project.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                 c_void_p]
+_lib.engram_project_q2k.argtypes = [c_void_p, c_int64, c_void_p, c_int64, c_int32, c_void_p,
+                                    c_void_p, c_int32, c_int32, c_void_p, c_void_p]
 _lib.engram_gate.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                              c_int32, c_int32, c_float, c_float, c_float, c_void_p]
 _lib.engram_workspace_bytes.argtypes = [c_int32, c_int32, c_int32, c_int32, c_int32]
@@ -68,7 +70,8 @@ _lib.engram_forward.argtypes = [_P(_HashParams), _P(_Tokens), _P(_Layer), c_void
                                 c_int32, c_float, c_float, c_float, c_void_p, c_size_t,
                                 c_void_p, c_void_p]
 _lib.engram_last_error.restype = c_char_p
-for _name in ("engram_hash", "engram_rows", "engram_project", "engram_gate", "engram_forward"):
+for _name in ("engram_hash", "engram_rows", "engram_project", "engram_project_q2k", "engram_gate",
+              "engram_forward"):
     getattr(_lib, _name).restype = c_int
 
 
@@ -179,6 +182,19 @@ def engram_project(rows, wkv, kv, T: int, K: int, N: int, stream=None) -> None:
                                _dptr(wkv, torch.int16, N * K, "wkv"),
                                _dptr(kv, torch.int16, T * N, "kv"), int(T), int(K), int(N),
                                _stream(stream)))
+
+
+def engram_project_q2k(table, num_rows: int, ids, ids_token_stride: int, cols: int, wkv, kv,
+                       T: int, N: int, bad_ids=None, stream=None) -> None:
+    """Stages 2 + 3 fused for a Q2_K table: kv [T, N] from ids, bit-identical
+    to engram_rows followed by engram_project."""
+    K = cols * HEAD_DIM
+    need_ids = 0 if T <= 0 else (T - 1) * ids_token_stride + cols
+    _check(_lib.engram_project_q2k(
+        _dptr(table, torch.uint8, num_rows * Q2K_ROW_BYTES, "table"), int(num_rows),
+        _dptr(ids, torch.int32, need_ids, "ids"), int(ids_token_stride), int(cols),
+        _dptr(wkv, torch.int16, N * K, "wkv"), _dptr(kv, torch.int16, T * N, "kv"), int(T),
+        int(N), _dptr(bad_ids, torch.int32, 1, "bad_ids"), _stream(stream)))
 
 
 def engram_gate(h, kv, q_weight, k_weight, token_mask, T: int, hc: int, dim: int, eps: float,

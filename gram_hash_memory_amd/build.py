@@ -1,6 +1,8 @@
 """Build libengram.so in-tree with hipcc for gfx950.
 
-    python -m gram_hash_memory_amd.build          # or: python gram_hash_memory_amd/build.py
+    python gram_hash_memory_amd/build.py
+
+(not `python -m`: importing the package loads the library this builds)
 
 Each HIP source is compiled to an object file under _build/, in parallel, and
 the objects are linked into gram_hash_memory_amd/libengram.so.  No GPU is
@@ -20,7 +22,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libengram.so")
-SOURCES = ["api.cpp", "hash.hip", "rows.hip", "gemm.hip", "gate.hip"]
+SOURCES = ["api.cpp", "hash.hip", "rows.hip", "gemm.hip", "gemm_q2k.hip", "gate.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

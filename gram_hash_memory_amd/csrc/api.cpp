@@ -188,6 +188,31 @@ engram_status engram_project(const uint16_t *rows, const uint16_t *wkv, uint16_t
                     "engram_project launch");
 }
 
+engram_status engram_project_q2k(const uint8_t *table, int64_t num_rows, const int32_t *ids,
+                                 int64_t ids_token_stride, int32_t cols, const uint16_t *wkv,
+                                 uint16_t *kv, int32_t T, int32_t N, int32_t *bad_ids,
+                                 hipStream_t stream) {
+  engram_status st = check_rows_shape(ENGRAM_ROWS_Q2K, num_rows, ids_token_stride, cols, T);
+  if (st != ENGRAM_OK) return st;
+  REQUIRE(int64_t(cols) * ENGRAM_HEAD_DIM <= kInt32Max, "cols=%d too large", cols);
+  const int32_t K = cols * ENGRAM_HEAD_DIM;
+  if ((st = check_project_shape(T, K, N)) != ENGRAM_OK) return st;
+  REQUIRE_SUP(cols <= ENGRAM_Q2K_FUSED_MAX_COLS, "cols=%d exceeds the fused kernel's %d", cols,
+              ENGRAM_Q2K_FUSED_MAX_COLS);
+  REQUIRE_SUP(engram::project_q2k_supported(num_rows, cols),
+              "Q2_K table of %lld rows exceeds the fused kernel's %lld bytes",
+              (long long)num_rows, (long long)ENGRAM_Q2K_FUSED_MAX_BYTES);
+  if (T == 0) return ENGRAM_OK;
+  REQUIRE(table && aligned(table, 4), "table is NULL or not 4-byte aligned");
+  REQUIRE(ids && aligned(ids, 4), "ids is NULL or misaligned");
+  REQUIRE(!bad_ids || aligned(bad_ids, 4), "bad_ids misaligned");
+  REQUIRE(wkv && kv && aligned(wkv, 16) && aligned(kv, 16),
+          "wkv or kv is NULL or not 16-byte aligned");
+  return hip_status(engram::launch_project_q2k(table, num_rows, ids, ids_token_stride, cols, wkv,
+                                               kv, T, N, bad_ids, stream),
+                    "engram_project_q2k launch");
+}
+
 engram_status engram_gate(float *h, const uint16_t *kv, const uint16_t *q_weight,
                           const uint16_t *k_weight, const uint8_t *token_mask, int32_t T,
                           int32_t hc, int32_t dim, float eps, float clamp, float dot_scale,
@@ -261,14 +286,22 @@ engram_status engram_forward(const engram_hash_params *params, const engram_toke
     return st;
   for (int l = 0; l < L; ++l) {
     const engram_layer &ly = layers[l];
-    if ((st = hip_status(engram::launch_rows(ly.fmt, ly.table, ly.scales, ly.num_rows,
-                                             ids + l * cols, int64_t(L) * cols, cols, T, rows,
-                                             bad_ids, stream),
-                         "rows launch")) != ENGRAM_OK)
-      return st;
-    if ((st = hip_status(engram::launch_project(rows, ly.wkv, kv, T, K, N, stream),
-                         "project launch")) != ENGRAM_OK)
-      return st;
+    if (ly.fmt == ENGRAM_ROWS_Q2K && engram::project_q2k_supported(ly.num_rows, cols)) {
+      if ((st = hip_status(engram::launch_project_q2k(ly.table, ly.num_rows, ids + l * cols,
+                                                      int64_t(L) * cols, cols, ly.wkv, kv, T,
+                                                      N, bad_ids, stream),
+                           "fused rows+project launch")) != ENGRAM_OK)
+        return st;
+    } else {
+      if ((st = hip_status(engram::launch_rows(ly.fmt, ly.table, ly.scales, ly.num_rows,
+                                               ids + l * cols, int64_t(L) * cols, cols, T, rows,
+                                               bad_ids, stream),
+                           "rows launch")) != ENGRAM_OK)
+        return st;
+      if ((st = hip_status(engram::launch_project(rows, ly.wkv, kv, T, K, N, stream),
+                           "project launch")) != ENGRAM_OK)
+        return st;
+    }
     if ((st = hip_status(engram::launch_gate(h, kv, ly.q_weight, ly.k_weight,
                                              tokens->token_mask, T, hc, dim, eps, clamp,
                                              dot_scale, stream),

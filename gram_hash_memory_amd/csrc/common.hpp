@@ -21,9 +21,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
-// Two fp32 -> packed bf16 pair (low half = a).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair (low half = a), both rounded to nearest even
+// by one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16);
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -53,6 +58,13 @@ hipError_t launch_rows(engram_row_format fmt, const uint8_t *table, const uint8_
 
 hipError_t launch_project(const uint16_t *a, const uint16_t *w, uint16_t *c, int32_t M,
                           int32_t K, int32_t N, hipStream_t stream);
+
+// Rows + projection fused for Q2_K tables (kv bit-identical to rows -> project).
+bool project_q2k_supported(int64_t num_rows, int32_t cols);
+hipError_t launch_project_q2k(const uint8_t *table, int64_t num_rows, const int32_t *ids,
+                              int64_t ids_token_stride, int32_t cols, const uint16_t *w,
+                              uint16_t *c, int32_t M, int32_t N, int32_t *bad_ids,
+                              hipStream_t stream);
 
 hipError_t launch_gate(float *h, const uint16_t *kv, const uint16_t *qw, const uint16_t *kw,
                        const uint8_t *mask, int32_t T, int32_t hc, int32_t dim, float eps,

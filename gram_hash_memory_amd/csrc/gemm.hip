@@ -20,83 +20,12 @@
 // which has its own L2.  The block id is remapped so that every XCD gets a
 // contiguous run of tiles, and that run walks 8 M-tiles before it moves along N.
 // The ~32 tiles an XCD has in flight then share their A and B panels in its L2.
-#include "common.hpp"
+#include "gemm_common.hpp"
 
 namespace engram {
 namespace {
 
-constexpr int BM = 256, BN = 256;
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr int kGroupM = 8;
-constexpr int kNumXcd = 8;
-// sched_group_barrier instruction classes.
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedVmemRead = 0x020;
-constexpr int kSchedDsRead = 0x100;
-constexpr int kSchedDsWrite = 0x200;
-
-// s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14,
-// expcnt 6:4 (left at max), lgkmcnt 11:8.
-constexpr int waitcnt(int vm, int lgkm) {
-  return (vm & 15) | (((vm >> 4) & 3) << 14) | (7 << 4) | ((lgkm & 15) << 8);
-}
-
-// LDS layout of one operand tile: BM rows of BK bf16, in 16-byte chunks.
-// gfx950's LDS serves a ds_read_b128 16 lanes per cycle across 64 banks.
-// Our fragment reads hit 16 consecutive rows at one logical chunk.  The
-// chunk is stored at (logical chunk) ^ key(row), and the key makes those 16
-// rows land on 16 distinct 16-byte bank groups:
-//   BK = 64 (8 chunks, 128 B rows): the bank group is (row % 2, chunk), so key
-//     = (row & 7) ^ ((row >> 3) & 1) is a bijection on the 8 even and on the
-//     8 odd rows;
-//   BK = 32 (4 chunks, 64 B rows): the bank group is (row % 4, chunk), so key
-//     = (row >> 2) & 3 is a bijection on each residue class mod 4.
-template <int BK>
-__device__ __forceinline__ int swz_key(int row) {
-  if constexpr (BK == 64) return (row & 7) ^ ((row >> 3) & 1);
-  else return (row >> 2) & 3;
-}
-// Workgroup barrier for the K pipeline.  __syncthreads() carries a release
-// fence, which makes the compiler wait for ALL outstanding loads (vmcnt(0)),
-// the LDS-DMA loads of later stages included, and that would serialise the
-// prefetch.  Instead: wait explicitly for what this stage needs (the
-// s_waitcnt immediate kImm), then a bare s_barrier.  LDS has no cache, so a DMA write
-// is visible to every wave once it has been counted down.  The empty asm
-// statements stop the compiler from moving LDS accesses across the barrier.
-template <int kImm>
-__device__ __forceinline__ void stage_barrier() {
-  __builtin_amdgcn_s_waitcnt(kImm);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-template <int BK>
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * BK + ((chunk ^ swz_key<BK>(row)) << 3);
-}
-
-__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int &tm,
-                                            int &tn) {
-  const int total = tiles_m * tiles_n;
-  const int xcd = bid % kNumXcd, pos = bid / kNumXcd;
-  const int base = total / kNumXcd, extra = total % kNumXcd;
-  const int lid = xcd * base + min(xcd, extra) + pos;
-  const int per_group = kGroupM * tiles_n;
-  const int group = lid / per_group;
-  const int first_m = group * kGroupM;
-  const int gsize = min(tiles_m - first_m, kGroupM);
-  const int in_group = lid - group * per_group;
-  tm = first_m + in_group % gsize;
-  tn = in_group / gsize;
-}
-
-// Raw buffer resource over [base, base + bytes): loads past the end return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
-  const int32_t n = int32_t(bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : (bytes < 0 ? 0 : bytes));
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
-}
+using namespace gemm;
 
 // One 256 x 256 output tile per workgroup.  K streams through two LDS stages
 // (BK = 64 each) fed from two register stages: slice s is requested from

@@ -189,6 +189,27 @@ ENGRAM_API engram_status engram_rows(engram_row_format fmt, const uint8_t *table
 ENGRAM_API engram_status engram_project(const uint16_t *rows, const uint16_t *wkv, uint16_t *kv,
                              int32_t T, int32_t K, int32_t N, hipStream_t stream);
 
+/* Stages 2 + 3 fused for Q2_K tables ([spark] overview stages 2-3): kv =
+ * bf16(dequant(table[ids])) x wkv^T without writing the bf16 rows to memory.
+ * The projection reads each row's 84-byte block and dequantises it on chip,
+ * so kv is bit for bit what engram_rows followed by engram_project gives
+ * (same values, same fp32 accumulation order).
+ *   table DEVICE Q2_K [num_rows][84], 4-byte aligned; ids, ids_token_stride,
+ *   cols, bad_ids as for engram_rows (K = cols * 256); wkv DEVICE bf16 [N][K];
+ *   kv DEVICE bf16 [T][N], 16-byte aligned, fully overwritten.
+ *   Limits: num_rows * 84 <= ENGRAM_Q2K_FUSED_MAX_BYTES (the blocks are read
+ *   through one 32-bit-offset buffer descriptor) and cols <=
+ *   ENGRAM_Q2K_FUSED_MAX_COLS (each workgroup keeps its rows' block offsets in
+ *   LDS); beyond either the call returns ENGRAM_ERR_UNSUPPORTED and
+ *   engram_forward uses rows -> projection instead.
+ */
+#define ENGRAM_Q2K_FUSED_MAX_BYTES 2147483504LL
+#define ENGRAM_Q2K_FUSED_MAX_COLS 32
+ENGRAM_API engram_status engram_project_q2k(const uint8_t *table, int64_t num_rows,
+                                 const int32_t *ids, int64_t ids_token_stride, int32_t cols,
+                                 const uint16_t *wkv, uint16_t *kv, int32_t T, int32_t N,
+                                 int32_t *bad_ids, hipStream_t stream);
+
 /* Stage 4 -- gate, in place on the fp32 highway ([spark] overview stage 4;
  * [NeMo] _engram_gate_core, compile_engram_gate; [vLLM] Engram).
  *   h DEVICE fp32 [T][hc][dim], updated in place.
@@ -214,6 +235,8 @@ ENGRAM_API size_t engram_workspace_bytes(int32_t T, int32_t n_layers, int32_t co
 
 /* The whole forward ([spark] overview, stages 1-4): hash every layer once,
  * then for each layer in order: rows -> projection -> gate on the same h.
+ * Q2_K layers within the limits of engram_project_q2k run rows -> projection
+ * as that fused kernel (same kv bits).
  *   layers: HOST array [params->n_layers] of DEVICE-pointer descriptors.
  *   workspace: DEVICE, at least engram_workspace_bytes(...) bytes, 256-byte
  *   aligned; its contents are scratch.  Every other argument is as for the

@@ -20,9 +20,8 @@ NO_GPU = not os.path.exists("/dev/kfd")
 
 @pytest.fixture(scope="module")
 def eg():
-    from gram_hash_memory_amd.build import LIB, build
-    if not os.path.exists(LIB):
-        build()
+    import __graft_entry__
+    __graft_entry__._ensure_built()
     import gram_hash_memory_amd
     return gram_hash_memory_amd
 
@@ -34,7 +33,7 @@ def declared_functions():
 
 def test_header_declares_the_five_calls_and_helpers():
     names = declared_functions()
-    for want in ("engram_hash", "engram_rows", "engram_project", "engram_gate",
+    for want in ("engram_hash", "engram_rows", "engram_project", "engram_project_q2k", "engram_gate",
                  "engram_forward", "engram_workspace_bytes", "engram_last_error"):
         assert want in names
 
@@ -94,6 +93,10 @@ def _raw(eg):
                                 ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.engram_project.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int32] * 3 + [ctypes.c_void_p]
+    lib.engram_project_q2k.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_void_p, ctypes.c_void_p]
     lib.engram_gate.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int32] * 3 +
                                 [ctypes.c_float] * 3 + [ctypes.c_void_p])
     return lib
@@ -175,6 +178,27 @@ class TestValidation:
                      (FAKE, FAKE + 8, FAKE, 8, 64, 64)):
             assert lib.engram_project(*args, None) == eg.ENGRAM_ERR_ARG, args
         assert lib.engram_project(None, None, None, 0, 64, 64, None) == eg.ENGRAM_OK
+
+    def test_project_q2k_rejects(self, eg):
+        lib = _raw(eg)
+        ok = dict(table=FAKE, nrows=100, ids=FAKE, stride=24, cols=24, wkv=FAKE, kv=FAKE, T=8,
+                  N=512, bad=None)
+
+        def call(**kw):
+            a = dict(ok, **kw)
+            return lib.engram_project_q2k(a["table"], a["nrows"], a["ids"], a["stride"],
+                                          a["cols"], a["wkv"], a["kv"], a["T"], a["N"],
+                                          a["bad"], None)
+        for kw in (dict(nrows=0), dict(cols=0), dict(stride=23), dict(T=-1), dict(N=0),
+                   dict(table=None), dict(table=FAKE + 2), dict(ids=None), dict(ids=FAKE + 1),
+                   dict(wkv=None), dict(wkv=FAKE + 8), dict(kv=FAKE + 8), dict(bad=FAKE + 2)):
+            assert call(**kw) == eg.ENGRAM_ERR_ARG, kw
+        # 2^31 / 84 rows and more no longer fit the kernel's 32-bit block offsets.
+        too_many = 2147483504 // 84 + 1
+        assert call(nrows=too_many) == eg.ENGRAM_ERR_UNSUPPORTED
+        assert "exceeds" in lib.engram_last_error().decode()
+        assert call(nrows=too_many - 1, T=0, table=None, ids=None, wkv=None,
+                    kv=None) == eg.ENGRAM_OK
 
     def test_gate_rejects(self, eg):
         lib = _raw(eg)

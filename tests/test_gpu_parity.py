@@ -31,10 +31,8 @@ _host, _dev, _ids = {}, {}, {}
 
 @pytest.fixture(scope="module")
 def eg():
-    import os
-    from gram_hash_memory_amd.build import LIB, build
-    if not os.path.exists(LIB):
-        build()
+    import __graft_entry__
+    __graft_entry__._ensure_built()
     import gram_hash_memory_amd
     torch.cuda.set_device(0)
     return gram_hash_memory_amd
@@ -210,6 +208,79 @@ def test_project_workloads_sampled(eg, c):
         rows_np = rows.cpu().numpy().view(np.uint16)[pick]
         got = kv.cpu().numpy().view(np.uint16)[pick]
         _check_kv(got, rows_np, wl.layers[layer].wkv)
+
+
+# ------------------------------------------------- rows + projection, fused (Q2_K)
+
+Q2K_CONFIGS = [c for c in CONFIGS if workloads.SPECS[c].fmt == "q2k"]
+
+
+@pytest.mark.parametrize("c", Q2K_CONFIGS)
+def test_project_q2k_bit_identical_to_rows_then_project(eg, c):
+    # Same bf16 operands, same MFMA order: the fused kernel's kv must equal the
+    # two-kernel path's bit for bit on the whole output, at the full size.
+    wl = host(c)
+    s = wl.spec
+    for layer in range(len(s.layer_ids)):
+        ids, rows = gpu_rows(eg, c, layer, eg.ENGRAM_ROWS_Q2K)
+        L = dev(c).layers[layer]
+        kv_two = torch.empty((s.T, s.N), dtype=torch.int16, device="cuda")
+        eg.engram_project(rows, L.wkv, kv_two, s.T, s.K, s.N)
+        kv = torch.full((s.T, s.N), 0x7777, dtype=torch.int16, device="cuda")
+        bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+        eg.engram_project_q2k(L.table, L.table.numel() // 84, ids.view(-1)[layer * s.cols:],
+                              len(s.layer_ids) * s.cols, s.cols, L.wkv, kv, s.T, s.N, bad)
+        assert bad.item() == 0
+        diff = int((kv != kv_two).sum().item())
+        assert diff == 0, f"layer {layer}: {diff} kv values differ"
+        pick = sample_tokens(wl)
+        want_rows = oracle.rows_q2k(wl.layers[layer].table, oracle_ids(c)[pick, layer])
+        _check_kv(kv.cpu().numpy().view(np.uint16)[pick], want_rows, wl.layers[layer].wkv)
+
+
+@pytest.mark.parametrize("T,cols,N", [(1, 1, 64), (3, 3, 320), (255, 5, 520), (257, 6, 256),
+                                      (300, 24, 4096), (513, 2, 1000)])
+def test_project_q2k_ragged_and_bad_ids(eg, T, cols, N):
+    # Ragged tiles in M and N, an odd column count (the kernel's half-unrolled
+    # tail), and ids outside the table: zero rows, counted once per (token,
+    # column) -- exactly as engram_rows does.
+    rng = np.random.default_rng(7 * T + cols)
+    R = 777
+    table_np = workloads.q2k_table(0, 0, R)
+    ids_np = rng.integers(0, R, (T, cols)).astype(np.int32)
+    bad_mask = rng.random((T, cols)) < 0.05
+    ids_np[bad_mask] = rng.choice([-1, R, R + 5, 2**31 - 1, -(2**31)], int(bad_mask.sum()))
+    wkv_np = oracle.bf16_bits(oracle.bf16_round(0.05 * rng.standard_normal((N, cols * 256))))
+    table, ids, wkv = tensor(table_np, "cuda"), tensor(ids_np, "cuda"), tensor(wkv_np, "cuda")
+    kv = torch.full((T, N), 0x7777, dtype=torch.int16, device="cuda")
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    eg.engram_project_q2k(table, R, ids, cols, cols, wkv, kv, T, N, bad)
+    rows = torch.empty((T, cols * 256), dtype=torch.int16, device="cuda")
+    bad2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    eg.engram_rows(eg.ENGRAM_ROWS_Q2K, table, None, R, ids, cols, cols, T, rows, bad2)
+    kv_two = torch.empty((T, N), dtype=torch.int16, device="cuda")
+    eg.engram_project(rows, wkv, kv_two, T, cols * 256, N)
+    assert bad.item() == int(bad_mask.sum()) == bad2.item()
+    assert torch.equal(kv, kv_two)
+    want_rows = oracle.rows_q2k(table_np, ids_np)
+    _check_kv(kv.cpu().numpy().view(np.uint16), want_rows, wkv_np)
+
+
+def test_project_q2k_strided_ids_of_second_layer(eg):
+    # ids laid out [T][n_layers][cols]; layer 1 is read with an offset pointer
+    # and stride n_layers * cols, as engram_forward does.
+    c = 3
+    wl = host(c)
+    s = wl.spec
+    ids, rows = gpu_rows(eg, c, 1, eg.ENGRAM_ROWS_Q2K)
+    L = dev(c).layers[1]
+    T = 700                                   # a prefix: ragged in M
+    kv = torch.empty((T, s.N), dtype=torch.int16, device="cuda")
+    eg.engram_project_q2k(L.table, L.table.numel() // 84, ids.view(-1)[s.cols:], 2 * s.cols,
+                          s.cols, L.wkv, kv, T, s.N)
+    kv_two = torch.empty((T, s.N), dtype=torch.int16, device="cuda")
+    eg.engram_project(rows, L.wkv, kv_two, T, s.K, s.N)
+    assert torch.equal(kv, kv_two)
 
 
 # ------------------------------------------------------------------------- gate
