@@ -34,6 +34,7 @@ METRIC = "Engram forward tokens/s at T=8192 (1 GPU); % HBM roofline gather+gate,
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published (no sparsity)
 Q2K_FUSED_MAX_BYTES = 2147483504   # engram.h: ENGRAM_Q2K_FUSED_MAX_BYTES
+SKINNY_MAX_TOKENS = 128            # engram_project streams wkv at or below this many tokens
 CPU_SAMPLE_TOKENS = 8192       # whole sequences of the workload, up to this many tokens
 
 
@@ -156,8 +157,10 @@ def main() -> int:
     rows = torch.empty((s.T, s.K), dtype=torch.int16, device="cuda")
     kv = torch.empty((s.T, s.N), dtype=torch.int16, device="cuda")
     num_rows = [l.table.numel() // (84 if fmt == eg.ENGRAM_ROWS_Q2K else 256) for l in dw.layers]
-    # The fused Q2_K rows+projection kernel, as engram_forward picks it.
-    fused = fmt == eg.ENGRAM_ROWS_Q2K and all(n * 84 <= Q2K_FUSED_MAX_BYTES for n in num_rows)
+    # The fused Q2_K rows+projection kernel, as engram_forward picks it (more
+    # than SKINNY_MAX_TOKENS tokens, table and columns within its limits).
+    fused = (fmt == eg.ENGRAM_ROWS_Q2K and s.T > SKINNY_MAX_TOKENS and s.cols <= 32 and
+             all(n * 84 <= Q2K_FUSED_MAX_BYTES for n in num_rows))
 
     def layer_ids(l):
         return ids.view(-1)[l * s.cols:]
@@ -263,6 +266,20 @@ def main() -> int:
         dom_name, dom_kernel = "project", "gemm_nt_kernel (engram_project)"
         dom_prof = "gemm_nt_prefill_T8192.md"
     dom_tf = tflops(per_launch_ms[dom_name])
+    skinny = s.T <= SKINNY_MAX_TOKENS
+    if skinny:
+        # Few tokens: the projection streams wkv once and is bound by HBM.
+        dom_kernel = "gemm_skinny_kernel (engram_project, T <= 128)"
+        dom_bytes = 2.0 * (s.N * s.K + s.T * s.K + s.T * s.N)
+        dom_gbs = gbs(dom_bytes, per_launch_ms[dom_name])
+        roofline = {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "bytes_per_launch": dom_bytes}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(dom_tf, 1), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(dom_tf / BF16_PEAK_TFLOPS, 4),
+                    "traffic": prof(dom_prof)}
+    roofline.update({"kernel": dom_kernel, "per_launch_ms": round(per_launch_ms[dom_name], 4)})
     stages = {
         "hash": {"ms": round(per_launch_ms["hash"], 4), "bound": "alu",
                  "hbm_gbs": round(gbs(alg["hash"], per_launch_ms["hash"]), 1),
@@ -281,7 +298,8 @@ def main() -> int:
                       "bytes_per_launch": alg["rows"],
                       "traffic": prof("rows_q2k_prefill_T8192.md"),
                       "in_step": not fused}
-    stages["project"] = {"ms": round(per_launch_ms["project"], 4), "bound": "mfma",
+    stages["project"] = {"ms": round(per_launch_ms["project"], 4),
+                         "bound": "hbm" if skinny else "mfma",
                          "achieved_tflops": round(proj_tf, 1),
                          "frac": round(proj_tf / BF16_PEAK_TFLOPS, 4),
                          "traffic": prof("gemm_nt_prefill_T8192.md"),
@@ -315,12 +333,7 @@ def main() -> int:
                                f"{s.num_rows} rows, dim={s.dim}, hc={s.hc}, "
                                f"{s.id_dist} ids",
                    "T": s.T, "K": s.K, "N": s.N, "row_format": s.fmt},
-        "roofline": {"bound": "mfma", "achieved": round(dom_tf, 1),
-                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(dom_tf / BF16_PEAK_TFLOPS, 4),
-                     "traffic": prof(dom_prof),
-                     "kernel": dom_kernel,
-                     "per_launch_ms": round(per_launch_ms[dom_name], 4)},
+        "roofline": roofline,
         "stages": stages,
     }
     if not args.no_cpu_baseline:

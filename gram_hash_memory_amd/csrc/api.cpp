@@ -286,7 +286,10 @@ engram_status engram_forward(const engram_hash_params *params, const engram_toke
     return st;
   for (int l = 0; l < L; ++l) {
     const engram_layer &ly = layers[l];
-    if (ly.fmt == ENGRAM_ROWS_Q2K && engram::project_q2k_supported(ly.num_rows, cols)) {
+    // Few tokens: rows -> the weight-streaming projection beats the fused
+    // 256 x 256 tiles (the dequant is then a few microseconds).
+    if (ly.fmt == ENGRAM_ROWS_Q2K && !engram::project_uses_skinny(T) &&
+        engram::project_q2k_supported(ly.num_rows, cols)) {
       if ((st = hip_status(engram::launch_project_q2k(ly.table, ly.num_rows, ids + l * cols,
                                                       int64_t(L) * cols, cols, ly.wkv, kv, T,
                                                       N, bad_ids, stream),

@@ -56,8 +56,12 @@ hipError_t launch_rows(engram_row_format fmt, const uint8_t *table, const uint8_
                        int32_t cols, int32_t T, uint16_t *rows, int32_t *bad_ids,
                        hipStream_t stream);
 
+// Picks the weight-streaming kernel of gemm_skinny.hip for few tokens.
 hipError_t launch_project(const uint16_t *a, const uint16_t *w, uint16_t *c, int32_t M,
                           int32_t K, int32_t N, hipStream_t stream);
+bool project_uses_skinny(int32_t M);
+hipError_t launch_project_skinny(const uint16_t *a, const uint16_t *w, uint16_t *c, int32_t M,
+                                 int32_t K, int32_t N, hipStream_t stream);
 
 // Rows + projection fused for Q2_K tables (kv bit-identical to rows -> project).
 bool project_q2k_supported(int64_t num_rows, int32_t cols);

@@ -206,6 +206,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
 
 hipError_t launch_project(const uint16_t *a, const uint16_t *w, uint16_t *c, int32_t M,
                           int32_t K, int32_t N, hipStream_t stream) {
+  if (project_uses_skinny(M)) return launch_project_skinny(a, w, c, M, K, N, stream);
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const size_t lds = size_t(2) * (BM + BN) * 64 * sizeof(uint16_t);
   const void *fn = reinterpret_cast<const void *>(&gemm_nt_kernel);

@@ -184,16 +184,20 @@ ENGRAM_API engram_status engram_rows(engram_row_format fmt, const uint8_t *table
  * Engram, the wkv linear without bias).
  *   rows DEVICE bf16 [T][K], wkv DEVICE bf16 [N][K], kv DEVICE bf16 [T][N],
  *   all row-major; K % 64 == 0.  Products accumulate in fp32 on the matrix
- *   cores and each output is rounded to bf16 once.
+ *   cores and each output is rounded to bf16 once.  T <= 128 (decode) runs a
+ *   kernel that streams wkv once from HBM with K split four ways per
+ *   workgroup; more tokens run 256 x 256 output tiles.  Either way the
+ *   result does not depend on timing.
  */
 ENGRAM_API engram_status engram_project(const uint16_t *rows, const uint16_t *wkv, uint16_t *kv,
                              int32_t T, int32_t K, int32_t N, hipStream_t stream);
 
 /* Stages 2 + 3 fused for Q2_K tables ([spark] overview stages 2-3): kv =
  * bf16(dequant(table[ids])) x wkv^T without writing the bf16 rows to memory.
- * The projection reads each row's 84-byte block and dequantises it on chip,
- * so kv is bit for bit what engram_rows followed by engram_project gives
- * (same values, same fp32 accumulation order).
+ * The projection reads each row's 84-byte block and dequantises it on chip.
+ * For T > 128 kv is bit for bit what engram_rows followed by engram_project
+ * gives (same values, same fp32 accumulation order); for fewer tokens
+ * engram_project streams wkv with another kernel and sums in another order.
  *   table DEVICE Q2_K [num_rows][84], 4-byte aligned; ids, ids_token_stride,
  *   cols, bad_ids as for engram_rows (K = cols * 256); wkv DEVICE bf16 [N][K];
  *   kv DEVICE bf16 [T][N], 16-byte aligned, fully overwritten.
@@ -236,7 +240,7 @@ ENGRAM_API size_t engram_workspace_bytes(int32_t T, int32_t n_layers, int32_t co
 /* The whole forward ([spark] overview, stages 1-4): hash every layer once,
  * then for each layer in order: rows -> projection -> gate on the same h.
  * Q2_K layers within the limits of engram_project_q2k run rows -> projection
- * as that fused kernel (same kv bits).
+ * as that fused kernel (same kv bits) when T > 128.
  *   layers: HOST array [params->n_layers] of DEVICE-pointer descriptors.
  *   workspace: DEVICE, at least engram_workspace_bytes(...) bytes, 256-byte
  *   aligned; its contents are scratch.  Every other argument is as for the

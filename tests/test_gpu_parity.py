@@ -183,8 +183,11 @@ def _check_kv(got_bits, rows_bits, wkv_bits):
     return float(np.mean(got == want))
 
 
+# Few tokens (<= 128) take the weight-streaming kernel, more the 256 x 256 tiles.
 @pytest.mark.parametrize("M,N,K", [(1, 64, 64), (300, 520, 512), (257, 256, 1536),
-                                   (512, 768, 192)])
+                                   (512, 768, 192), (3, 16, 128), (17, 80, 6144),
+                                   (64, 20480, 6144), (65, 1000, 1536), (100, 300, 320),
+                                   (128, 384, 256), (129, 384, 256)])
 def test_project_ragged_shapes_full_compare(eg, M, N, K):
     rng = np.random.default_rng(M + N + K)
     a = oracle.bf16_bits(oracle.bf16_round(rng.standard_normal((M, K))))
@@ -215,10 +218,15 @@ def test_project_workloads_sampled(eg, c):
 Q2K_CONFIGS = [c for c in CONFIGS if workloads.SPECS[c].fmt == "q2k"]
 
 
+SKINNY_MAX_TOKENS = 128     # engram_project streams wkv for at most this many tokens
+
+
 @pytest.mark.parametrize("c", Q2K_CONFIGS)
 def test_project_q2k_bit_identical_to_rows_then_project(eg, c):
     # Same bf16 operands, same MFMA order: the fused kernel's kv must equal the
-    # two-kernel path's bit for bit on the whole output, at the full size.
+    # two-kernel path's bit for bit on the whole output, at the full size --
+    # where engram_project uses the same 256 x 256 tiles (more than 128
+    # tokens); with fewer it sums in another order, and both meet the bound.
     wl = host(c)
     s = wl.spec
     for layer in range(len(s.layer_ids)):
@@ -231,8 +239,9 @@ def test_project_q2k_bit_identical_to_rows_then_project(eg, c):
         eg.engram_project_q2k(L.table, L.table.numel() // 84, ids.view(-1)[layer * s.cols:],
                               len(s.layer_ids) * s.cols, s.cols, L.wkv, kv, s.T, s.N, bad)
         assert bad.item() == 0
-        diff = int((kv != kv_two).sum().item())
-        assert diff == 0, f"layer {layer}: {diff} kv values differ"
+        if s.T > SKINNY_MAX_TOKENS:
+            diff = int((kv != kv_two).sum().item())
+            assert diff == 0, f"layer {layer}: {diff} kv values differ"
         pick = sample_tokens(wl)
         want_rows = oracle.rows_q2k(wl.layers[layer].table, oracle_ids(c)[pick, layer])
         _check_kv(kv.cpu().numpy().view(np.uint16)[pick], want_rows, wl.layers[layer].wkv)
@@ -261,7 +270,8 @@ def test_project_q2k_ragged_and_bad_ids(eg, T, cols, N):
     kv_two = torch.empty((T, N), dtype=torch.int16, device="cuda")
     eg.engram_project(rows, wkv, kv_two, T, cols * 256, N)
     assert bad.item() == int(bad_mask.sum()) == bad2.item()
-    assert torch.equal(kv, kv_two)
+    if T > SKINNY_MAX_TOKENS:
+        assert torch.equal(kv, kv_two)
     want_rows = oracle.rows_q2k(table_np, ids_np)
     _check_kv(kv.cpu().numpy().view(np.uint16), want_rows, wkv_np)
 
