@@ -42,8 +42,9 @@ def profiled_traffic(profile: str) -> int | None:
     """HBM bytes per launch from a committed rocprofv3 summary, or None.
 
     The summary records the FETCH_SIZE + WRITE_SIZE bytes (copy-calibrated)
-    and the sha256 of the kernel source it was taken on; a different source
-    today means the number is stale, so none is reported.
+    and the sha256 of the kernel's sources (concatenated, in the order
+    listed) it was taken on; different sources today mean the number is
+    stale, so none is reported.
     """
     import hashlib
     import re
@@ -51,12 +52,14 @@ def profiled_traffic(profile: str) -> int | None:
     try:
         text = open(path).read()
         traffic = int(re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M).group(1))
-        src = re.search(r"^source: (\S+)$", text, re.M).group(1)
+        srcs = re.search(r"^source: (.+)$", text, re.M).group(1).split()
         sha = re.search(r"^source_sha256: ([0-9a-f]+)$", text, re.M).group(1)
-        now = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
+        h = hashlib.sha256()
+        for src in srcs:
+            h.update(open(os.path.join(ROOT, src), "rb").read())
     except (OSError, AttributeError, ValueError):
         return None
-    return traffic if now == sha else None
+    return traffic if h.hexdigest() == sha else None
 
 
 def log(msg: str) -> None:
@@ -257,14 +260,16 @@ def main() -> int:
     ms_per_step = elapsed * 1e3 / args.steps
 
     def prof(name):
-        return profiled_traffic(name) if args.config == 2 else None
+        # Summaries exist for the prefill (T=8192) and decode (T=64) workloads.
+        suffix = {2: "_prefill_T8192.md", 1: "_decode_T64.md"}.get(args.config)
+        return profiled_traffic(name + suffix) if suffix else None
 
     if fused:
         dom_name, dom_kernel = "rows_project", "gemm_q2k_kernel (engram_project_q2k)"
-        dom_prof = "gemm_q2k_prefill_T8192.md"
+        dom_prof = "gemm_q2k"
     else:
         dom_name, dom_kernel = "project", "gemm_nt_kernel (engram_project)"
-        dom_prof = "gemm_nt_prefill_T8192.md"
+        dom_prof = "gemm_nt"
     dom_tf = tflops(per_launch_ms[dom_name])
     skinny = s.T <= SKINNY_MAX_TOKENS
     if skinny:
@@ -273,7 +278,8 @@ def main() -> int:
         dom_bytes = 2.0 * (s.N * s.K + s.T * s.K + s.T * s.N)
         dom_gbs = gbs(dom_bytes, per_launch_ms[dom_name])
         roofline = {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                    "traffic": prof("gemm_skinny"),
                     "bytes_per_launch": dom_bytes}
     else:
         roofline = {"bound": "mfma", "achieved": round(dom_tf, 1), "peak": BF16_PEAK_TFLOPS,
@@ -283,7 +289,7 @@ def main() -> int:
     stages = {
         "hash": {"ms": round(per_launch_ms["hash"], 4), "bound": "alu",
                  "hbm_gbs": round(gbs(alg["hash"], per_launch_ms["hash"]), 1),
-                 "traffic": prof("hash_prefill_T8192.md")},
+                 "traffic": prof("hash")},
     }
     if fused:
         stages["rows_project"] = {
@@ -296,20 +302,20 @@ def main() -> int:
                       "achieved_gbs": round(rows_gbs, 1),
                       "frac": round(rows_gbs / HBM_PEAK_GBS, 4),
                       "bytes_per_launch": alg["rows"],
-                      "traffic": prof("rows_q2k_prefill_T8192.md"),
+                      "traffic": prof("rows_q2k"),
                       "in_step": not fused}
     stages["project"] = {"ms": round(per_launch_ms["project"], 4),
                          "bound": "hbm" if skinny else "mfma",
                          "achieved_tflops": round(proj_tf, 1),
                          "frac": round(proj_tf / BF16_PEAK_TFLOPS, 4),
-                         "traffic": prof("gemm_nt_prefill_T8192.md"),
+                         "traffic": prof("gemm_skinny" if skinny else "gemm_nt"),
                          "in_step": not fused}
     gate_gbs = gbs(alg["gate"], per_launch_ms["gate"])
     stages["gate"] = {"ms": round(per_launch_ms["gate"], 4), "bound": "hbm",
                       "achieved_gbs": round(gate_gbs, 1),
                       "frac": round(gate_gbs / HBM_PEAK_GBS, 4),
                       "bytes_per_launch": alg["gate"],
-                      "traffic": prof("gate_prefill_T8192.md")}
+                      "traffic": prof("gate")}
     stages["gather_plus_gate"] = {"ms": round(gg_ms, 4), "achieved_gbs": round(gg_gbs, 1),
                                   "frac": round(gg_gbs / HBM_PEAK_GBS, 4),
                                   "kernels": "engram_rows + engram_gate"}
