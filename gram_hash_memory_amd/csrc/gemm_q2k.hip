@@ -8,9 +8,11 @@
 // through L2 by about a third; the bf16 values it multiplies are the same
 // ones engram_rows produces, so kv is bit-identical to rows -> project.
 //
-// Same tiling and pipeline as gemm.hip (256 x 256 tile, 4 waves of 128 x 128,
-// two LDS stages of BK = 64, B through two register stages).  For A, thread t
-// owns tile row t.  The 84-byte block of row t for table column c (K range
+// Same tiling as gemm.hip (256 x 256 tile, 4 waves of 128 x 128, two LDS
+// stages of BK = 64).  B goes straight from global memory into its LDS stage
+// (buffer_load ... lds, one stage ahead): that drops the VGPR staging, its LDS
+// stores and their waits, which in this kernel cost more than the LDS-DMA
+// path's lower raw rate.  For A, thread t owns tile row t.  The 84-byte block of row t for table column c (K range
 // 256c .. 256c + 255) sits in 21 VGPRs: it is loaded when column c - 1
 // starts, and its id one column earlier still.  Every stage, each thread
 // decodes its row's 64 values straight into the LDS A tile.  A stage spans
@@ -37,8 +39,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
   constexpr int BK = 64;
   constexpr int kStageElems = (BM + BN) * BK;
   constexpr int kChunks = BK / 8;
-  constexpr int kRowStep = kThreads / kChunks;
-  constexpr int kLoads = BN / kRowStep;            // B loads per thread per stage: 8
+  constexpr int kSegs = BN * BK * 2 / 1024 / kWaves;   // 1 KB B segments per wave per stage: 8
   extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
 
   int tm, tn;
@@ -51,24 +52,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
   const int cols = K / ENGRAM_HEAD_DIM;
   const int nk = K / BK;
 
-  // ---- B: as in gemm.hip.
+  // ---- B: global -> LDS by LDS-DMA.  One instruction fills a 1 KB segment
+  // (8 tile rows); lane L lands at byte 16 L, i.e. row L / 8 of the segment,
+  // physical chunk L % 8, and fetches the logical chunk the swizzle keeps
+  // there.  For segment s the swizzle key of that row is (L / 8) ^ (s & 1).
+  // Rows past N read as zeros (the resource starts at the tile's first row).
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + int64_t(n0) * K, int64_t(N - n0) * K * 2);
-  const int lrow = tid / kChunks, lchunk = tid % kChunks;
-  const uint32_t voff = uint32_t(lrow * K + lchunk * 8) * 2;
-  const uint32_t row_step = uint32_t(kRowStep * K) * 2;
-  u32x4 gb[2][kLoads];
-  auto load_b = [&](int set, int slice) {
+  const int seg_row = lane >> 3;
+  const uint32_t voff_even = uint32_t(seg_row * K + ((lane & 7) ^ seg_row) * 8) * 2;
+  const uint32_t voff_odd = uint32_t(seg_row * K + ((lane & 7) ^ seg_row ^ 1) * 8) * 2;
+  const uint32_t seg_stride = uint32_t(8 * K) * 2;
+  auto dma_b = [&](int stage, int slice) {
     const int k0 = min(slice, nk - 1) * BK;
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i)
-      gb[set][i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, voff, int(i * row_step) + k0 * 2, 0));
-  };
-  auto store_b = [&](int set, int stage) {
     uint16_t *sb = smem + stage * kStageElems + BM * BK;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i)
-      *reinterpret_cast<u32x4 *>(sb + swz<BK>(lrow + i * kRowStep, lchunk)) = gb[set][i];
+    for (int i = 0; i < kSegs; ++i) {
+      const int seg = wave * kSegs + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, sb + seg * 512, 16,
+                                               (i & 1) ? voff_odd : voff_even,
+                                               int(seg * seg_stride) + k0 * 2, 0, 0);
+    }
   };
 
   // ---- A: the Q2_K block of tile row `tid`, one table column at a time.
@@ -202,23 +205,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
     }
   };
 
-  // Iteration kt multiplies stage kt and prepares stage kt + 1 (as in gemm.hip);
-  // j = kt % 8 fixes the register sets at compile time:
-  //  - B slice kt + 2 -> set kt % 2; B slice kt + 1 (set (kt + 1) % 2) -> LDS;
+  // Iteration kt multiplies stage kt % 2 and fills stage (kt + 1) % 2, which
+  // every wave finished reading before the previous barrier; j = kt % 8 fixes
+  // the register sets at compile time:
+  //  - B slice kt + 1 is requested into its LDS stage first thing;
   //  - A stage kt + 1 is column (kt + 1) / 4, quarter (kt + 1) % 4, decoded
   //    from block set ((kt + 1) / 4) % 2;
   //  - when kt % 4 == 0 (column m = kt / 4 starts), the block of column m + 1
-  //    is requested.
+  //    is requested, after the B segments (6 loads);
+  //  - before the barrier, vmcnt lets only those 6 block loads stay in
+  //    flight: the B segments (older) have then landed in LDS.
   // Scheduling fences around the loads keep them at the top of the iteration
   // (the compiler would otherwise sink them towards their first use, which
   // shortens the prefetch distance), and keep work of a later iteration (such
   // as the fp16 d of a block still in flight) from being hoisted into this
   // one, where it would wait for the load.
   auto iteration = [&](int kt, const int j) {
-    const int bset = j & 1;
-    const int stage = bset;                          // kt % 2
+    const int stage = j & 1;                         // kt % 2
     __builtin_amdgcn_sched_barrier(0);
-    load_b(bset, kt + 2);
+    dma_b(stage ^ 1, kt + 1);
     if (j % 4 == 0) load_block(((j / 4) + 1) & 1, kt / 4 + 1);
     __builtin_amdgcn_sched_barrier(0);
     load_frags(stage, 1, 1);
@@ -229,24 +234,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
     mfma_block(1);
     decode_a(((j + 1) / 4) & 1, (j + 1) % 4, stage ^ 1, 2, 4);
     sched_reads_decode();
-    store_b(bset ^ 1, stage ^ 1);
     load_frags(stage, 3, 1);
     mfma_block(0);
     sched_reads();
-    stage_barrier<waitcnt(63, 0)>();
+    if (j % 4 == 0) stage_barrier<waitcnt(6, 0)>();
+    else stage_barrier<waitcnt(0, 0)>();
     load_frags(stage ^ 1, 0, 0);
     mfma_block(1);
     sched_reads();
   };
 
-  // Prologue: block of column 0, B slices 0 and 1; stage 0 gets B slice 0 and
-  // A quarter 0 of column 0.  (Iteration 0 then requests the block of column 1.)
+  // Prologue: stage 0 gets B slice 0 and A quarter 0 of column 0.  (Iteration
+  // 0 then requests B slice 1 and the block of column 1.)
   load_block(0, 0);
-  load_b(0, 0);
-  load_b(1, 1);
-  store_b(0, 0);
+  dma_b(0, 0);
   decode_a(0, 0, 0, 0, 4);
-  stage_barrier<waitcnt(63, 0)>();
+  stage_barrier<waitcnt(0, 0)>();
   load_frags(0, 0, 0);
 
   int kt = 0;
