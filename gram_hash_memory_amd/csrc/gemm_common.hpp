@@ -82,6 +82,41 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
 }
 
+// Epilogue of a 256 x 256 tile computed by 4 waves of 128 x 128 with
+// v_mfma_f32_32x32x16_bf16 (accumulator r of a 32 x 32 block is row
+// 8 * (r / 4) + 4 * (lane / 32) + r % 4, column lane % 32): the bf16 results go
+// through LDS (row-major, 512 B per row) so that global memory sees 16-byte
+// stores of whole row segments instead of 2-byte stores scattered over rows.
+// `smem` needs 128 KB that no wave reads any more; the caller's barrier
+// before this call guarantees that.
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], uint16_t *smem,
+                                           uint16_t *__restrict__ C, int M, int N, int m0,
+                                           int n0, int wm, int wn, int lane, int tid) {
+  const int frow = lane & 31, fhalf = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
+        smem[row * BN + wn * 128 + j * 32 + frow] = f32_to_bf16(acc[i][j][r]);
+      }
+  __syncthreads();
+  const bool vec = (N % 8) == 0;
+  for (int idx = tid; idx < BM * BN / 8; idx += kThreads) {
+    const int row = idx / (BN / 8), c8 = (idx % (BN / 8)) * 8;
+    const int grow = m0 + row, gcol = n0 + c8;
+    if (grow >= M || gcol >= N) continue;
+    uint16_t *dst = C + int64_t(grow) * N + gcol;
+    const uint16_t *src = smem + row * BN + c8;
+    if (vec) {
+      *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(src);
+    } else {
+      for (int e = 0; e < 8 && gcol + e < N; ++e) dst[e] = src[e];
+    }
+  }
+}
 
 }  // namespace gemm
 }  // namespace engram

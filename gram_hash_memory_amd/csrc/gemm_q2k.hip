@@ -270,19 +270,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
     iteration(kt + 3, 3);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
-
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 128 + j * 32 + frow;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
-        if (row < M && col < N) C[int64_t(row) * N + col] = f32_to_bf16(acc[i][j][r]);
-      }
-    }
-  }
+  __syncthreads();                                 // every wave is done with the stages
+  store_tile(acc, smem, C, M, N, m0, n0, wm, wn, lane, tid);
 }
 
 }  // namespace
