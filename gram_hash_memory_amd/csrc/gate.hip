@@ -8,8 +8,9 @@
 // streams.  [vLLM engram page, Engram]: one key per stream plus a shared
 // value; clamp 1e-6 before the square root.
 //
-// One workgroup per token.  Every thread loads its 8-wide slices of all hc
-// streams into registers, together with the matching key and value slices.
+// One workgroup per token (or, for a few tokens, per token and stream: see
+// launch_gate).  Every thread loads its 8-wide slices of all hc streams into
+// registers, together with the matching key and value slices.
 // It accumulates the 3*hc partial sums, and the sums are reduced with wave
 // shuffles plus one LDS exchange.  Each thread then derives the hc gates and
 // writes x + g * v from the registers, so h is read once and written once
@@ -38,17 +39,27 @@ __device__ __forceinline__ void bf16x8_to_f32(const u32x4 w, float *f) {
   }
 }
 
-template <int HC, int NCH>
+// HC streams per workgroup; with SPLIT the workgroup handles stream
+// blockIdx.x % hc of token blockIdx.x / hc only (HC = 1 then, hc the real
+// stream count): the value is then read once per stream, but a decode batch
+// of a few dozen tokens spreads over hc times more workgroups.
+template <int HC, int NCH, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void gate_kernel(
     float *__restrict__ h, const uint16_t *__restrict__ kv, const uint16_t *__restrict__ qw,
     const uint16_t *__restrict__ kw, const uint8_t *__restrict__ mask, int32_t dim,
-    float eps, float clamp, float dot_scale) {
-  const int64_t t = blockIdx.x;
+    int32_t hc, float eps, float clamp, float dot_scale) {
+  const int64_t t = SPLIT ? blockIdx.x / hc : blockIdx.x;
+  const int s0 = SPLIT ? int(blockIdx.x % hc) : 0;   // first stream of this workgroup
+  const int nstreams = SPLIT ? hc : HC;
   if (mask && mask[t] == 0) return;
   __shared__ float red[kWaves][3 * HC];
 
-  float *ht = h + t * HC * int64_t(dim);
-  const uint16_t *kvt = kv + t * (HC + 1) * int64_t(dim);
+  float *ht = h + (t * nstreams + s0) * int64_t(dim);
+  const uint16_t *kvt = kv + t * (nstreams + 1) * int64_t(dim);
+  const uint16_t *vt = kvt + nstreams * int64_t(dim);       // the shared value
+  kvt += s0 * int64_t(dim);
+  qw += s0 * int64_t(dim);
+  kw += s0 * int64_t(dim);
 
   float x[HC][NCH][kVec];
   float ssx[HC], ssk[HC], dot[HC];
@@ -119,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(
     const int i0 = (threadIdx.x + c * kThreads) * kVec;
     if (i0 < dim) {
       float v[kVec];
-      bf16x8_to_f32(*reinterpret_cast<const u32x4 *>(kvt + HC * dim + i0), v);
+      bf16x8_to_f32(*reinterpret_cast<const u32x4 *>(vt + i0), v);
 #pragma unroll
       for (int s = 0; s < HC; ++s) {
         f32x4 a, b;
@@ -135,43 +146,47 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(
   }
 }
 
-template <int HC>
+template <int HC, bool SPLIT>
 hipError_t launch_hc(float *h, const uint16_t *kv, const uint16_t *qw, const uint16_t *kw,
-                     const uint8_t *mask, int32_t T, int32_t dim, float eps, float clamp,
-                     float dot_scale, hipStream_t stream) {
+                     const uint8_t *mask, int32_t T, int32_t hc, int32_t dim, float eps,
+                     float clamp, float dot_scale, hipStream_t stream) {
   const int nch = (dim + kThreads * kVec - 1) / (kThreads * kVec);
-  const dim3 grid(T), block(kThreads);
+  const dim3 grid(SPLIT ? unsigned(T) * unsigned(hc) : unsigned(T)), block(kThreads);
   switch (nch) {
     case 1:
-      hipLaunchKernelGGL((gate_kernel<HC, 1>), grid, block, 0, stream, h, kv, qw, kw, mask,
-                         dim, eps, clamp, dot_scale);
+      hipLaunchKernelGGL((gate_kernel<HC, 1, SPLIT>), grid, block, 0, stream, h, kv, qw, kw,
+                         mask, dim, hc, eps, clamp, dot_scale);
       break;
     case 2:
-      hipLaunchKernelGGL((gate_kernel<HC, 2>), grid, block, 0, stream, h, kv, qw, kw, mask,
-                         dim, eps, clamp, dot_scale);
+      hipLaunchKernelGGL((gate_kernel<HC, 2, SPLIT>), grid, block, 0, stream, h, kv, qw, kw,
+                         mask, dim, hc, eps, clamp, dot_scale);
       break;
     default:
-      hipLaunchKernelGGL((gate_kernel<HC, 4>), grid, block, 0, stream, h, kv, qw, kw, mask,
-                         dim, eps, clamp, dot_scale);
+      hipLaunchKernelGGL((gate_kernel<HC, 4, SPLIT>), grid, block, 0, stream, h, kv, qw, kw,
+                         mask, dim, hc, eps, clamp, dot_scale);
       break;
   }
   return hipGetLastError();
 }
+
+// Below this many workgroups a token-per-workgroup grid leaves most CUs idle.
+constexpr int kSplitBelow = 1024;
 
 }  // namespace
 
 hipError_t launch_gate(float *h, const uint16_t *kv, const uint16_t *qw, const uint16_t *kw,
                        const uint8_t *mask, int32_t T, int32_t hc, int32_t dim, float eps,
                        float clamp, float dot_scale, hipStream_t stream) {
+  if (T < kSplitBelow && hc > 1)
+    return launch_hc<1, true>(h, kv, qw, kw, mask, T, hc, dim, eps, clamp, dot_scale, stream);
   switch (hc) {
-    case 1: return launch_hc<1>(h, kv, qw, kw, mask, T, dim, eps, clamp, dot_scale, stream);
-    case 2: return launch_hc<2>(h, kv, qw, kw, mask, T, dim, eps, clamp, dot_scale, stream);
-    case 3: return launch_hc<3>(h, kv, qw, kw, mask, T, dim, eps, clamp, dot_scale, stream);
-    case 4: return launch_hc<4>(h, kv, qw, kw, mask, T, dim, eps, clamp, dot_scale, stream);
-    case 5: return launch_hc<5>(h, kv, qw, kw, mask, T, dim, eps, clamp, dot_scale, stream);
-    case 6: return launch_hc<6>(h, kv, qw, kw, mask, T, dim, eps, clamp, dot_scale, stream);
-    case 7: return launch_hc<7>(h, kv, qw, kw, mask, T, dim, eps, clamp, dot_scale, stream);
-    default: return launch_hc<8>(h, kv, qw, kw, mask, T, dim, eps, clamp, dot_scale, stream);
+#define ENGRAM_GATE_HC(n) \
+    case n: return launch_hc<n, false>(h, kv, qw, kw, mask, T, hc, dim, eps, clamp, dot_scale, stream);
+    ENGRAM_GATE_HC(1) ENGRAM_GATE_HC(2) ENGRAM_GATE_HC(3) ENGRAM_GATE_HC(4)
+    ENGRAM_GATE_HC(5) ENGRAM_GATE_HC(6) ENGRAM_GATE_HC(7)
+#undef ENGRAM_GATE_HC
+    default: return launch_hc<8, false>(h, kv, qw, kw, mask, T, hc, dim, eps, clamp, dot_scale,
+                                        stream);
   }
 }
 

@@ -5,17 +5,35 @@
 // 2..max_ngram over n_heads heads; each (order, head) column owns a prime-sized
 // bucket range; missing or blocked history reads as the pad id.
 //
-// One thread per position.  Its history (max_ngram - 1 ids back, with the
-// blocking rule) is resolved once and then shared by every layer.  The tables
-// travel as kernel arguments: all lanes index them uniformly, so they are read
-// with scalar loads.  The whole stage is a few hundred integer operations per
-// position; it is bound by launch latency, not by bandwidth.
+// One thread per (position, column), so that even a decode batch of a few
+// dozen tokens spreads over enough lanes; the column's order n fixes how many
+// history positions (n - 1) the thread resolves.  The tables travel as kernel
+// arguments: all lanes index them uniformly per layer, so they are read with
+// scalar loads.  Sequence boundaries are searched in an LDS copy of
+// cu_seqlens when it fits, which turns a chain of dependent global loads into
+// one cooperative load.
 #include "common.hpp"
 
 namespace engram {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kCuLds = 4096;           // cu_seqlens entries searched in LDS
+
+// x mod p for 64-bit x and a 31-bit prime p.  The quotient estimate from fp64
+// is within a few units of floor(x / p) once p >= 2^12 (relative error of the
+// three roundings <= 3.3 * 2^-53, and x / p < 2^52), so a couple of
+// corrections make the remainder exact; smaller moduli take the integer
+// division.  The difference x - q*p is formed mod 2^64, and its true value
+// lies within a few p of 0, so reading it as int64 is exact.
+__device__ __forceinline__ uint32_t mod_prime(uint64_t x, uint32_t p) {
+  if (p < 4096u) return uint32_t(x % p);
+  const uint64_t q = uint64_t(double(x) * (1.0 / double(p)));
+  int64_t r = int64_t(x - q * uint64_t(p));
+  while (r < 0) r += int64_t(p);
+  while (r >= int64_t(p)) r -= int64_t(p);
+  return uint32_t(r);
+}
 
 __global__ __launch_bounds__(kThreads) void hash_kernel(
     const HashTables tab, int32_t T, int32_t n_seqs, int32_t depth,
@@ -23,17 +41,27 @@ __global__ __launch_bounds__(kThreads) void hash_kernel(
     const int32_t *__restrict__ doc_ids, const uint8_t *__restrict__ mask,
     const int32_t *__restrict__ lookback, const uint8_t *__restrict__ lookback_live,
     int32_t *__restrict__ ids) {
-  const int32_t t = blockIdx.x * kThreads + threadIdx.x;
-  if (t >= T) return;
+  __shared__ int32_t cu_lds[kCuLds];
+  const bool cu_in_lds = n_seqs + 1 <= kCuLds;
+  if (cu_in_lds) {
+    for (int i = threadIdx.x; i <= n_seqs; i += kThreads) cu_lds[i] = cu[i];
+    __syncthreads();
+  }
+
+  const int32_t cols = (tab.max_ngram - 1) * tab.n_heads;
+  const int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (g >= int64_t(T) * cols) return;
+  const int32_t t = int32_t(g / cols), c = int32_t(g % cols);
+  const int order = 2 + c / tab.n_heads;
 
   // Chunk of t: the last s with cu[s] <= t (empty chunks are skipped over).
   int32_t lo = 0, hi = n_seqs - 1;
   while (lo < hi) {
     const int32_t mid = (lo + hi + 1) >> 1;
-    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+    if ((cu_in_lds ? cu_lds[mid] : cu[mid]) <= t) lo = mid; else hi = mid - 1;
   }
   const int32_t s = lo;
-  const int32_t start = max(cu[s], 0);
+  const int32_t start = max(cu_in_lds ? cu_lds[s] : cu[s], 0);
 
   // History: distance 0 is t itself; walking back, the first position that
   // is absent or not live, and everything before it, reads as pad_id.
@@ -44,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void hash_kernel(
   const uint64_t pad = uint64_t(int64_t(tab.pad_id));
 #pragma unroll
   for (int k = 1; k < ENGRAM_MAX_NGRAM; ++k) {
-    if (k >= tab.max_ngram) break;
+    if (k >= order) break;
     int32_t tokv = tab.pad_id;
     if (!blocked) {
       const int32_t q = t - k;
@@ -67,18 +95,13 @@ __global__ __launch_bounds__(kThreads) void hash_kernel(
     hist[k] = blocked ? pad : uint64_t(int64_t(tokv));
   }
 
-  const int32_t cols = (tab.max_ngram - 1) * tab.n_heads;
-  int32_t *out = ids + int64_t(t) * tab.n_layers * cols;
+  int32_t *out = ids + int64_t(t) * tab.n_layers * cols + c;
   for (int l = 0; l < tab.n_layers; ++l) {
     uint64_t mix = hist[0] * tab.mult[l][0];
-    for (int n = 2; n <= tab.max_ngram; ++n) {
-      mix ^= hist[n - 1] * tab.mult[l][n - 1];      // wraps mod 2^64
-      const int c0 = (n - 2) * tab.n_heads;
-      for (int j = 0; j < tab.n_heads; ++j) {
-        const int c = c0 + j;
-        out[l * cols + c] = int32_t(tab.offset[l][c] + uint32_t(mix % tab.prime[l][c]));
-      }
-    }
+#pragma unroll
+    for (int k = 1; k < ENGRAM_MAX_NGRAM; ++k)
+      if (k < order) mix ^= hist[k] * tab.mult[l][k];   // products wrap mod 2^64
+    out[l * cols] = int32_t(tab.offset[l][c] + mod_prime(mix, tab.prime[l][c]));
   }
 }
 
@@ -86,9 +109,10 @@ __global__ __launch_bounds__(kThreads) void hash_kernel(
 
 hipError_t launch_hash(const HashTables &tab, const engram_tokens &tok, int32_t *ids,
                        hipStream_t stream) {
-  const int blocks = (tok.T + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL(hash_kernel, dim3(blocks), dim3(kThreads), 0, stream, tab, tok.T,
-                     tok.n_seqs, tok.lookback ? tok.lookback_depth : 0, tok.cids,
+  const int64_t cols = int64_t(tab.max_ngram - 1) * tab.n_heads;
+  const int64_t blocks = (int64_t(tok.T) * cols + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(hash_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, tab,
+                     tok.T, tok.n_seqs, tok.lookback ? tok.lookback_depth : 0, tok.cids,
                      tok.cu_seqlens, tok.doc_ids, tok.token_mask, tok.lookback,
                      tok.lookback_live, ids);
   return hipGetLastError();
