@@ -29,10 +29,13 @@ from .numerics import (bf16_round, bf16_bits, bf16_value, fp16_value,
                        e4m3fn_value, e8m0_scale)
 from .engram import (hash_ids, rows_q2k, rows_fp8, project, gate, forward,
                      Q2K_ROW_BYTES, FP8_ROW_BYTES, HEAD_DIM)
+from .mx import (e8m0_mx_scale, quantize_mxfp8, mx_values, rows_fp8_mx, project_mxfp8,
+                 MX_BLOCK)
 
 __all__ = [
     "is_prime", "next_unused_prime", "engram_layout", "hash_multipliers",
     "bf16_round", "bf16_bits", "bf16_value", "fp16_value", "e4m3fn_value",
     "e8m0_scale", "hash_ids", "rows_q2k", "rows_fp8", "project", "gate",
-    "forward", "Q2K_ROW_BYTES", "FP8_ROW_BYTES", "HEAD_DIM",
+    "forward", "Q2K_ROW_BYTES", "FP8_ROW_BYTES", "HEAD_DIM", "e8m0_mx_scale",
+    "quantize_mxfp8", "mx_values", "rows_fp8_mx", "project_mxfp8", "MX_BLOCK",
 ]

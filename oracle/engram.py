@@ -28,6 +28,7 @@ import numpy as np
 
 from .numerics import (bf16_round, bf16_bits, bf16_value, fp16_value,
                        e4m3fn_value, e8m0_scale)
+from .mx import rows_fp8_mx, project_mxfp8
 
 HEAD_DIM = 256          # values per table row
 Q2K_ROW_BYTES = 84      # [spark] ENGRAM_ROW_BYTES: one Q2_K super-block
@@ -252,7 +253,9 @@ def forward(h, cids, cu_seqlens, hash_params, layers, eps, clamp, dot_scale,
     hash_params: dict(multipliers, primes, offsets, max_ngram, n_heads, pad_id).
     layers: list of dicts with 'fmt' ('q2k' or 'fp8'), 'table', 'scales'
     (fp8 only), 'wkv', 'q_weight', 'k_weight' (bf16 bits); they run in order
-    on the same h (reading A18).  The gate mask is token_mask.
+    on the same h (reading A18).  The gate mask is token_mask.  An fp8 layer
+    that also carries 'wkv_mx' = (codes, scales) from mx.quantize_mxfp8 is
+    projected in MXFP8 (mx.project_mxfp8 of the raw rows) instead.
     """
     ids = hash_ids(cids, cu_seqlens, hash_params["multipliers"], hash_params["primes"],
                    hash_params["offsets"], hash_params["max_ngram"],
@@ -264,11 +267,17 @@ def forward(h, cids, cu_seqlens, hash_params, layers, eps, clamp, dot_scale,
     for l, layer in enumerate(layers):
         if layer["fmt"] == "q2k":
             rows = rows_q2k(layer["table"], ids[:, l, :])
+        elif layer["fmt"] == "fp8" and layer.get("wkv_mx") is not None:
+            # MXFP8 projection (oracle.mx): raw rows against the MXFP8 wkv copy
+            a_codes, a_scales = rows_fp8_mx(layer["table"], layer["scales"], ids[:, l, :])
+            rows = None
+            kv = project_mxfp8(a_codes, a_scales, *layer["wkv_mx"])
         elif layer["fmt"] == "fp8":
             rows = rows_fp8(layer["table"], layer["scales"], ids[:, l, :])
         else:
             raise ValueError(layer["fmt"])
-        kv = project(rows, layer["wkv"])
+        if rows is not None:
+            kv = project(rows, layer["wkv"])
         h = gate(h, kv, layer["q_weight"], layer["k_weight"], token_mask, eps, clamp,
                  dot_scale)
         inter.append({"rows": rows, "kv": kv})

@@ -391,6 +391,47 @@ def test_forward_against_oracle(eg, c):
         assert np.array_equal(got[off].view(np.uint32), wl.h[off].view(np.uint32))
 
 
+@pytest.mark.parametrize("T,max_ngram,n_heads", [(300, 5, 9), (100, 4, 8)])
+def test_forward_kernel_choices_against_oracle(eg, T, max_ngram, n_heads):
+    # engram_forward picks, per layer, between the fused Q2_K projection (more
+    # than 128 tokens and at most 32 columns), the weight-streaming projection
+    # (at most 128 tokens) and rows -> 256 x 256 tiles (here: 36 columns).
+    # Each choice must give the oracle's forward.
+    from oracle.layout import engram_layout, hash_multipliers
+    cols = (max_ngram - 1) * n_heads
+    V, hc, dim = 5000, 2, 128
+    primes, offsets = engram_layout(1, max_ngram, n_heads, 6007)
+    R = int((offsets + primes).max())
+    hp = dict(multipliers=hash_multipliers([1], max_ngram, V), primes=primes, offsets=offsets,
+              max_ngram=max_ngram, n_heads=n_heads, pad_id=0)
+    rng = np.random.default_rng(T + cols)
+    cids = rng.integers(0, V, T).astype(np.int32)
+    cu = np.array([0, T // 3, T], dtype=np.int32)
+    table = workloads.q2k_table(0, 0, R)
+    K, N = cols * 256, (hc + 1) * dim
+    wkv = oracle.bf16_bits(oracle.bf16_round(0.02 * rng.standard_normal((N, K))))
+    qw = oracle.bf16_bits(oracle.bf16_round(1 + 0.1 * rng.standard_normal((hc, dim))))
+    kw = oracle.bf16_bits(oracle.bf16_round(1 + 0.1 * rng.standard_normal((hc, dim))))
+    h0 = rng.standard_normal((T, hc, dim)).astype(np.float32)
+    eps, clamp, dot_scale = 1e-6, 1e-6, 1 / np.sqrt(dim)
+    params = eg.HashParams.from_dict(hp)
+    tokens = eg.Tokens(tensor(cids, "cuda"), tensor(cu, "cuda"))
+    layer = eg.Layer(eg.ENGRAM_ROWS_Q2K, tensor(table, "cuda"), None, tensor(wkv, "cuda"),
+                     tensor(qw, "cuda"), tensor(kw, "cuda"), hc, dim, cols)
+    h = tensor(h0, "cuda")
+    ws = torch.empty(eg.engram_workspace_bytes(T, 1, cols, hc, dim), dtype=torch.uint8,
+                     device="cuda")
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    eg.engram_forward(params, tokens, [layer], h, hc, dim, eps, clamp, dot_scale, ws, bad)
+    got = h.cpu().numpy()
+    want = oracle.forward(h0, cids, cu, hp, [dict(fmt="q2k", table=table, scales=None, wkv=wkv,
+                                                  q_weight=qw, k_weight=kw)],
+                          eps, clamp, dot_scale)
+    err = np.abs(got - want) / np.maximum(1.0, np.abs(want))
+    assert bad.item() == 0
+    assert err.max() <= 1e-2, err.max()
+
+
 def test_forward_empty_batch(eg):
     wl = host(0)
     s = wl.spec
