@@ -2,8 +2,8 @@
 
 The package is a thin ctypes binding over libengram.so: a C-ABI library of
 hand-written HIP kernels (hash, row gather + dequant, bf16 MFMA projection,
-the projection fused with the Q2_K row dequant, and the gate) plus their
-composition.  Build the library with
+the projection fused with the Q2_K row dequant, the MXFP8 projection of raw
+FP8 rows, and the gate) plus their composition.  Build the library with
 `python gram_hash_memory_amd/build.py`.  Importing the package without it
 raises ImportError; there is no CPU fallback.
 """
@@ -12,6 +12,6 @@ from ._binding import (  # noqa: F401
     ENGRAM_OK, ENGRAM_ERR_ARG, ENGRAM_ERR_UNSUPPORTED, ENGRAM_ERR_HIP,
     ENGRAM_ROWS_Q2K, ENGRAM_ROWS_FP8_E4M3_E8M0, HEAD_DIM, Q2K_ROW_BYTES, FP8_ROW_BYTES,
     FP8_SCALE_BYTES, EXPORTS, LIB_PATH, EngramError, HashParams, Tokens, Layer,
-    engram_hash, engram_rows, engram_project, engram_project_q2k, engram_gate, engram_workspace_bytes,
-    engram_forward, engram_last_error,
+    engram_hash, engram_rows, engram_project, engram_project_q2k, engram_quantize_mxfp8,
+    engram_project_mxfp8, engram_gate, engram_workspace_bytes, engram_forward, engram_last_error,
 )

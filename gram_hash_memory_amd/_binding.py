@@ -28,7 +28,8 @@ ENGRAM_OK, ENGRAM_ERR_ARG, ENGRAM_ERR_UNSUPPORTED, ENGRAM_ERR_HIP = 0, 1, 2, 3
 ENGRAM_ROWS_Q2K, ENGRAM_ROWS_FP8_E4M3_E8M0 = 0, 1
 HEAD_DIM, Q2K_ROW_BYTES, FP8_ROW_BYTES, FP8_SCALE_BYTES = 256, 84, 256, 8
 
-EXPORTS = ("engram_hash", "engram_rows", "engram_project", "engram_project_q2k", "engram_gate",
+EXPORTS = ("engram_hash", "engram_rows", "engram_project", "engram_project_q2k",
+           "engram_quantize_mxfp8", "engram_project_mxfp8", "engram_gate",
            "engram_workspace_bytes", "engram_forward", "engram_last_error")
 
 if not os.path.exists(LIB_PATH):
@@ -51,7 +52,7 @@ class _Tokens(ctypes.Structure):
 class _Layer(ctypes.Structure):
     _fields_ = [("fmt", c_int), ("num_rows", c_int64), ("table", c_void_p),
                 ("scales", c_void_p), ("wkv", c_void_p), ("q_weight", c_void_p),
-                ("k_weight", c_void_p)]
+                ("k_weight", c_void_p), ("wkv_mx", c_void_p), ("wkv_mx_scales", c_void_p)]
 
 
 _P = ctypes.POINTER
@@ -62,6 +63,10 @@ _lib.engram_project.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, 
                                 c_void_p]
 _lib.engram_project_q2k.argtypes = [c_void_p, c_int64, c_void_p, c_int64, c_int32, c_void_p,
                                     c_void_p, c_int32, c_int32, c_void_p, c_void_p]
+_lib.engram_quantize_mxfp8.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
+_lib.engram_project_mxfp8.argtypes = [c_void_p, c_void_p, c_int64, c_void_p, c_int64, c_int32,
+                                      c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
+                                      c_void_p]
 _lib.engram_gate.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                              c_int32, c_int32, c_float, c_float, c_float, c_void_p]
 _lib.engram_workspace_bytes.argtypes = [c_int32, c_int32, c_int32, c_int32, c_int32]
@@ -70,8 +75,8 @@ _lib.engram_forward.argtypes = [_P(_HashParams), _P(_Tokens), _P(_Layer), c_void
                                 c_int32, c_float, c_float, c_float, c_void_p, c_size_t,
                                 c_void_p, c_void_p]
 _lib.engram_last_error.restype = c_char_p
-for _name in ("engram_hash", "engram_rows", "engram_project", "engram_project_q2k", "engram_gate",
-              "engram_forward"):
+for _name in ("engram_hash", "engram_rows", "engram_project", "engram_project_q2k",
+              "engram_quantize_mxfp8", "engram_project_mxfp8", "engram_gate", "engram_forward"):
     getattr(_lib, _name).restype = c_int
 
 
@@ -197,6 +202,30 @@ def engram_project_q2k(table, num_rows: int, ids, ids_token_stride: int, cols: i
         int(N), _dptr(bad_ids, torch.int32, 1, "bad_ids"), _stream(stream)))
 
 
+def engram_quantize_mxfp8(w, N: int, K: int, codes, scales, stream=None) -> None:
+    """MXFP8 copy of bf16 w [N, K]: codes uint8 [N, K] (e4m3fn), scales uint8 [N, K/32] (e8m0)."""
+    _check(_lib.engram_quantize_mxfp8(_dptr(w, torch.int16, N * K, "w"), int(N), int(K),
+                                      _dptr(codes, torch.uint8, N * K, "codes"),
+                                      _dptr(scales, torch.uint8, N * (K // 32), "scales"),
+                                      _stream(stream)))
+
+
+def engram_project_mxfp8(table, scales, num_rows: int, ids, ids_token_stride: int, cols: int,
+                         wkv_codes, wkv_scales, kv, T: int, N: int, bad_ids=None,
+                         stream=None) -> None:
+    """Stages 2 + 3 for an FP8 table in MXFP8: kv [T, N] from ids and the MXFP8 wkv."""
+    K = cols * HEAD_DIM
+    need_ids = 0 if T <= 0 else (T - 1) * ids_token_stride + cols
+    _check(_lib.engram_project_mxfp8(
+        _dptr(table, torch.uint8, num_rows * FP8_ROW_BYTES, "table"),
+        _dptr(scales, torch.uint8, num_rows * FP8_SCALE_BYTES, "scales"), int(num_rows),
+        _dptr(ids, torch.int32, need_ids, "ids"), int(ids_token_stride), int(cols),
+        _dptr(wkv_codes, torch.uint8, N * K, "wkv_codes"),
+        _dptr(wkv_scales, torch.uint8, N * (K // 32), "wkv_scales"),
+        _dptr(kv, torch.int16, T * N, "kv"), int(T), int(N),
+        _dptr(bad_ids, torch.int32, 1, "bad_ids"), _stream(stream)))
+
+
 def engram_gate(h, kv, q_weight, k_weight, token_mask, T: int, hc: int, dim: int, eps: float,
                 clamp: float, dot_scale: float, stream=None) -> None:
     """Stage 4: update fp32 h [T, hc, dim] in place."""
@@ -217,16 +246,19 @@ class Layer:
     """engram_layer over GPU tensors (kept alive as long as this object)."""
 
     def __init__(self, fmt: int, table, scales, wkv, q_weight, k_weight, hc: int, dim: int,
-                 cols: int):
+                 cols: int, wkv_mx=None, wkv_mx_scales=None):
         row_bytes = Q2K_ROW_BYTES if fmt == ENGRAM_ROWS_Q2K else FP8_ROW_BYTES
         self.num_rows = int(table.numel()) // row_bytes
-        self._keep = (table, scales, wkv, q_weight, k_weight)
+        self._keep = (table, scales, wkv, q_weight, k_weight, wkv_mx, wkv_mx_scales)
+        n, k = (hc + 1) * dim, cols * HEAD_DIM
         self.c = _Layer(int(fmt), self.num_rows,
                         _dptr(table, torch.uint8, self.num_rows * row_bytes, "table"),
                         _dptr(scales, torch.uint8, self.num_rows * FP8_SCALE_BYTES, "scales"),
-                        _dptr(wkv, torch.int16, (hc + 1) * dim * cols * HEAD_DIM, "wkv"),
+                        _dptr(wkv, torch.int16, n * k, "wkv"),
                         _dptr(q_weight, torch.int16, hc * dim, "q_weight"),
-                        _dptr(k_weight, torch.int16, hc * dim, "k_weight"))
+                        _dptr(k_weight, torch.int16, hc * dim, "k_weight"),
+                        _dptr(wkv_mx, torch.uint8, n * k, "wkv_mx"),
+                        _dptr(wkv_mx_scales, torch.uint8, n * (k // 32), "wkv_mx_scales"))
 
 
 def engram_forward(params: HashParams, tokens: Tokens, layers, h, hc: int, dim: int,

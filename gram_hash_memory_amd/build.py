@@ -22,7 +22,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libengram.so")
-SOURCES = ["api.cpp", "hash.hip", "rows.hip", "gemm.hip", "gemm_skinny.hip", "gemm_q2k.hip", "gate.hip"]
+SOURCES = ["api.cpp", "hash.hip", "rows.hip", "gemm.hip", "gemm_skinny.hip", "gemm_q2k.hip",
+           "gemm_mx.hip", "mx_quant.hip", "gate.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

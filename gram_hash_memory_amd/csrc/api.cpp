@@ -23,6 +23,14 @@ engram_status fail(engram_status st, const char *fmt, ...) {
   return st;
 }
 
+// Prefixes the current message with the layer index (copied first: the
+// message buffer is also the destination).
+engram_status fail_layer(engram_status st, int layer) {
+  char msg[sizeof(g_error)];
+  std::memcpy(msg, g_error, sizeof(msg));
+  return fail(st, "layer %d: %s", layer, msg);
+}
+
 engram_status hip_status(hipError_t e, const char *what) {
   if (e == hipSuccess) return ENGRAM_OK;
   return fail(ENGRAM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -213,6 +221,60 @@ engram_status engram_project_q2k(const uint8_t *table, int64_t num_rows, const i
                     "engram_project_q2k launch");
 }
 
+engram_status engram_quantize_mxfp8(const uint16_t *w, int32_t N, int32_t K, uint8_t *codes,
+                                    uint8_t *scales, hipStream_t stream) {
+  REQUIRE(N >= 0, "N=%d < 0", N);
+  REQUIRE(K > 0 && K % 32 == 0, "K=%d must be a positive multiple of 32", K);
+  if (N == 0) return ENGRAM_OK;
+  REQUIRE(w && codes && scales, "w, codes or scales is NULL");
+  REQUIRE(aligned(w, 16) && aligned(codes, 16), "w and codes must be 16-byte aligned");
+  return hip_status(engram::launch_quantize_mx(w, N, K, codes, scales, stream),
+                    "engram_quantize_mxfp8 launch");
+}
+
+namespace {
+engram_status check_project_mx(const uint8_t *table, const uint8_t *scales, int64_t num_rows,
+                               const int32_t *ids, int64_t stride, int32_t cols,
+                               const uint8_t *wc, const uint8_t *ws, const uint16_t *kv,
+                               int32_t T, int32_t N, const int32_t *bad_ids) {
+  engram_status st =
+      check_rows_shape(ENGRAM_ROWS_FP8_E4M3_E8M0, num_rows, stride, cols, T);
+  if (st != ENGRAM_OK) return st;
+  REQUIRE(int64_t(cols) * ENGRAM_HEAD_DIM <= kInt32Max, "cols=%d too large", cols);
+  const int32_t K = cols * ENGRAM_HEAD_DIM;
+  if ((st = check_project_shape(T, K, N)) != ENGRAM_OK) return st;
+  REQUIRE_SUP(engram::project_mx_supported(N, K),
+              "MXFP8 weight of %d x %d bytes exceeds %lld", N, K,
+              (long long)ENGRAM_MX_MAX_WEIGHT_BYTES);
+  REQUIRE_SUP(int64_t(T) * stride * 4 <= ENGRAM_MX_MAX_WEIGHT_BYTES,
+              "T * ids_token_stride * 4 exceeds %lld", (long long)ENGRAM_MX_MAX_WEIGHT_BYTES);
+  if (T == 0) return ENGRAM_OK;
+  REQUIRE(table && aligned(table, 16), "table is NULL or not 16-byte aligned");
+  REQUIRE(scales && aligned(scales, 4), "scales is NULL or not 4-byte aligned");
+  REQUIRE(ids && aligned(ids, 4), "ids is NULL or misaligned");
+  REQUIRE(!bad_ids || aligned(bad_ids, 4), "bad_ids misaligned");
+  REQUIRE(wc && aligned(wc, 16), "wkv codes are NULL or not 16-byte aligned");
+  REQUIRE(ws && aligned(ws, 4), "wkv scales are NULL or not 4-byte aligned");
+  REQUIRE(kv && aligned(kv, 16), "kv is NULL or not 16-byte aligned");
+  return ENGRAM_OK;
+}
+}  // namespace
+
+engram_status engram_project_mxfp8(const uint8_t *table, const uint8_t *scales,
+                                   int64_t num_rows, const int32_t *ids,
+                                   int64_t ids_token_stride, int32_t cols,
+                                   const uint8_t *wkv_codes, const uint8_t *wkv_scales,
+                                   uint16_t *kv, int32_t T, int32_t N, int32_t *bad_ids,
+                                   hipStream_t stream) {
+  engram_status st = check_project_mx(table, scales, num_rows, ids, ids_token_stride, cols,
+                                      wkv_codes, wkv_scales, kv, T, N, bad_ids);
+  if (st != ENGRAM_OK || T == 0) return st;
+  return hip_status(engram::launch_project_mx(table, scales, num_rows, ids, ids_token_stride,
+                                              cols, wkv_codes, wkv_scales, kv, T, N, bad_ids,
+                                              stream),
+                    "engram_project_mxfp8 launch");
+}
+
 engram_status engram_gate(float *h, const uint16_t *kv, const uint16_t *q_weight,
                           const uint16_t *k_weight, const uint8_t *token_mask, int32_t T,
                           int32_t hc, int32_t dim, float eps, float clamp, float dot_scale,
@@ -254,7 +316,7 @@ engram_status engram_forward(const engram_hash_params *params, const engram_toke
   for (int l = 0; l < L; ++l) {
     const engram_layer &ly = layers[l];
     if ((st = check_rows_shape(ly.fmt, ly.num_rows, int64_t(L) * cols, cols, T)) != ENGRAM_OK)
-      return fail(st, "layer %d: %s", l, engram_last_error());
+      return fail_layer(st, l);
     int64_t max_row = 0;
     for (int c = 0; c < cols; ++c)
       max_row = std::max<int64_t>(max_row, int64_t(tab.offset[l][c]) + tab.prime[l][c]);
@@ -275,10 +337,16 @@ engram_status engram_forward(const engram_hash_params *params, const engram_toke
 
   for (int l = 0; l < L; ++l) {
     const engram_layer &ly = layers[l];
-    if ((st = check_rows_ptrs(ly.fmt, ly.table, ly.scales, ids, rows, bad_ids)) != ENGRAM_OK ||
-        (st = check_project_ptrs(rows, ly.wkv, kv)) != ENGRAM_OK ||
-        (st = check_gate_ptrs(h, kv, ly.q_weight, ly.k_weight)) != ENGRAM_OK)
-      return fail(st, "layer %d: %s", l, engram_last_error());
+    if (ly.wkv_mx || ly.wkv_mx_scales) {
+      REQUIRE(ly.fmt == ENGRAM_ROWS_FP8_E4M3_E8M0, "layer %d: wkv_mx needs an FP8 table", l);
+      st = check_project_mx(ly.table, ly.scales, ly.num_rows, ids, int64_t(L) * cols, cols,
+                            ly.wkv_mx, ly.wkv_mx_scales, kv, T, N, bad_ids);
+    } else if ((st = check_rows_ptrs(ly.fmt, ly.table, ly.scales, ids, rows, bad_ids)) ==
+               ENGRAM_OK) {
+      st = check_project_ptrs(rows, ly.wkv, kv);
+    }
+    if (st != ENGRAM_OK || (st = check_gate_ptrs(h, kv, ly.q_weight, ly.k_weight)) != ENGRAM_OK)
+      return fail_layer(st, l);
   }
 
   if ((st = hip_status(engram::launch_hash(tab, *tokens, ids, stream), "hash launch")) !=
@@ -288,8 +356,15 @@ engram_status engram_forward(const engram_hash_params *params, const engram_toke
     const engram_layer &ly = layers[l];
     // Few tokens: rows -> the weight-streaming projection beats the fused
     // 256 x 256 tiles (the dequant is then a few microseconds).
-    if (ly.fmt == ENGRAM_ROWS_Q2K && !engram::project_uses_skinny(T) &&
-        engram::project_q2k_supported(ly.num_rows, cols)) {
+    if (ly.wkv_mx) {
+      if ((st = hip_status(engram::launch_project_mx(ly.table, ly.scales, ly.num_rows,
+                                                     ids + l * cols, int64_t(L) * cols, cols,
+                                                     ly.wkv_mx, ly.wkv_mx_scales, kv, T, N,
+                                                     bad_ids, stream),
+                           "MXFP8 rows+project launch")) != ENGRAM_OK)
+        return st;
+    } else if (ly.fmt == ENGRAM_ROWS_Q2K && !engram::project_uses_skinny(T) &&
+               engram::project_q2k_supported(ly.num_rows, cols)) {
       if ((st = hip_status(engram::launch_project_q2k(ly.table, ly.num_rows, ids + l * cols,
                                                       int64_t(L) * cols, cols, ly.wkv, kv, T,
                                                       N, bad_ids, stream),

@@ -70,6 +70,15 @@ hipError_t launch_project_q2k(const uint8_t *table, int64_t num_rows, const int3
                               uint16_t *c, int32_t M, int32_t N, int32_t *bad_ids,
                               hipStream_t stream);
 
+// MXFP8 projection for FP8 tables (gemm_mx.hip) and its weight prep (mx_quant.hip).
+bool project_mx_supported(int32_t N, int32_t K);
+hipError_t launch_project_mx(const uint8_t *table, const uint8_t *scales, int64_t num_rows,
+                             const int32_t *ids, int64_t ids_token_stride, int32_t cols,
+                             const uint8_t *w_codes, const uint8_t *w_scales, uint16_t *c,
+                             int32_t M, int32_t N, int32_t *bad_ids, hipStream_t stream);
+hipError_t launch_quantize_mx(const uint16_t *w, int32_t N, int32_t K, uint8_t *codes,
+                              uint8_t *scales, hipStream_t stream);
+
 hipError_t launch_gate(float *h, const uint16_t *kv, const uint16_t *qw, const uint16_t *kw,
                        const uint8_t *mask, int32_t T, int32_t hc, int32_t dim, float eps,
                        float clamp, float dot_scale, hipStream_t stream);

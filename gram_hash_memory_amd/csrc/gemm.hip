@@ -67,9 +67,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   auto load_global = [&](int set, int k0) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int soff = int(i * row_step) + k0 * 2;
-      ga[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, voff, soff, 0));
-      gb[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, voff, soff, 0));
+      // The row goes into the VGPR offset: only that part is range-checked.
+      const uint32_t v = voff + i * row_step;
+      ga[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, v, k0 * 2, 0));
+      gb[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, v, k0 * 2, 0));
     }
   };
   auto store_lds = [&](int set, int stage) {

@@ -1,0 +1,324 @@
+// Stages 2 + 3 for FP8 tables as one MXFP8 projection:
+//   kv = bf16( sum_k a[t, k] * w[n, k] ),
+// a = the raw FP8 rows of the table (E4M3 codes, one E8M0 scale per 32
+// values), w = an MXFP8 copy of wkv (engram_quantize_mxfp8).
+//
+// [vLLM engram page, EngramBatch / wkv_input]: an FP8 table row already is a
+// run of MX blocks, so the block-scaled matrix cores can take it as it is
+// stored; the vLLM path feeds the same blocks to an MXFP8 WKV GEMM.  On
+// gfx950 that is v_mfma_scale_f32_32x32x64_f8f6f4: 32 x 32 outputs, 64 k per
+// instruction, each lane's operand bytes scaled by one E8M0 byte of its own.
+//
+// Tiling: 256 x 256 output tile per workgroup, 4 waves of 128 x 128, K in
+// stages of 128 values (128 bytes per operand row, the same LDS footprint per
+// stage as the bf16 kernels' 64).  Every operand byte reaches LDS by DMA:
+//  - A rows are gathered straight from the table: each lane owns one 16-byte
+//    chunk of a tile row and loads it with global_load_lds through a 64-bit
+//    address (tables may exceed the 4 GB a buffer descriptor can span); an id
+//    outside the table, or a row past T, points at a zero row;
+//  - B and both scale vectors come by buffer_load ... lds.
+// A stage's LDS is free again once every wave has read its fragments into
+// registers, which is before the middle barrier of the iteration that
+// multiplies it; the DMA for the stage after next starts right there, one
+// full stage ahead of its use.
+//
+// MFMA operand layout (32x32x64, 8-bit formats): lane l = 32 g + i holds row
+// (A) or column (B) i, bytes 0..15 = k 16 g .. 16 g + 15 and bytes 16..31 =
+// k 32 + 16 g .. 32 + 16 g + 15 of the instruction's 64; its scale byte is
+// the one of MX block g (k 32 g .. 32 g + 31).  A lane keeps its row's four
+// scale bytes of a stage in one dword shifted right by 8 g, so byte 0 is the
+// block of sub-step 0 and byte 2 that of sub-step 1, picked by op_sel.
+#include "gemm_common.hpp"
+
+namespace engram {
+namespace {
+
+using namespace gemm;
+
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kBK = 128;                            // fp8 values per stage
+constexpr int kTileBytes = BM * kBK;                // 32 KB per operand per stage
+constexpr int kScaleBytes = BM * (kBK / 32);        // 1 KB: 4 scale bytes per row
+constexpr int kStageBytes = 2 * kTileBytes + 2 * kScaleBytes;
+constexpr int kSegs = kTileBytes / 1024 / kWaves;   // 1 KB segments per wave per operand: 8
+constexpr int kIdsPerLane = kSegs + 1;              // A code rows + the A scale row
+
+static_assert(2 * kStageBytes >= BM * BN * 2, "the epilogue reuses the stages");
+
+// Stand-in row for ids outside the table and rows past T: zero codes (so the
+// product is exactly 0 whatever the scale) and zero scale bytes (2^-127,
+// finite).
+__device__ __attribute__((aligned(256))) const uint8_t kZeroRow[ENGRAM_HEAD_DIM] = {};
+
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(3))) void *lds_ptr(T *p) {
+  return (__attribute__((address_space(3))) void *)(p);
+}
+
+// Scheduling of one row block: 4 MFMAs with kReads LDS reads spread between
+// them, reads first; the fence keeps the next block's work out of it.
+template <int kReads>
+__device__ __forceinline__ void sched_row() {
+  constexpr int n0 = kReads / 4, n1 = kReads * 2 / 4 - n0, n2 = kReads * 3 / 4 - n0 - n1,
+                n3 = kReads - n0 - n1 - n2;
+  if constexpr (n0 > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, n0, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+  if constexpr (n1 > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, n1, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+  if constexpr (n2 > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, n2, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+  if constexpr (n3 > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, n3, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
+    const uint8_t *__restrict__ table, const uint8_t *__restrict__ tscales, int64_t num_rows,
+    const int32_t *__restrict__ ids, int64_t ids_stride, const uint8_t *__restrict__ W,
+    const uint8_t *__restrict__ WS, uint16_t *__restrict__ C, int M, int N, int K,
+    int tiles_m, int tiles_n, int32_t *__restrict__ bad_ids) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int cols = K / ENGRAM_HEAD_DIM;
+  const int nk = K / kBK;                            // 2 stages per table column
+  const int ks = K / 32;                             // scale bytes per row
+
+  // Ids outside the table, counted once per (row, column) by the first
+  // column of tiles.
+  if (tn == 0 && bad_ids && m0 + tid < M) {
+    const int32_t *id_row = ids + int64_t(m0 + tid) * ids_stride;
+    int bad = 0;
+    for (int c = 0; c < cols; ++c) {
+      const int32_t v = id_row[c];
+      bad += v < 0 || v >= num_rows;
+    }
+    if (bad) atomicAdd(bad_ids, bad);
+  }
+
+  // ---- B codes: one buffer_load ... lds fills a 1 KB segment (8 tile rows);
+  // lane L lands at byte 16 L (row L / 8, physical chunk L % 8) and fetches
+  // the logical chunk the swizzle keeps there; for segment s the row's key is
+  // (L / 8) ^ (s & 1).  Rows past N read as zeros: a buffer load range-checks
+  // its VGPR offset only, so every row offset goes there and the SGPR offset
+  // carries just the position along K.
+  const int seg_row = lane >> 3;
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(W + int64_t(n0) * K, int64_t(N - n0) * K);
+  const uint32_t voff_even = uint32_t(seg_row * K + ((lane & 7) ^ seg_row) * 16);
+  const uint32_t voff_odd = uint32_t(seg_row * K + ((lane & 7) ^ seg_row ^ 1) * 16);
+  // ---- B scales: lane L of wave w brings the stage's 4 bytes of row 64 w + L.
+  const __amdgpu_buffer_rsrc_t rbs = make_rsrc(WS + int64_t(n0) * ks, int64_t(N - n0) * ks);
+  const uint32_t voff_bs = uint32_t((wave * 64 + lane) * ks);
+
+  // ---- A: per table column, the lane's 8 code rows 64 w + 8 k + L / 8
+  // (chunk as for B) and its scale row 64 w + L, resolved from the ids into
+  // 64-bit addresses.  The ids come through a buffer descriptor (rows past T
+  // read as 0 and are replaced below), loaded two columns ahead of their use.
+  const __amdgpu_buffer_rsrc_t rid = make_rsrc(ids, int64_t(M) * ids_stride * 4);
+  const int row0 = m0 + wave * 64;
+  const uint32_t voff_id = uint32_t((row0 + seg_row) * ids_stride * 4);
+  const uint32_t voff_ids = uint32_t((row0 + lane) * ids_stride * 4);
+  const int chunk_even = ((lane & 7) ^ seg_row) * 16, chunk_odd = chunk_even ^ 16;
+  int32_t idn[kIdsPerLane];
+  const uint8_t *a_src[kSegs];
+  const uint8_t *as_src;
+  auto load_ids = [&](int c) {
+    c = min(c, cols - 1);
+#pragma unroll
+    for (int k = 0; k < kSegs; ++k)
+      idn[k] = __builtin_amdgcn_raw_buffer_load_b32(
+          rid, voff_id + uint32_t(8 * k * ids_stride * 4), c * 4, 0);
+    idn[kSegs] = __builtin_amdgcn_raw_buffer_load_b32(rid, voff_ids, c * 4, 0);
+  };
+  auto resolve = [&]() {
+#pragma unroll
+    for (int k = 0; k < kSegs; ++k) {
+      const bool ok = row0 + 8 * k + seg_row < M && idn[k] >= 0 && idn[k] < num_rows;
+      a_src[k] = (ok ? table + int64_t(idn[k]) * ENGRAM_HEAD_DIM : kZeroRow) +
+                 ((k & 1) ? chunk_odd : chunk_even);
+    }
+    const bool ok = row0 + lane < M && idn[kSegs] >= 0 && idn[kSegs] < num_rows;
+    as_src = ok ? tscales + int64_t(idn[kSegs]) * (ENGRAM_HEAD_DIM / 32) : kZeroRow;
+  };
+  // Stage kt (values 128 kt .. 128 kt + 127: half kt % 2 of column kt / 2)
+  // into LDS buffer `buf`.  `half` is kt % 2 as a constant, since it is the
+  // instruction's immediate offset into the row; a_src/as_src must hold
+  // column kt / 2 (clamped to the last column).
+  auto dma = [&](int buf, int kt, const int half) {
+    uint8_t *st = smem + buf * kStageBytes;
+    const int kb = min(kt, nk - 1);
+#pragma unroll
+    for (int i = 0; i < kSegs; ++i) {
+      const int seg = wave * kSegs + i;
+      if (half == 0)
+        __builtin_amdgcn_global_load_lds(a_src[i], lds_ptr(st + seg * 1024), 16, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(a_src[i], lds_ptr(st + seg * 1024), 16, kBK, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kSegs; ++i) {
+      const int seg = wave * kSegs + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, lds_ptr(st + kTileBytes + seg * 1024), 16,
+                                               ((i & 1) ? voff_odd : voff_even) + seg * 8 * K,
+                                               kb * kBK, 0, 0);
+    }
+    if (half == 0)
+      __builtin_amdgcn_global_load_lds(as_src, lds_ptr(st + 2 * kTileBytes + wave * 256), 4, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(as_src, lds_ptr(st + 2 * kTileBytes + wave * 256), 4, 4, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rbs, lds_ptr(st + 2 * kTileBytes + kScaleBytes + wave * 256), 4, voff_bs, kb * 4, 0, 0);
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  // Fragments: the wave's 4 B fragments of the current and of the next
+  // sub-step, and a ring of 2 A fragments (row block i multiplies while row
+  // block i + 1 is read).  Fragment f of sub-step s is chunks 4 s + g and
+  // 4 s + 2 + g of row f * 32 + frow of the wave's operand rows; the swizzle
+  // key of those rows is that of frow, so a lane's chunk offsets are the
+  // same for all four fragments.
+  const int frow = lane & 31, fhalf = lane >> 5;
+  const int fkey = swz_key<64>(frow);
+  const int a_frag = (wm * 128 + frow) * kBK, b_frag = kTileBytes + (wn * 128 + frow) * kBK;
+  i32x8 fa[2], fb[2][4];
+  uint32_t sca[2][4], scb[2][4];
+  auto read_frag = [&](int buf, int base, int f, const int s) {
+    const uint8_t *p = smem + buf * kStageBytes + base + f * 32 * kBK;
+    const u32x4 lo = *reinterpret_cast<const u32x4 *>(p + (((4 * s + fhalf) ^ fkey) << 4));
+    const u32x4 hi = *reinterpret_cast<const u32x4 *>(p + (((4 * s + 2 + fhalf) ^ fkey) << 4));
+    return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto load_scales = [&](int buf, const int set) {
+    const uint32_t *ss = reinterpret_cast<const uint32_t *>(smem + buf * kStageBytes +
+                                                            2 * kTileBytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sca[set][i] = ss[wm * 128 + i * 32 + frow] >> (8 * fhalf);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) scb[set][j] = ss[BM + wn * 128 + j * 32 + frow] >> (8 * fhalf);
+  };
+  // Row block i of sub-step s: A fragment fa[fs] against the 4 B fragments
+  // fb[bs], scales of set `set` (op_sel 0 picks sub-step 0's block, 2 sub-step 1's).
+  auto mfma_row = [&](const int i, const int fs, const int bs, const int set, const int s) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (s == 0)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            fa[fs], fb[bs][j], acc[i][j], 0, 0, 0, sca[set][i], 0, scb[set][j]);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            fa[fs], fb[bs][j], acc[i][j], 0, 0, 2, sca[set][i], 2, scb[set][j]);
+    }
+  };
+  // Iteration kt multiplies the stage in buffer j = kt % 2; on entry fa[0]
+  // and fb[0] hold its sub-step 0 fragments and sca/scb[j] its scales.
+  //  - at even kt, the ids of column kt / 2 + 2 are requested (9 loads);
+  //  - sub-step 0 reads the next A fragments and sub-step 1's B fragments;
+  //  - sub-step 1 reads its own A fragments; after row block 2 (the last
+  //    read of buffer j), the barrier waits for stage kt + 1's DMA (issued
+  //    one iteration ago; at even kt only the 9 younger id loads may stay in
+  //    flight) and for every wave's reads of buffer j;
+  //  - buffer j then takes stage kt + 2 (column kt / 2 + 1, half j), and at
+  //    odd kt the addresses of column kt / 2 + 2 are resolved for the next
+  //    two DMAs;
+  //  - stage kt + 1's sub-step 0 fragments and scales are read while the
+  //    last row block of stage kt multiplies.
+  auto iteration = [&](int kt, const int j) {
+    const int b = j;
+    __builtin_amdgcn_sched_barrier(0);
+    if (j == 0) load_ids(kt / 2 + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    fa[1] = read_frag(b, a_frag, 1, 0);
+    fb[1][0] = read_frag(b, b_frag, 0, 1);
+    mfma_row(0, 0, 0, j, 0);
+    sched_row<4>();
+    fa[0] = read_frag(b, a_frag, 2, 0);
+    fb[1][1] = read_frag(b, b_frag, 1, 1);
+    mfma_row(1, 1, 0, j, 0);
+    sched_row<4>();
+    fa[1] = read_frag(b, a_frag, 3, 0);
+    fb[1][2] = read_frag(b, b_frag, 2, 1);
+    mfma_row(2, 0, 0, j, 0);
+    sched_row<4>();
+    fa[0] = read_frag(b, a_frag, 0, 1);
+    fb[1][3] = read_frag(b, b_frag, 3, 1);
+    mfma_row(3, 1, 0, j, 0);
+    sched_row<4>();
+    fa[1] = read_frag(b, a_frag, 1, 1);
+    mfma_row(0, 0, 1, j, 1);
+    sched_row<2>();
+    fa[0] = read_frag(b, a_frag, 2, 1);
+    mfma_row(1, 1, 1, j, 1);
+    sched_row<2>();
+    fa[1] = read_frag(b, a_frag, 3, 1);
+    mfma_row(2, 0, 1, j, 1);
+    sched_row<2>();
+    if (j == 0) stage_barrier<waitcnt(kIdsPerLane, 0)>();
+    else stage_barrier<waitcnt(0, 0)>();
+    dma(b, kt + 2, j);
+    if (j == 1) resolve();
+    __builtin_amdgcn_sched_barrier(0);
+    fa[0] = read_frag(b ^ 1, a_frag, 0, 0);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) fb[0][f] = read_frag(b ^ 1, b_frag, f, 0);
+    load_scales(b ^ 1, j ^ 1);
+    mfma_row(3, 1, 1, j, 1);
+    sched_row<18>();
+  };
+
+  // Prologue: stages 0 and 1 (column 0) in flight, then column 1's addresses.
+  load_ids(0);
+  resolve();
+  dma(0, 0, 0);
+  dma(1, 1, 1);
+  load_ids(1);
+  resolve();
+  stage_barrier<waitcnt(0, 0)>();
+  fa[0] = read_frag(0, a_frag, 0, 0);
+#pragma unroll
+  for (int f = 0; f < 4; ++f) fb[0][f] = read_frag(0, b_frag, f, 0);
+  load_scales(0, 0);
+
+  for (int kt = 0; kt < nk; kt += 2) {               // nk = 2 * cols is even
+    iteration(kt, 0);
+    iteration(kt + 1, 1);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
+  __syncthreads();                                   // every wave is done with the stages
+  store_tile(acc, reinterpret_cast<uint16_t *>(smem), C, M, N, m0, n0, wm, wn, lane, tid);
+}
+
+}  // namespace
+
+bool project_mx_supported(int32_t N, int32_t K) {
+  return int64_t(N) * K <= 0x7FFFFFF0LL;
+}
+
+hipError_t launch_project_mx(const uint8_t *table, const uint8_t *scales, int64_t num_rows,
+                             const int32_t *ids, int64_t ids_token_stride, int32_t cols,
+                             const uint8_t *w_codes, const uint8_t *w_scales, uint16_t *c,
+                             int32_t M, int32_t N, int32_t *bad_ids, hipStream_t stream) {
+  const int K = cols * ENGRAM_HEAD_DIM;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const size_t lds = size_t(2) * kStageBytes;
+  const void *fn = reinterpret_cast<const void *>(&gemm_mx_kernel);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gemm_mx_kernel, dim3(tiles_m * tiles_n), dim3(kThreads), lds, stream,
+                     table, scales, num_rows, ids, ids_token_stride, w_codes, w_scales, c, M, N,
+                     K, tiles_m, tiles_n, bad_ids);
+  return hipGetLastError();
+}
+
+}  // namespace engram

@@ -56,7 +56,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
   // (8 tile rows); lane L lands at byte 16 L, i.e. row L / 8 of the segment,
   // physical chunk L % 8, and fetches the logical chunk the swizzle keeps
   // there.  For segment s the swizzle key of that row is (L / 8) ^ (s & 1).
-  // Rows past N read as zeros (the resource starts at the tile's first row).
+  // Rows past N read as zeros (the resource starts at the tile's first row,
+  // and the row is part of the VGPR offset, the range-checked part; the
+  // SGPR offset only carries the K position).
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + int64_t(n0) * K, int64_t(N - n0) * K * 2);
   const int seg_row = lane >> 3;
   const uint32_t voff_even = uint32_t(seg_row * K + ((lane & 7) ^ seg_row) * 8) * 2;
@@ -69,8 +71,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
     for (int i = 0; i < kSegs; ++i) {
       const int seg = wave * kSegs + i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, sb + seg * 512, 16,
-                                               (i & 1) ? voff_odd : voff_even,
-                                               int(seg * seg_stride) + k0 * 2, 0, 0);
+                                               ((i & 1) ? voff_odd : voff_even) + seg * seg_stride,
+                                               k0 * 2, 0, 0);
     }
   };
 

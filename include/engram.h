@@ -130,6 +130,10 @@ typedef struct engram_tokens {
  *   wkv [(hc+1)*dim][cols*256] bf16, row-major (the projection's weight;
  *        output o = sum_k rows[k] * wkv[o][k]).
  *   q_weight, k_weight [hc][dim] bf16 (learned branch-norm weights).
+ *   wkv_mx, wkv_mx_scales: NULL, or (FP8 layers only) the MXFP8 copy of wkv
+ *        from engram_quantize_mxfp8, codes [(hc+1)*dim][cols*256] and scales
+ *        [(hc+1)*dim][cols*8].  When given, the layer projects its raw FP8
+ *        rows against them (engram_project_mxfp8) and wkv may be NULL.
  */
 typedef struct engram_layer {
   engram_row_format fmt;
@@ -139,6 +143,8 @@ typedef struct engram_layer {
   const uint16_t *wkv;
   const uint16_t *q_weight;
   const uint16_t *k_weight;
+  const uint8_t *wkv_mx;
+  const uint8_t *wkv_mx_scales;
 } engram_layer;
 
 /* Stage 1 -- n-gram hash ([spark] overview stage 1; [vLLM] EngramLayout,
@@ -214,6 +220,47 @@ ENGRAM_API engram_status engram_project_q2k(const uint8_t *table, int64_t num_ro
                                  const uint16_t *wkv, uint16_t *kv, int32_t T, int32_t N,
                                  int32_t *bad_ids, hipStream_t stream);
 
+/* MXFP8 copy of a bf16 weight, for engram_project_mxfp8 ([vLLM] EngramBatch:
+ * the WKV GEMM there takes MXFP8 operands, in the OCP MX v1.0 format).
+ *   w DEVICE bf16 [N][K], K % 32 == 0; codes DEVICE [N][K] e4m3fn, 16-byte
+ *   aligned; scales DEVICE [N][K/32] e8m0 (byte b means 2^(b-127)).
+ *   Per 32 consecutive k of a row: amax = max |w|; scale byte =
+ *   floor(log2 amax) - 8 + 127 clamped to 0..254 (127 when amax = 0); each
+ *   code is w / 2^(byte-127) saturated to +-448 and rounded to the nearest
+ *   E4M3 value, ties to even (negative zero keeps its sign).  Inf/NaN inputs
+ *   are not supported.  Runs once per weight; the result is deterministic.
+ */
+ENGRAM_API engram_status engram_quantize_mxfp8(const uint16_t *w, int32_t N, int32_t K,
+                                               uint8_t *codes, uint8_t *scales,
+                                               hipStream_t stream);
+
+/* Stages 2 + 3 for FP8 tables in MXFP8 ([vLLM] EngramBatch / wkv_input: FP8
+ * rows with per-32 E8M0 scales are MX blocks already): kv[t][n] =
+ * bf16(sum_k a[t][k] * w[n][k]), a[t][r*256 + i] = e4m3(table[ids[t][r]][i])
+ * * 2^(scales[ids[t][r]][i/32] - 127), w = wkv_codes/wkv_scales likewise.
+ * The rows are read raw by the block-scaled matrix cores
+ * (v_mfma_scale_f32_32x32x64_f8f6f4) and never dequantised to memory;
+ * products accumulate in fp32 and each output is rounded to bf16 once.
+ *   table DEVICE [num_rows][256] e4m3fn codes, 16-byte aligned; scales DEVICE
+ *   [num_rows][8], 4-byte aligned; ids, ids_token_stride, cols, bad_ids as for
+ *   engram_rows (K = cols * 256; an id outside the table contributes 0);
+ *   wkv_codes DEVICE [N][K], 16-byte aligned, and wkv_scales DEVICE [N][K/32],
+ *   4-byte aligned, from engram_quantize_mxfp8; kv DEVICE bf16 [T][N], 16-byte
+ *   aligned, fully overwritten.
+ *   Limits: N * K <= ENGRAM_MX_MAX_WEIGHT_BYTES and T * ids_token_stride * 4 <=
+ *   ENGRAM_MX_MAX_WEIGHT_BYTES (both are read through 32-bit-offset buffer
+ *   descriptors); beyond either the call returns ENGRAM_ERR_UNSUPPORTED.  The
+ *   table has no size limit (its rows are read through 64-bit addresses).
+ */
+#define ENGRAM_MX_MAX_WEIGHT_BYTES 2147483632LL
+ENGRAM_API engram_status engram_project_mxfp8(const uint8_t *table, const uint8_t *scales,
+                                              int64_t num_rows, const int32_t *ids,
+                                              int64_t ids_token_stride, int32_t cols,
+                                              const uint8_t *wkv_codes,
+                                              const uint8_t *wkv_scales, uint16_t *kv,
+                                              int32_t T, int32_t N, int32_t *bad_ids,
+                                              hipStream_t stream);
+
 /* Stage 4 -- gate, in place on the fp32 highway ([spark] overview stage 4;
  * [NeMo] _engram_gate_core, compile_engram_gate; [vLLM] Engram).
  *   h DEVICE fp32 [T][hc][dim], updated in place.
@@ -240,7 +287,8 @@ ENGRAM_API size_t engram_workspace_bytes(int32_t T, int32_t n_layers, int32_t co
 /* The whole forward ([spark] overview, stages 1-4): hash every layer once,
  * then for each layer in order: rows -> projection -> gate on the same h.
  * Q2_K layers within the limits of engram_project_q2k run rows -> projection
- * as that fused kernel (same kv bits) when T > 128.
+ * as that fused kernel (same kv bits) when T > 128.  FP8 layers that carry
+ * wkv_mx run engram_project_mxfp8 instead of rows -> projection.
  *   layers: HOST array [params->n_layers] of DEVICE-pointer descriptors.
  *   workspace: DEVICE, at least engram_workspace_bytes(...) bytes, 256-byte
  *   aligned; its contents are scratch.  Every other argument is as for the

@@ -33,7 +33,8 @@ def declared_functions():
 
 def test_header_declares_the_five_calls_and_helpers():
     names = declared_functions()
-    for want in ("engram_hash", "engram_rows", "engram_project", "engram_project_q2k", "engram_gate",
+    for want in ("engram_hash", "engram_rows", "engram_project", "engram_project_q2k",
+                 "engram_quantize_mxfp8", "engram_project_mxfp8", "engram_gate",
                  "engram_forward", "engram_workspace_bytes", "engram_last_error"):
         assert want in names
 
@@ -81,6 +82,13 @@ class _TK(ctypes.Structure):
                 ("lookback_live", ctypes.c_void_p)]
 
 
+class _LY(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int), ("num_rows", ctypes.c_int64), ("table", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("wkv", ctypes.c_void_p),
+                ("q_weight", ctypes.c_void_p), ("k_weight", ctypes.c_void_p),
+                ("wkv_mx", ctypes.c_void_p), ("wkv_mx_scales", ctypes.c_void_p)]
+
+
 FAKE = 0x10000      # aligned, never dereferenced by the host checks
 
 
@@ -97,6 +105,18 @@ def _raw(eg):
                                        ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_void_p, ctypes.c_void_p]
+    lib.engram_quantize_mxfp8.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.engram_project_mxfp8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+    lib.engram_forward.argtypes = [ctypes.POINTER(_HP), ctypes.POINTER(_TK),
+                                   ctypes.POINTER(_LY), ctypes.c_void_p, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_float, ctypes.c_float,
+                                   ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_void_p, ctypes.c_void_p]
     lib.engram_gate.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int32] * 3 +
                                 [ctypes.c_float] * 3 + [ctypes.c_void_p])
     return lib
@@ -199,6 +219,64 @@ class TestValidation:
         assert "exceeds" in lib.engram_last_error().decode()
         assert call(nrows=too_many - 1, T=0, table=None, ids=None, wkv=None,
                     kv=None) == eg.ENGRAM_OK
+
+    def test_quantize_mxfp8_rejects(self, eg):
+        lib = _raw(eg)
+        for args in ((FAKE, 8, 0, FAKE, FAKE), (FAKE, 8, 48, FAKE, FAKE),
+                     (FAKE, -1, 64, FAKE, FAKE), (None, 8, 64, FAKE, FAKE),
+                     (FAKE, 8, 64, None, FAKE), (FAKE, 8, 64, FAKE, None),
+                     (FAKE + 2, 8, 64, FAKE, FAKE), (FAKE, 8, 64, FAKE + 4, FAKE)):
+            assert lib.engram_quantize_mxfp8(*args, None) == eg.ENGRAM_ERR_ARG, args
+        assert lib.engram_quantize_mxfp8(None, 0, 64, None, None, None) == eg.ENGRAM_OK
+
+    def test_project_mxfp8_rejects(self, eg):
+        lib = _raw(eg)
+        ok = dict(table=FAKE, scales=FAKE, nrows=100, ids=FAKE, stride=24, cols=24, wc=FAKE,
+                  ws=FAKE, kv=FAKE, T=8, N=512, bad=None)
+
+        def call(**kw):
+            a = dict(ok, **kw)
+            return lib.engram_project_mxfp8(a["table"], a["scales"], a["nrows"], a["ids"],
+                                            a["stride"], a["cols"], a["wc"], a["ws"], a["kv"],
+                                            a["T"], a["N"], a["bad"], None)
+        for kw in (dict(nrows=0), dict(cols=0), dict(stride=23), dict(T=-1), dict(N=0),
+                   dict(table=None), dict(table=FAKE + 4), dict(scales=None),
+                   dict(scales=FAKE + 2), dict(ids=None), dict(ids=FAKE + 1), dict(wc=None),
+                   dict(wc=FAKE + 8), dict(ws=None), dict(ws=FAKE + 1), dict(kv=None),
+                   dict(kv=FAKE + 8), dict(bad=FAKE + 2)):
+            assert call(**kw) == eg.ENGRAM_ERR_ARG, kw
+        # the weight and the ids are read through 32-bit-offset buffer descriptors
+        assert call(N=2147483632 // 6144 + 1) == eg.ENGRAM_ERR_UNSUPPORTED
+        assert "exceeds" in lib.engram_last_error().decode()
+        assert call(T=2147483632 // (24 * 4) + 1) == eg.ENGRAM_ERR_UNSUPPORTED
+        # a table of 2^32 bytes and more is fine (64-bit row addresses)
+        assert call(nrows=2**25, T=0, table=None, ids=None, wc=None, ws=None,
+                    kv=None) == eg.ENGRAM_OK
+
+    def test_forward_mx_layer_rejects(self, eg):
+        lib = _raw(eg)
+        m, p, o = _tables()
+        hp = _hp(m, p, o)
+        tk = _TK(16, 1, 0, FAKE, FAKE, None, None, None, None)
+        F, Q = eg.ENGRAM_ROWS_FP8_E4M3_E8M0, eg.ENGRAM_ROWS_Q2K
+        ws = eg.engram_workspace_bytes(16, 1, 6, 2, 64)
+
+        def call(**kw):
+            d = dict(fmt=F, num_rows=64, table=FAKE, scales=FAKE, wkv=None, q_weight=FAKE,
+                     k_weight=FAKE, wkv_mx=FAKE, wkv_mx_scales=FAKE)
+            d.update(kw)
+            ly = _LY(d["fmt"], d["num_rows"], d["table"], d["scales"], d["wkv"],
+                     d["q_weight"], d["k_weight"], d["wkv_mx"], d["wkv_mx_scales"])
+            return lib.engram_forward(ctypes.byref(hp), ctypes.byref(tk), ctypes.byref(ly), FAKE,
+                                      2, 64, 1e-6, 1e-6, 0.1, FAKE, ws, None, None)
+        for kw, msg in ((dict(fmt=Q, scales=None), "FP8"), (dict(wkv_mx_scales=None), "scales"),
+                        (dict(wkv_mx=None), "codes"), (dict(wkv_mx=FAKE + 8), "codes"),
+                        (dict(scales=None), "scales"), (dict(table=FAKE + 4), "table")):
+            assert call(**kw) == eg.ENGRAM_ERR_ARG, kw
+            err = lib.engram_last_error().decode()
+            assert err.startswith("layer 0: ") and msg in err, (kw, err)
+        # without wkv_mx the layer needs the bf16 wkv
+        assert call(wkv_mx=None, wkv_mx_scales=None) == eg.ENGRAM_ERR_ARG
 
     def test_gate_rejects(self, eg):
         lib = _raw(eg)

@@ -454,3 +454,221 @@ def test_binding_rejects_short_buffers(eg):
     short = torch.empty(s.T * s.cols - 1, dtype=torch.int32, device="cuda")
     with pytest.raises(ValueError):
         eg.engram_hash(params, tokens, short)
+
+
+# ------------------------------------------------ MXFP8 projection (FP8 tables)
+
+FP8_CONFIGS = [c for c in CONFIGS if workloads.SPECS[c].fmt == "fp8"]
+
+
+def _oracle_mx_weight(wkv_bits, chunk=2048):
+    """oracle.quantize_mxfp8 of a bf16 weight, in row chunks (it is row-wise)."""
+    n, k = wkv_bits.shape
+    codes = np.empty((n, k), np.uint8)
+    scales = np.empty((n, k // 32), np.uint8)
+    for a in range(0, n, chunk):
+        codes[a:a + chunk], scales[a:a + chunk] = oracle.quantize_mxfp8(wkv_bits[a:a + chunk])
+    return codes, scales
+
+
+def _gpu_mx_weight(eg, wkv_dev, N, K):
+    codes = torch.full((N, K), 0x55, dtype=torch.uint8, device="cuda")
+    scales = torch.full((N, K // 32), 0x55, dtype=torch.uint8, device="cuda")
+    eg.engram_quantize_mxfp8(wkv_dev, N, K, codes, scales)
+    return codes, scales
+
+
+def _check_kv_mx(got_bits, a_codes, a_scales, w_codes, w_scales):
+    """The projection bar for MXFP8 operands: one bf16 ulp + K * 2^-24 * sum|a||w|
+    against the oracle's exactly summed, once-rounded value."""
+    want = oracle.bf16_value(oracle.project_mxfp8(a_codes, a_scales, w_codes, w_scales))
+    got = oracle.bf16_value(got_bits)
+    a, b = oracle.mx_values(a_codes, a_scales), oracle.mx_values(w_codes, w_scales)
+    K = a.shape[1]
+    bound = bf16_ulp(np.maximum(np.abs(want), np.abs(got))) + K * 2.0 ** -24 * (np.abs(a) @ np.abs(b).T)
+    err = np.abs(got - want)
+    assert (err <= bound).all(), f"max err/bound {np.max(err / bound):.3f}"
+    return float(np.mean(got == want))
+
+
+def test_quantize_mxfp8_bit_exact_edge_blocks(eg):
+    # Blocks over 2^-40 .. 2^40, a zero and a negative-zero block, subnormal
+    # bf16 inputs, huge values, round-to-even ties, saturation and negative
+    # zeros inside a block: codes and scale bytes must equal the oracle's.
+    rng = np.random.default_rng(21)
+    N, K = 67, 1536
+    w = rng.standard_normal((N, K)) * np.repeat(2.0 ** rng.integers(-40, 40, (N, K // 32)), 32,
+                                                axis=1)
+    w[0, :32] = 0.0
+    w[0, 32:64] = -0.0
+    w[1, :32] = 2.0 ** -130 * rng.standard_normal(32)
+    w[2, :32] = 1e38 * rng.standard_normal(32)
+    w[3, :32] = 0.0
+    w[3, :9] = [256.0, 1.0625, 1.1875, -1.0625, 3 * 2.0 ** -10, 2.0 ** -10, -0.0, -2.0 ** -12,
+                2.0 ** -6 - 2.0 ** -10]
+    w[4, :32] = 0.5
+    w[4, :3] = [500.0, -480.0, 448.0]
+    wb = oracle.bf16_bits(oracle.bf16_round(w))
+    want_c, want_s = oracle.quantize_mxfp8(wb)
+    codes, scales = _gpu_mx_weight(eg, tensor(wb, "cuda"), N, K)
+    assert np.array_equal(scales.cpu().numpy(), want_s)
+    got_c = codes.cpu().numpy()
+    bad = np.argwhere(got_c != want_c)
+    assert len(bad) == 0, f"{len(bad)} codes differ, first at {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("c", FP8_CONFIGS)
+def test_quantize_mxfp8_workload_weight_sampled(eg, c):
+    wl = host(c)
+    s = wl.spec
+    for layer in range(len(s.layer_ids)):
+        codes, scales = _gpu_mx_weight(eg, dev(c).layers[layer].wkv, s.N, s.K)
+        pick = np.sort(np.random.default_rng(c).choice(s.N, 384, replace=False))
+        pick[0], pick[-1] = 0, s.N - 1
+        want_c, want_s = oracle.quantize_mxfp8(wl.layers[layer].wkv[pick])
+        assert np.array_equal(scales.cpu().numpy()[pick], want_s)
+        assert np.array_equal(codes.cpu().numpy()[pick], want_c)
+
+
+@pytest.mark.parametrize("T,cols,N,stride", [(1, 1, 64, 1), (3, 3, 320, 3), (255, 5, 520, 5),
+                                             (257, 6, 256, 12), (300, 24, 4096, 24),
+                                             (513, 2, 1000, 2), (600, 24, 700, 48)])
+def test_project_mxfp8_ragged_and_bad_ids(eg, T, cols, N, stride):
+    # Ragged tiles in M and N, few and many columns, ids read with a stride
+    # (as for one layer of several), and ids outside the table (zero rows,
+    # counted once per (token, column)).
+    rng = np.random.default_rng(11 * T + cols)
+    R = 777
+    table_np, scales_np = workloads.fp8_table(4, 0, R)
+    ids_full = rng.integers(0, R, (T, stride)).astype(np.int32)
+    bad_mask = rng.random((T, stride)) < 0.05
+    ids_full[bad_mask] = rng.choice([-1, R, R + 5, 2**31 - 1, -(2**31)], int(bad_mask.sum()))
+    off = stride - cols                         # read the last `cols` of each token's ids
+    ids_np = ids_full[:, off:]
+    K = cols * 256
+    wkv_np = oracle.bf16_bits(oracle.bf16_round(0.05 * rng.standard_normal((N, K))))
+    w_codes, w_scales = oracle.quantize_mxfp8(wkv_np)
+    table, tscales = tensor(table_np, "cuda"), tensor(scales_np, "cuda")
+    ids = tensor(ids_full, "cuda")
+    kv = torch.full((T, N), 0x7777, dtype=torch.int16, device="cuda")
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    eg.engram_project_mxfp8(table, tscales, R, ids.view(-1)[off:], stride, cols,
+                            tensor(w_codes, "cuda"), tensor(w_scales, "cuda"), kv, T, N, bad)
+    assert bad.item() == int(bad_mask[:, off:].sum())
+    # the GPU's own MXFP8 copy of the weight is the oracle's, bit for bit
+    gc, gs = _gpu_mx_weight(eg, tensor(wkv_np, "cuda"), N, K)
+    assert np.array_equal(gc.cpu().numpy(), w_codes) and np.array_equal(gs.cpu().numpy(), w_scales)
+    a_codes, a_scales = oracle.rows_fp8_mx(table_np, scales_np, ids_np)
+    exact = _check_kv_mx(kv.cpu().numpy().view(np.uint16), a_codes, a_scales, w_codes, w_scales)
+    assert exact > 0.9, exact
+
+
+@pytest.mark.parametrize("c", FP8_CONFIGS)
+def test_project_mxfp8_workload_sampled(eg, c):
+    # Full size, the launch the forward makes: every token, every output;
+    # checked on sampled tokens x sampled outputs.
+    wl = host(c)
+    s = wl.spec
+    for layer in range(len(s.layer_ids)):
+        ids = torch.empty((s.T, len(s.layer_ids), s.cols), dtype=torch.int32, device="cuda")
+        params, tokens, _, _ = binding_objs(eg, c)
+        eg.engram_hash(params, tokens, ids)
+        L = dev(c).layers[layer]
+        w_codes, w_scales = _gpu_mx_weight(eg, L.wkv, s.N, s.K)
+        kv = torch.full((s.T, s.N), 0x7777, dtype=torch.int16, device="cuda")
+        bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+        eg.engram_project_mxfp8(L.table, L.scales, L.table.numel() // 256,
+                                ids.view(-1)[layer * s.cols:], len(s.layer_ids) * s.cols,
+                                s.cols, w_codes, w_scales, kv, s.T, s.N, bad)
+        assert bad.item() == 0
+        pick = sample_tokens(wl)
+        outs = np.sort(np.random.default_rng(layer).choice(s.N, 1024, replace=False))
+        outs[0], outs[-1] = 0, s.N - 1
+        hl = wl.layers[layer]
+        a_codes, a_scales = oracle.rows_fp8_mx(hl.table, hl.scales, oracle_ids(c)[pick, layer])
+        wc, ws = oracle.quantize_mxfp8(hl.wkv[outs])
+        got = kv.cpu().numpy().view(np.uint16)[pick][:, outs]
+        exact = _check_kv_mx(got, a_codes, a_scales, wc, ws)
+        print(f"config {c} layer {layer}: {exact:.4f} of sampled kv bit-exact", flush=True)
+
+
+def _mx_layer(eg, fmt, dl, hc, dim, cols, wkv_mx):
+    return eg.Layer(fmt, dl.table, dl.scales, None, dl.q_weight, dl.k_weight, hc, dim, cols,
+                    wkv_mx=wkv_mx[0], wkv_mx_scales=wkv_mx[1])
+
+
+@pytest.mark.parametrize("c", FP8_CONFIGS)
+def test_forward_mx_against_oracle(eg, c):
+    # The forward with FP8 layers projected in MXFP8 against the oracle's
+    # forward with the oracle's MXFP8 weight copy, at the highway bar.
+    wl = host(c)
+    s = wl.spec
+    params, tokens, _, fmt = binding_objs(eg, c)
+    layers = [_mx_layer(eg, fmt, dl, s.hc, s.dim, s.cols, _gpu_mx_weight(eg, dl.wkv, s.N, s.K))
+              for dl in dev(c).layers]
+    h = dev(c).h.clone()
+    ws = torch.empty(eg.engram_workspace_bytes(s.T, len(s.layer_ids), s.cols, s.hc, s.dim),
+                     dtype=torch.uint8, device="cuda")
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    eg.engram_forward(params, tokens, layers, h, s.hc, s.dim, s.eps, s.clamp, s.dot_scale, ws,
+                      bad)
+    got = h.cpu().numpy()
+    assert bad.item() == 0
+    pick = sample_tokens(wl)
+    ids = oracle_ids(c)[pick]
+    want = wl.h[pick]
+    for l, L in enumerate(wl.layers):
+        a_codes, a_scales = oracle.rows_fp8_mx(L.table, L.scales, ids[:, l])
+        kv = oracle.project_mxfp8(a_codes, a_scales, *_oracle_mx_weight(L.wkv))
+        mask = None if wl.token_mask is None else wl.token_mask[pick]
+        want = oracle.gate(want, kv, L.q_weight, L.k_weight, mask, s.eps, s.clamp, s.dot_scale)
+    err = np.abs(got[pick] - want) / np.maximum(1.0, np.abs(want))
+    print(f"config {c} (MXFP8): max rel err {err.max():.3e} over {len(pick)} tokens", flush=True)
+    assert err.max() <= 1e-2
+    if wl.token_mask is not None:
+        off = np.flatnonzero(wl.token_mask == 0)
+        assert np.array_equal(got[off].view(np.uint32), wl.h[off].view(np.uint32))
+
+
+@pytest.mark.parametrize("T", [100, 300])
+def test_forward_mx_small_full_compare(eg, T):
+    # Two FP8 layers, both in MXFP8, every token checked against oracle.forward.
+    from oracle.layout import engram_layout, hash_multipliers
+    max_ngram, n_heads, V, hc, dim = 4, 2, 3000, 2, 128
+    cols = (max_ngram - 1) * n_heads
+    primes, offsets = engram_layout(2, max_ngram, n_heads, 4099)
+    R = int((offsets + primes).max())
+    hp = dict(multipliers=hash_multipliers([1, 14], max_ngram, V), primes=primes,
+              offsets=offsets, max_ngram=max_ngram, n_heads=n_heads, pad_id=0)
+    rng = np.random.default_rng(T)
+    cids = rng.integers(0, V, T).astype(np.int32)
+    cu = np.array([0, T // 2, T], dtype=np.int32)
+    mask = (rng.random(T) > 0.1).astype(np.uint8)
+    K, N = cols * 256, (hc + 1) * dim
+    host_layers, dev_layers = [], []
+    for l in range(2):
+        table, scales = workloads.fp8_table(4, l, R)
+        wkv = oracle.bf16_bits(oracle.bf16_round(0.02 * rng.standard_normal((N, K))))
+        qw = oracle.bf16_bits(oracle.bf16_round(1 + 0.1 * rng.standard_normal((hc, dim))))
+        kw = oracle.bf16_bits(oracle.bf16_round(1 + 0.1 * rng.standard_normal((hc, dim))))
+        host_layers.append(dict(fmt="fp8", table=table, scales=scales, wkv=wkv, q_weight=qw,
+                                k_weight=kw, wkv_mx=oracle.quantize_mxfp8(wkv)))
+        mx = _gpu_mx_weight(eg, tensor(wkv, "cuda"), N, K)
+        dev_layers.append(eg.Layer(eg.ENGRAM_ROWS_FP8_E4M3_E8M0, tensor(table, "cuda"),
+                                   tensor(scales, "cuda"), None, tensor(qw, "cuda"),
+                                   tensor(kw, "cuda"), hc, dim, cols, wkv_mx=mx[0],
+                                   wkv_mx_scales=mx[1]))
+    h0 = rng.standard_normal((T, hc, dim)).astype(np.float32)
+    eps, clamp, dot_scale = 1e-6, 1e-6, 1 / np.sqrt(dim)
+    params = eg.HashParams.from_dict(hp)
+    tokens = eg.Tokens(tensor(cids, "cuda"), tensor(cu, "cuda"), token_mask=tensor(mask, "cuda"))
+    h = tensor(h0, "cuda")
+    ws = torch.empty(eg.engram_workspace_bytes(T, 2, cols, hc, dim), dtype=torch.uint8,
+                     device="cuda")
+    eg.engram_forward(params, tokens, dev_layers, h, hc, dim, eps, clamp, dot_scale, ws)
+    got = h.cpu().numpy()
+    want = oracle.forward(h0, cids, cu, hp, host_layers, eps, clamp, dot_scale, token_mask=mask)
+    err = np.abs(got - want) / np.maximum(1.0, np.abs(want))
+    assert err.max() <= 1e-2, err.max()
+    off = np.flatnonzero(mask == 0)
+    assert np.array_equal(got[off].view(np.uint32), h0[off].view(np.uint32))
