@@ -1,6 +1,6 @@
 """Benchmark: Engram forward tokens/s on one MI355X, with per-stage roofline fractions.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline] [--mxfp8]
 
 A step is one pass of the whole hot path over the batch: the hash for every
 layer, then per layer the row gather, the projection and the gate.  The
@@ -10,7 +10,10 @@ records HIP events between them, so each kernel's average duration comes from
 the timed run itself.  For Q2_K tables that is engram_project_q2k (row gather
 and projection fused into one kernel); the two-kernel path it replaces
 (engram_rows, engram_project) is timed after the steps for comparison, as is
-engram_forward itself.
+engram_forward itself.  With --mxfp8 (FP8 tables only) the layers carry an
+MXFP8 copy of wkv, made once before timing, and the step runs
+engram_project_mxfp8 (raw FP8 rows on the block-scaled matrix cores) in place
+of rows -> projection.
 
 Prints ONE JSON line: the headline metric, plus `roofline` for the dominant
 kernel (the bf16 MFMA projection), `stages` for every kernel, and
@@ -33,6 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "Engram forward tokens/s at T=8192 (1 GPU); % HBM roofline gather+gate, % MFMA GEMM"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published (no sparsity)
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published (no sparsity)
 Q2K_FUSED_MAX_BYTES = 2147483504   # engram.h: ENGRAM_Q2K_FUSED_MAX_BYTES
 SKINNY_MAX_TOKENS = 128            # engram_project streams wkv at or below this many tokens
 CPU_SAMPLE_TOKENS = 8192       # whole sequences of the workload, up to this many tokens
@@ -84,8 +88,12 @@ def algorithmic(spec, token_mask) -> dict:
     }
 
 
-def cpu_baseline(wl) -> dict:
-    """The oracle, as it stands, on the workload's first whole sequences (<= CPU_SAMPLE_TOKENS)."""
+def cpu_baseline(wl, mx: bool = False) -> dict:
+    """The oracle, as it stands, on the workload's first whole sequences (<= CPU_SAMPLE_TOKENS).
+
+    With mx, the oracle's layers carry its own MXFP8 copy of wkv, made before
+    the clock starts (as the GPU's is).
+    """
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -98,16 +106,21 @@ def cpu_baseline(wl) -> dict:
     n = cu[n_seq]
     sl = slice(0, n)
     opt = lambda a: None if a is None else a[sl]
+    layers = [l.as_dict() for l in wl.layers]
+    if mx:
+        for d in layers:
+            d["wkv_mx"] = oracle.quantize_mxfp8(d["wkv"])
     t0 = time.perf_counter()
     oracle.forward(wl.h[sl], wl.cids[sl], np.array(cu[:n_seq + 1], dtype=np.int32),
-                   wl.hash_params, [l.as_dict() for l in wl.layers], s.eps, s.clamp,
+                   wl.hash_params, layers, s.eps, s.clamp,
                    s.dot_scale, doc_ids=opt(wl.doc_ids), token_mask=opt(wl.token_mask),
                    lookback=None if wl.lookback is None else wl.lookback[:n_seq],
                    lookback_live=None if wl.lookback_live is None else wl.lookback_live[:n_seq])
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {n} tokens ({n_seq} sequences) of the {s.name} workload, whole "
-                      f"forward (hash, rows, projection, gate) in float64 numpy; {dt:.1f} s"}
+                      f"forward (hash, rows, {'MXFP8 ' if mx else ''}projection, gate) in "
+                      f"float64 numpy; {dt:.1f} s"}
 
 
 def main() -> int:
@@ -120,6 +133,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mxfp8", action="store_true",
+                    help="FP8 tables: project the raw rows in MXFP8 against an MXFP8 copy "
+                         "of wkv (engram_project_mxfp8)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (for scaling "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -156,8 +172,20 @@ def main() -> int:
     params = eg.HashParams.from_dict(wl.hash_params)
     tokens = eg.Tokens(dw.cids, dw.cu_seqlens, dw.doc_ids, dw.token_mask, dw.lookback,
                        dw.lookback_live)
+    mx = args.mxfp8
+    if mx and fmt != eg.ENGRAM_ROWS_FP8_E4M3_E8M0:
+        print("--mxfp8 needs a workload with FP8 tables (config 4)", file=sys.stderr)
+        return 2
+    wmx = []
+    if mx:
+        # Weight prep, once per weight, outside the timed region.
+        for l in dw.layers:
+            codes = torch.empty((s.N, s.K), dtype=torch.uint8, device="cuda")
+            scl = torch.empty((s.N, s.K // 32), dtype=torch.uint8, device="cuda")
+            eg.engram_quantize_mxfp8(l.wkv, s.N, s.K, codes, scl)
+            wmx.append((codes, scl))
     layers = [eg.Layer(fmt, l.table, l.scales, l.wkv, l.q_weight, l.k_weight, s.hc, s.dim,
-                       s.cols) for l in dw.layers]
+                       s.cols, *(wmx[i] if mx else ())) for i, l in enumerate(dw.layers)]
     h = dw.h
     ids = torch.empty((s.T, L, s.cols), dtype=torch.int32, device="cuda")
     rows = torch.empty((s.T, s.K), dtype=torch.int16, device="cuda")
@@ -184,6 +212,11 @@ def main() -> int:
         eg.engram_project_q2k(dl.table, num_rows[l], layer_ids(l), L * s.cols, s.cols, dl.wkv,
                               kv, s.T, s.N, None, stream)
 
+    def mx_call(l):
+        dl = dw.layers[l]
+        eg.engram_project_mxfp8(dl.table, dl.scales, num_rows[l], layer_ids(l), L * s.cols,
+                                s.cols, wmx[l][0], wmx[l][1], kv, s.T, s.N, None, stream)
+
     def gate_call(l):
         dl = dw.layers[l]
         eg.engram_gate(h, kv, dl.q_weight, dl.k_weight, dw.token_mask, s.T, s.hc, s.dim, s.eps,
@@ -192,7 +225,9 @@ def main() -> int:
     # One step = the launches engram_forward makes, in its order.
     plan = [("hash", lambda: eg.engram_hash(params, tokens, ids, stream))]
     for l in range(L):
-        if fused:
+        if mx:
+            plan.append(("rows_project", lambda l=l: mx_call(l)))
+        elif fused:
             plan.append(("rows_project", lambda l=l: fused_call(l)))
         else:
             plan += [("rows", lambda l=l: rows_call(l)), ("project", lambda l=l: project_call(l))]
@@ -239,7 +274,7 @@ def main() -> int:
         return e0.elapsed_time(e1) / n
 
     n_ref = max(3, args.steps // 2)
-    if fused:
+    if fused or mx:
         # The two-kernel path the fused kernel replaces, for comparison (the
         # row gather is also a C-ABI entry point of its own).
         per_launch_ms["rows"] = time_alone(lambda: rows_call(0), n_ref)
@@ -264,17 +299,22 @@ def main() -> int:
 
     def prof(name):
         # Summaries exist for the prefill (T=8192) and decode (T=64) workloads.
-        suffix = {2: "_prefill_T8192.md", 1: "_decode_T64.md"}.get(args.config)
+        suffix = {2: "_prefill_T8192.md", 1: "_decode_T64.md",
+                  4: "_fp8_T16384.md"}.get(args.config)
         return profiled_traffic(name + suffix) if suffix else None
 
-    if fused:
+    if mx:
+        dom_name, dom_kernel = "rows_project", "gemm_mx_kernel (engram_project_mxfp8)"
+        dom_prof = "gemm_mx"
+    elif fused:
         dom_name, dom_kernel = "rows_project", "gemm_q2k_kernel (engram_project_q2k)"
         dom_prof = "gemm_q2k"
     else:
         dom_name, dom_kernel = "project", "gemm_nt_kernel (engram_project)"
         dom_prof = "gemm_nt"
     dom_tf = tflops(per_launch_ms[dom_name])
-    skinny = s.T <= SKINNY_MAX_TOKENS
+    dom_peak = FP8_PEAK_TFLOPS if mx else BF16_PEAK_TFLOPS
+    skinny = s.T <= SKINNY_MAX_TOKENS and not mx
     if skinny:
         # Few tokens: the projection streams wkv once and is bound by HBM.
         dom_kernel = "gemm_skinny_kernel (engram_project, T <= 128)"
@@ -285,8 +325,8 @@ def main() -> int:
                     "traffic": prof("gemm_skinny"),
                     "bytes_per_launch": dom_bytes}
     else:
-        roofline = {"bound": "mfma", "achieved": round(dom_tf, 1), "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(dom_tf / BF16_PEAK_TFLOPS, 4),
+        roofline = {"bound": "mfma", "achieved": round(dom_tf, 1), "peak": dom_peak,
+                    "unit": "TFLOP/s", "frac": round(dom_tf / dom_peak, 4),
                     "traffic": prof(dom_prof)}
     roofline.update({"kernel": dom_kernel, "per_launch_ms": round(per_launch_ms[dom_name], 4)})
     stages = {
@@ -294,10 +334,10 @@ def main() -> int:
                  "hbm_gbs": round(gbs(alg["hash"], per_launch_ms["hash"]), 1),
                  "traffic": prof("hash")},
     }
-    if fused:
+    if fused or mx:
         stages["rows_project"] = {
             "ms": round(per_launch_ms["rows_project"], 4), "bound": "mfma",
-            "achieved_tflops": round(dom_tf, 1), "frac": round(dom_tf / BF16_PEAK_TFLOPS, 4),
+            "achieved_tflops": round(dom_tf, 1), "frac": round(dom_tf / dom_peak, 4),
             "traffic": prof(dom_prof)}
     rows_gbs = gbs(alg["rows"], per_launch_ms["rows"])
     proj_tf = tflops(per_launch_ms["project"])
@@ -305,14 +345,14 @@ def main() -> int:
                       "achieved_gbs": round(rows_gbs, 1),
                       "frac": round(rows_gbs / HBM_PEAK_GBS, 4),
                       "bytes_per_launch": alg["rows"],
-                      "traffic": prof("rows_q2k"),
-                      "in_step": not fused}
+                      "traffic": prof("rows_q2k" if s.fmt == "q2k" else "rows_fp8"),
+                      "in_step": not (fused or mx)}
     stages["project"] = {"ms": round(per_launch_ms["project"], 4),
                          "bound": "hbm" if skinny else "mfma",
                          "achieved_tflops": round(proj_tf, 1),
                          "frac": round(proj_tf / BF16_PEAK_TFLOPS, 4),
                          "traffic": prof("gemm_skinny" if skinny else "gemm_nt"),
-                         "in_step": not fused}
+                         "in_step": not (fused or mx)}
     gate_gbs = gbs(alg["gate"], per_launch_ms["gate"])
     stages["gate"] = {"ms": round(per_launch_ms["gate"], 4), "bound": "hbm",
                       "achieved_gbs": round(gate_gbs, 1),
@@ -335,19 +375,20 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp8" if mx else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{s.name}: T={s.T} ({len(s.seq_lens)}x{s.seq_lens[0]}), "
                                f"{L} layer(s), {s.cols} cols, {s.fmt} table "
                                f"{s.num_rows} rows, dim={s.dim}, hc={s.hc}, "
                                f"{s.id_dist} ids",
-                   "T": s.T, "K": s.K, "N": s.N, "row_format": s.fmt},
+                   "T": s.T, "K": s.K, "N": s.N, "row_format": s.fmt,
+                   "projection": "mxfp8" if mx else "bf16"},
         "roofline": roofline,
         "stages": stages,
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(wl)
+        result["cpu_baseline"] = cpu_baseline(wl, mx)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -148,19 +148,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
     as_src = ok ? tscales + int64_t(idn[kSegs]) * (ENGRAM_HEAD_DIM / 32) : kZeroRow;
   };
   // Stage kt (values 128 kt .. 128 kt + 127: half kt % 2 of column kt / 2)
-  // into LDS buffer `buf`.  `half` is kt % 2 as a constant, since it is the
-  // instruction's immediate offset into the row; a_src/as_src must hold
-  // column kt / 2 (clamped to the last column).
+  // into LDS buffer `buf`; a_src/as_src must hold column kt / 2 (clamped to
+  // the last column).  The half's offset goes into the address itself: the
+  // immediate offset of an LDS-DMA load moves its LDS destination as well.
   auto dma = [&](int buf, int kt, const int half) {
     uint8_t *st = smem + buf * kStageBytes;
     const int kb = min(kt, nk - 1);
 #pragma unroll
     for (int i = 0; i < kSegs; ++i) {
       const int seg = wave * kSegs + i;
-      if (half == 0)
-        __builtin_amdgcn_global_load_lds(a_src[i], lds_ptr(st + seg * 1024), 16, 0, 0);
-      else
-        __builtin_amdgcn_global_load_lds(a_src[i], lds_ptr(st + seg * 1024), 16, kBK, 0);
+      __builtin_amdgcn_global_load_lds(a_src[i] + half * kBK, lds_ptr(st + seg * 1024), 16, 0,
+                                       0);
     }
 #pragma unroll
     for (int i = 0; i < kSegs; ++i) {
@@ -169,10 +167,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
                                                ((i & 1) ? voff_odd : voff_even) + seg * 8 * K,
                                                kb * kBK, 0, 0);
     }
-    if (half == 0)
-      __builtin_amdgcn_global_load_lds(as_src, lds_ptr(st + 2 * kTileBytes + wave * 256), 4, 0, 0);
-    else
-      __builtin_amdgcn_global_load_lds(as_src, lds_ptr(st + 2 * kTileBytes + wave * 256), 4, 4, 0);
+    __builtin_amdgcn_global_load_lds(as_src + half * 4,
+                                     lds_ptr(st + 2 * kTileBytes + wave * 256), 4, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rbs, lds_ptr(st + 2 * kTileBytes + kScaleBytes + wave * 256), 4, voff_bs, kb * 4, 0, 0);
   };
