@@ -28,6 +28,8 @@
 // the one of MX block g (k 32 g .. 32 g + 31).  A lane keeps its row's four
 // scale bytes of a stage in one dword shifted right by 8 g, so byte 0 is the
 // block of sub-step 0 and byte 2 that of sub-step 1, picked by op_sel.
+#include <utility>
+
 #include "gemm_common.hpp"
 
 namespace engram {
@@ -56,20 +58,23 @@ __device__ __forceinline__ __attribute__((address_space(3))) void *lds_ptr(T *p)
   return (__attribute__((address_space(3))) void *)(p);
 }
 
-// Scheduling of one row block: 4 MFMAs with kReads LDS reads spread between
-// them, reads first; the fence keeps the next block's work out of it.
+// Scheduling of one sub-step: its 16 MFMAs with kReads LDS reads spread over
+// the first 12 of them (the reads feed the next sub-step, so the last MFMAs
+// cover their latency); the fence keeps later work out of the group.
+template <int kReads, int kPer, int R>
+__device__ __forceinline__ void sched_one() {
+  constexpr int lo = R * kPer < kReads ? R * kPer : kReads;
+  constexpr int hi = (R + 1) * kPer < kReads ? (R + 1) * kPer : kReads;
+  if constexpr (hi > lo) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, hi - lo, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+}
+template <int kReads, int kPer, int... R>
+__device__ __forceinline__ void sched_each(std::integer_sequence<int, R...>) {
+  (sched_one<kReads, kPer, R>(), ...);
+}
 template <int kReads>
-__device__ __forceinline__ void sched_row() {
-  constexpr int n0 = kReads / 4, n1 = kReads * 2 / 4 - n0, n2 = kReads * 3 / 4 - n0 - n1,
-                n3 = kReads - n0 - n1 - n2;
-  if constexpr (n0 > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, n0, 0);
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-  if constexpr (n1 > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, n1, 0);
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-  if constexpr (n2 > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, n2, 0);
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-  if constexpr (n3 > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, n3, 0);
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+__device__ __forceinline__ void sched_substep() {
+  sched_each<kReads, (kReads + 11) / 12>(std::make_integer_sequence<int, 16>{});
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -179,16 +184,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  // Fragments: the wave's 4 B fragments of the current and of the next
-  // sub-step, and a ring of 2 A fragments (row block i multiplies while row
-  // block i + 1 is read).  Fragment f of sub-step s is chunks 4 s + g and
-  // 4 s + 2 + g of row f * 32 + frow of the wave's operand rows; the swizzle
-  // key of those rows is that of frow, so a lane's chunk offsets are the
-  // same for all four fragments.
+  // Fragments: a sub-step's 4 A and 4 B fragments (8 VGPRs each), double
+  // buffered: those of the next sub-step are read while this one multiplies.
+  // Fragment f of sub-step s is chunks 4 s + g and 4 s + 2 + g of row
+  // f * 32 + frow of the wave's operand rows; the swizzle key of those rows is
+  // that of frow, so a lane's chunk offsets are the same for all four.
   const int frow = lane & 31, fhalf = lane >> 5;
   const int fkey = swz_key<64>(frow);
   const int a_frag = (wm * 128 + frow) * kBK, b_frag = kTileBytes + (wn * 128 + frow) * kBK;
-  i32x8 fa[2], fb[2][4];
+  i32x8 fa[2][4], fb[2][4];
   uint32_t sca[2][4], scb[2][4];
   auto read_frag = [&](int buf, int base, int f, const int s) {
     const uint8_t *p = smem + buf * kStageBytes + base + f * 32 * kBK;
@@ -204,73 +208,59 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) scb[set][j] = ss[BM + wn * 128 + j * 32 + frow] >> (8 * fhalf);
   };
-  // Row block i of sub-step s: A fragment fa[fs] against the 4 B fragments
-  // fb[bs], scales of set `set` (op_sel 0 picks sub-step 0's block, 2 sub-step 1's).
-  auto mfma_row = [&](const int i, const int fs, const int bs, const int set, const int s) {
+  auto load_frags = [&](int buf, const int s, const int slot) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (s == 0)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            fa[fs], fb[bs][j], acc[i][j], 0, 0, 0, sca[set][i], 0, scb[set][j]);
-      else
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            fa[fs], fb[bs][j], acc[i][j], 0, 0, 2, sca[set][i], 2, scb[set][j]);
+    for (int f = 0; f < 4; ++f) {
+      fa[slot][f] = read_frag(buf, a_frag, f, s);
+      fb[slot][f] = read_frag(buf, b_frag, f, s);
     }
   };
-  // Iteration kt multiplies the stage in buffer j = kt % 2; on entry fa[0]
-  // and fb[0] hold its sub-step 0 fragments and sca/scb[j] its scales.
+  // Sub-step s of a stage: 4 x 4 MFMAs of fragment slot `slot` with the
+  // scales of set `set` (op_sel 0 picks sub-step 0's block, 2 sub-step 1's).
+  auto mfma_block = [&](const int slot, const int set, const int s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (s == 0)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0, sca[set][i], 0, scb[set][j]);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 2, sca[set][i], 2, scb[set][j]);
+      }
+  };
+
+  // Iteration kt multiplies the stage in buffer j = kt % 2; on entry fragment
+  // slot 0 holds its sub-step 0 and sca/scb[j] its scales.
   //  - at even kt, the ids of column kt / 2 + 2 are requested (9 loads);
-  //  - sub-step 0 reads the next A fragments and sub-step 1's B fragments;
-  //  - sub-step 1 reads its own A fragments; after row block 2 (the last
-  //    read of buffer j), the barrier waits for stage kt + 1's DMA (issued
-  //    one iteration ago; at even kt only the 9 younger id loads may stay in
-  //    flight) and for every wave's reads of buffer j;
+  //  - sub-step 1's fragments are read while sub-step 0 multiplies: after
+  //    that, buffer j is no longer read;
+  //  - the barrier waits for stage kt + 1's DMA (issued one iteration ago;
+  //    at even kt only the 9 younger id loads may stay in flight) and for
+  //    every wave's reads of buffer j;
   //  - buffer j then takes stage kt + 2 (column kt / 2 + 1, half j), and at
   //    odd kt the addresses of column kt / 2 + 2 are resolved for the next
   //    two DMAs;
-  //  - stage kt + 1's sub-step 0 fragments and scales are read while the
-  //    last row block of stage kt multiplies.
+  //  - stage kt + 1's sub-step 0 fragments and scales are read while
+  //    sub-step 1 of stage kt multiplies.
   auto iteration = [&](int kt, const int j) {
     const int b = j;
     __builtin_amdgcn_sched_barrier(0);
     if (j == 0) load_ids(kt / 2 + 2);
     __builtin_amdgcn_sched_barrier(0);
-    fa[1] = read_frag(b, a_frag, 1, 0);
-    fb[1][0] = read_frag(b, b_frag, 0, 1);
-    mfma_row(0, 0, 0, j, 0);
-    sched_row<4>();
-    fa[0] = read_frag(b, a_frag, 2, 0);
-    fb[1][1] = read_frag(b, b_frag, 1, 1);
-    mfma_row(1, 1, 0, j, 0);
-    sched_row<4>();
-    fa[1] = read_frag(b, a_frag, 3, 0);
-    fb[1][2] = read_frag(b, b_frag, 2, 1);
-    mfma_row(2, 0, 0, j, 0);
-    sched_row<4>();
-    fa[0] = read_frag(b, a_frag, 0, 1);
-    fb[1][3] = read_frag(b, b_frag, 3, 1);
-    mfma_row(3, 1, 0, j, 0);
-    sched_row<4>();
-    fa[1] = read_frag(b, a_frag, 1, 1);
-    mfma_row(0, 0, 1, j, 1);
-    sched_row<2>();
-    fa[0] = read_frag(b, a_frag, 2, 1);
-    mfma_row(1, 1, 1, j, 1);
-    sched_row<2>();
-    fa[1] = read_frag(b, a_frag, 3, 1);
-    mfma_row(2, 0, 1, j, 1);
-    sched_row<2>();
+    load_frags(b, 1, 1);
+    mfma_block(0, j, 0);
+    sched_substep<16>();
     if (j == 0) stage_barrier<waitcnt(kIdsPerLane, 0)>();
     else stage_barrier<waitcnt(0, 0)>();
     dma(b, kt + 2, j);
     if (j == 1) resolve();
     __builtin_amdgcn_sched_barrier(0);
-    fa[0] = read_frag(b ^ 1, a_frag, 0, 0);
-#pragma unroll
-    for (int f = 0; f < 4; ++f) fb[0][f] = read_frag(b ^ 1, b_frag, f, 0);
+    load_frags(b ^ 1, 0, 0);
     load_scales(b ^ 1, j ^ 1);
-    mfma_row(3, 1, 1, j, 1);
-    sched_row<18>();
+    mfma_block(1, j, 1);
+    sched_substep<24>();
   };
 
   // Prologue: stages 0 and 1 (column 0) in flight, then column 1's addresses.
@@ -281,9 +271,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
   load_ids(1);
   resolve();
   stage_barrier<waitcnt(0, 0)>();
-  fa[0] = read_frag(0, a_frag, 0, 0);
-#pragma unroll
-  for (int f = 0; f < 4; ++f) fb[0][f] = read_frag(0, b_frag, f, 0);
+  load_frags(0, 0, 0);
   load_scales(0, 0);
 
   for (int kt = 0; kt < nk; kt += 2) {               // nk = 2 * cols is even
