@@ -284,6 +284,15 @@ def main() -> int:
     forward_ms = time_alone(lambda: eg.engram_forward(params, tokens, layers, h, s.hc, s.dim,
                                                       s.eps, s.clamp, s.dot_scale, ws, None,
                                                       stream), n_ref)
+    graph_ms = None
+    if s.T <= SKINNY_MAX_TOKENS:
+        # Decode: the same forward captured once in a HIP graph and replayed
+        # (launch overhead is a visible share of a ~0.1 ms step).
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            eg.engram_forward(params, tokens, layers, h, s.hc, s.dim, s.eps, s.clamp,
+                              s.dot_scale, ws, None)
+        graph_ms = time_alone(graph.replay, n_ref)
 
     alg = algorithmic(s, wl.token_mask)
 
@@ -363,6 +372,8 @@ def main() -> int:
                                   "frac": round(gg_gbs / HBM_PEAK_GBS, 4),
                                   "kernels": "engram_rows + engram_gate"}
     stages["engram_forward_ms"] = round(forward_ms, 4)
+    if graph_ms is not None:
+        stages["engram_forward_graph_replay_ms"] = round(graph_ms, 4)
 
     result = {
         "metric": METRIC,

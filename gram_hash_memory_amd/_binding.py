@@ -28,7 +28,7 @@ ENGRAM_OK, ENGRAM_ERR_ARG, ENGRAM_ERR_UNSUPPORTED, ENGRAM_ERR_HIP = 0, 1, 2, 3
 ENGRAM_ROWS_Q2K, ENGRAM_ROWS_FP8_E4M3_E8M0 = 0, 1
 HEAD_DIM, Q2K_ROW_BYTES, FP8_ROW_BYTES, FP8_SCALE_BYTES = 256, 84, 256, 8
 
-EXPORTS = ("engram_hash", "engram_rows", "engram_project", "engram_project_q2k",
+EXPORTS = ("engram_hash", "engram_history_update", "engram_rows", "engram_project", "engram_project_q2k",
            "engram_quantize_mxfp8", "engram_project_mxfp8", "engram_gate",
            "engram_workspace_bytes", "engram_forward", "engram_last_error")
 
@@ -57,6 +57,7 @@ class _Layer(ctypes.Structure):
 
 _P = ctypes.POINTER
 _lib.engram_hash.argtypes = [_P(_HashParams), _P(_Tokens), c_void_p, c_void_p]
+_lib.engram_history_update.argtypes = [_P(_Tokens), c_int32, c_void_p, c_void_p, c_void_p]
 _lib.engram_rows.argtypes = [c_int, c_void_p, c_void_p, c_int64, c_void_p, c_int64, c_int32,
                              c_int32, c_void_p, c_void_p, c_void_p]
 _lib.engram_project.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
@@ -75,7 +76,7 @@ _lib.engram_forward.argtypes = [_P(_HashParams), _P(_Tokens), _P(_Layer), c_void
                                 c_int32, c_float, c_float, c_float, c_void_p, c_size_t,
                                 c_void_p, c_void_p]
 _lib.engram_last_error.restype = c_char_p
-for _name in ("engram_hash", "engram_rows", "engram_project", "engram_project_q2k",
+for _name in ("engram_hash", "engram_history_update", "engram_rows", "engram_project", "engram_project_q2k",
               "engram_quantize_mxfp8", "engram_project_mxfp8", "engram_gate", "engram_forward"):
     getattr(_lib, _name).restype = c_int
 
@@ -166,6 +167,16 @@ def engram_hash(params: HashParams, tokens: Tokens, ids: torch.Tensor, stream=No
     """Stage 1: ids int32 [T, n_layers, cols] from the token batch."""
     p = _dptr(ids, torch.int32, tokens.T * params.n_layers * params.cols, "ids")
     _check(_lib.engram_hash(ctypes.byref(params.c), ctypes.byref(tokens.c), p, _stream(stream)))
+
+
+def engram_history_update(tokens: Tokens, history, history_live, stream=None) -> None:
+    """Update the lookback store (int32 and uint8 [n_seqs, depth]) in place after a batch."""
+    depth = int(history.shape[1]) if history.dim() == 2 else 0
+    n = tokens.n_seqs * depth
+    _check(_lib.engram_history_update(ctypes.byref(tokens.c), depth,
+                                      _dptr(history, torch.int32, n, "history"),
+                                      _dptr(history_live, torch.uint8, n, "history_live"),
+                                      _stream(stream)))
 
 
 def engram_rows(fmt: int, table, scales, num_rows: int, ids, ids_token_stride: int, cols: int,

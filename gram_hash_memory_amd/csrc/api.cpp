@@ -173,6 +173,21 @@ engram_status engram_hash(const engram_hash_params *params, const engram_tokens 
   return hip_status(engram::launch_hash(tab, *tokens, ids, stream), "engram_hash launch");
 }
 
+engram_status engram_history_update(const engram_tokens *tokens, int32_t depth,
+                                    int32_t *history, uint8_t *history_live,
+                                    hipStream_t stream) {
+  REQUIRE(depth >= 1 && depth <= ENGRAM_MAX_NGRAM - 1, "depth=%d outside 1..%d", depth,
+          ENGRAM_MAX_NGRAM - 1);
+  engram_status st = check_tokens(tokens, ENGRAM_MAX_NGRAM);
+  if (st != ENGRAM_OK) return st;
+  if (tokens->T == 0) return ENGRAM_OK;              // every chunk is empty
+  REQUIRE(history && history_live, "history or history_live is NULL");
+  REQUIRE(aligned(history, 4), "history misaligned");
+  return hip_status(engram::launch_history_update(*tokens, depth, history, history_live,
+                                                  stream),
+                    "engram_history_update launch");
+}
+
 engram_status engram_rows(engram_row_format fmt, const uint8_t *table, const uint8_t *scales,
                           int64_t num_rows, const int32_t *ids, int64_t ids_token_stride,
                           int32_t cols, int32_t T, uint16_t *rows, int32_t *bad_ids,

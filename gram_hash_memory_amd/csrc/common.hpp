@@ -51,6 +51,9 @@ struct HashTables {
 hipError_t launch_hash(const HashTables &tab, const engram_tokens &tok, int32_t *ids,
                        hipStream_t stream);
 
+hipError_t launch_history_update(const engram_tokens &tok, int32_t depth, int32_t *history,
+                                 uint8_t *history_live, hipStream_t stream);
+
 hipError_t launch_rows(engram_row_format fmt, const uint8_t *table, const uint8_t *scales,
                        int64_t num_rows, const int32_t *ids, int64_t ids_token_stride,
                        int32_t cols, int32_t T, uint16_t *rows, int32_t *bad_ids,

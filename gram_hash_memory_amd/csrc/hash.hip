@@ -105,7 +105,68 @@ __global__ __launch_bounds__(kThreads) void hash_kernel(
   }
 }
 
+// The lookback store after a batch, one thread per sequence: entry j (oldest
+// first) becomes the position that precedes the sequence's next chunk by
+// depth - j -- a position of this chunk, or an older entry of the store.  The
+// thread reads all of its sequence's old entries before it writes any, so
+// the update can run in place.
+__global__ __launch_bounds__(kThreads) void history_kernel(
+    int32_t n_seqs, int32_t depth, const int32_t *__restrict__ cids,
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ doc_ids,
+    const uint8_t *__restrict__ mask, int32_t *hist, uint8_t *live) {
+  const int32_t s = int32_t(blockIdx.x) * kThreads + int32_t(threadIdx.x);
+  if (s >= n_seqs) return;
+  const int32_t start = cu[s], end = cu[s + 1];
+  if (end <= start) return;                       // an empty chunk changes nothing
+  int32_t *h = hist + int64_t(s) * depth;
+  uint8_t *l = live + int64_t(s) * depth;
+  int32_t old_tok[ENGRAM_MAX_NGRAM];
+  bool old_live[ENGRAM_MAX_NGRAM];
+#pragma unroll
+  for (int j = 0; j < ENGRAM_MAX_NGRAM; ++j) {
+    if (j < depth) {
+      old_tok[j] = h[j];
+      old_live[j] = l[j] != 0;
+    }
+  }
+  // The next chunk continues the document of this chunk's last position; a
+  // document change inside the chunk, or a padding document, ends the older
+  // entries' usefulness.
+  const int32_t last_doc = doc_ids ? doc_ids[end - 1] : 1;
+  const bool old_ok = !doc_ids || (last_doc != 0 && doc_ids[start] == last_doc);
+#pragma unroll
+  for (int j = 0; j < ENGRAM_MAX_NGRAM; ++j) {
+    if (j >= depth) break;
+    const int32_t p = end - depth + j;
+    int32_t tok = 0;
+    bool ok = false;
+    if (p >= start) {
+      tok = cids[p];
+      ok = (!mask || mask[p] != 0) && (!doc_ids || (last_doc != 0 && doc_ids[p] == last_doc));
+    } else {
+      const int32_t jo = depth - (start - p);
+#pragma unroll
+      for (int k = 0; k < ENGRAM_MAX_NGRAM; ++k)
+        if (k == jo) {
+          tok = old_tok[k];
+          ok = old_live[k] && old_ok;
+        }
+    }
+    h[j] = tok;
+    l[j] = ok ? 1 : 0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_history_update(const engram_tokens &tok, int32_t depth, int32_t *history,
+                                 uint8_t *history_live, hipStream_t stream) {
+  const int64_t blocks = (int64_t(tok.n_seqs) + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(history_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                     tok.n_seqs, depth, tok.cids, tok.cu_seqlens, tok.doc_ids, tok.token_mask,
+                     history, history_live);
+  return hipGetLastError();
+}
 
 hipError_t launch_hash(const HashTables &tab, const engram_tokens &tok, int32_t *ids,
                        hipStream_t stream) {

@@ -163,6 +163,30 @@ typedef struct engram_layer {
 ENGRAM_API engram_status engram_hash(const engram_hash_params *params, const engram_tokens *tokens,
                           int32_t *ids, hipStream_t stream);
 
+/* Lookback store for streaming decode ([vLLM] module docstring and
+ * NgramHashState.forward: a decode step hashes against the ids just before
+ * its chunk).  history DEVICE int32 [n_seqs][depth] and history_live DEVICE
+ * [n_seqs][depth], oldest first, are updated IN PLACE to what the sequences'
+ * next chunks need as lookback (pass them as tokens->lookback /
+ * lookback_live of the next batch; start from all-zero history_live).  For
+ * sequence s with chunk [start, end), entry j becomes position
+ * p = end - depth + j:
+ *   p >= start: cids[p]; live unless token_mask[p] == 0, and, with doc_ids,
+ *     only if doc_ids[p] equals the document of position end - 1 and that
+ *     is not 0 (the next chunk continues that document);
+ *   p < start: the old entry depth - (start - p) (token 0, dead when that
+ *     index is negative); it keeps its liveness, except that with doc_ids
+ *     every older entry turns dead when doc_ids[start] differs from the
+ *     document of position end - 1 or that document is 0.
+ * An empty chunk leaves its sequence unchanged.  Uses tokens' T, n_seqs,
+ * cids, cu_seqlens, doc_ids and token_mask (its lookback fields are
+ * ignored: the store is the lookback).  Run it after the batch's hash on the
+ * same stream.  1 <= depth <= ENGRAM_MAX_NGRAM - 1.
+ */
+ENGRAM_API engram_status engram_history_update(const engram_tokens *tokens, int32_t depth,
+                                               int32_t *history, uint8_t *history_live,
+                                               hipStream_t stream);
+
 /* Stage 2 -- row gather + dequant to bf16 ([spark] overview stage 2,
  * ENGRAM_ROW_BYTES; [vLLM] _engram_lookup_kernel, bf16 mode).
  *   ids: DEVICE int32; row r of token t is ids[t * ids_token_stride + r],

@@ -27,7 +27,7 @@ neither the released model nor its files are available:
 from .layout import is_prime, next_unused_prime, engram_layout, hash_multipliers
 from .numerics import (bf16_round, bf16_bits, bf16_value, fp16_value,
                        e4m3fn_value, e8m0_scale)
-from .engram import (hash_ids, rows_q2k, rows_fp8, project, gate, forward,
+from .engram import (hash_ids, history_update, rows_q2k, rows_fp8, project, gate, forward,
                      Q2K_ROW_BYTES, FP8_ROW_BYTES, HEAD_DIM)
 from .mx import (e8m0_mx_scale, quantize_mxfp8, mx_values, rows_fp8_mx, project_mxfp8,
                  MX_BLOCK)
@@ -35,7 +35,7 @@ from .mx import (e8m0_mx_scale, quantize_mxfp8, mx_values, rows_fp8_mx, project_
 __all__ = [
     "is_prime", "next_unused_prime", "engram_layout", "hash_multipliers",
     "bf16_round", "bf16_bits", "bf16_value", "fp16_value", "e4m3fn_value",
-    "e8m0_scale", "hash_ids", "rows_q2k", "rows_fp8", "project", "gate",
+    "e8m0_scale", "hash_ids", "history_update", "rows_q2k", "rows_fp8", "project", "gate",
     "forward", "Q2K_ROW_BYTES", "FP8_ROW_BYTES", "HEAD_DIM", "e8m0_mx_scale",
     "quantize_mxfp8", "mx_values", "rows_fp8_mx", "project_mxfp8", "MX_BLOCK",
 ]

@@ -123,6 +123,54 @@ def hash_ids(cids, cu_seqlens, multipliers, primes, offsets, max_ngram, n_heads,
     return out.astype(np.int32)
 
 
+def history_update(history, history_live, cids, cu_seqlens, doc_ids=None, token_mask=None):
+    """The lookback store after a batch: (history, live), both [n_seqs, depth].
+
+    [vLLM] module docstring and NgramHashState.forward: a decode step hashes
+    its tokens against the ids just before its chunk (the lookback).  This
+    defines the store a streaming caller keeps so that step i + 1's lookback
+    is what step i leaves behind (reading A25).  Entry j of sequence s (oldest
+    first) is position p = end - depth + j, end = cu_seqlens[s + 1], the
+    position that precedes the sequence's next chunk by depth - j:
+      * inside the chunk (p >= start): its token; live unless masked, and,
+        with doc_ids, only if its document is the chunk's last position's
+        and not padding (the next chunk continues that document);
+      * before the chunk: the old entry start - p positions before the
+        chunk, if the old store reaches that far (else token 0, dead); it
+        keeps its liveness, except that with doc_ids a chunk whose first and
+        last documents differ, or whose last document is padding, leaves
+        every older entry dead.
+    An empty chunk leaves the sequence's entries unchanged.
+    """
+    hist = np.array(history, dtype=np.int64, copy=True)
+    live = np.array(history_live, dtype=np.uint8, copy=True)
+    n_seqs, depth = hist.shape
+    new_h = hist.copy()
+    new_l = live.copy()
+    cu = [int(v) for v in np.asarray(cu_seqlens)]
+    for s in range(n_seqs):
+        start, end = cu[s], cu[s + 1]
+        if end == start:
+            continue
+        last_doc = None if doc_ids is None else int(doc_ids[end - 1])
+        old_ok = last_doc is None or (last_doc != 0 and int(doc_ids[start]) == last_doc)
+        for j in range(depth):
+            p = end - depth + j
+            if p >= start:
+                tok = int(cids[p])
+                ok = token_mask is None or bool(token_mask[p])
+                if last_doc is not None:
+                    ok = ok and last_doc != 0 and int(doc_ids[p]) == last_doc
+            else:
+                jo = depth - (start - p)
+                if jo < 0:
+                    tok, ok = 0, False
+                else:
+                    tok, ok = int(hist[s, jo]), bool(live[s, jo]) and old_ok
+            new_h[s, j], new_l[s, j] = tok, 1 if ok else 0
+    return new_h.astype(np.int32), new_l
+
+
 # --------------------------------------------------------------------------- rows
 
 def _q2k_dequant_blocks(blocks: np.ndarray) -> np.ndarray:

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_declares_the_five_calls_and_helpers():
     names = declared_functions()
-    for want in ("engram_hash", "engram_rows", "engram_project", "engram_project_q2k",
+    for want in ("engram_hash", "engram_history_update", "engram_rows", "engram_project", "engram_project_q2k",
                  "engram_quantize_mxfp8", "engram_project_mxfp8", "engram_gate",
                  "engram_forward", "engram_workspace_bytes", "engram_last_error"):
         assert want in names
@@ -105,6 +105,8 @@ def _raw(eg):
                                        ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_void_p, ctypes.c_void_p]
+    lib.engram_history_update.argtypes = [ctypes.POINTER(_TK), ctypes.c_int32, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p]
     lib.engram_quantize_mxfp8.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.engram_project_mxfp8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
@@ -219,6 +221,20 @@ class TestValidation:
         assert "exceeds" in lib.engram_last_error().decode()
         assert call(nrows=too_many - 1, T=0, table=None, ids=None, wkv=None,
                     kv=None) == eg.ENGRAM_OK
+
+    def test_history_update_rejects(self, eg):
+        lib = _raw(eg)
+        tk = _TK(16, 2, 0, FAKE, FAKE, None, None, None, None)
+        for depth, hist, live in ((0, FAKE, FAKE), (8, FAKE, FAKE), (3, None, FAKE),
+                                  (3, FAKE, None), (3, FAKE + 2, FAKE)):
+            assert lib.engram_history_update(ctypes.byref(tk), depth, hist, live,
+                                             None) == eg.ENGRAM_ERR_ARG, (depth, hist, live)
+        bad = _TK(16, 0, 0, FAKE, FAKE, None, None, None, None)
+        assert lib.engram_history_update(ctypes.byref(bad), 3, FAKE, FAKE,
+                                         None) == eg.ENGRAM_ERR_ARG
+        empty = _TK(0, 0, 0, None, None, None, None, None, None)
+        assert lib.engram_history_update(ctypes.byref(empty), 3, None, None,
+                                         None) == eg.ENGRAM_OK
 
     def test_quantize_mxfp8_rejects(self, eg):
         lib = _raw(eg)

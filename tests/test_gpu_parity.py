@@ -672,3 +672,132 @@ def test_forward_mx_small_full_compare(eg, T):
     assert err.max() <= 1e-2, err.max()
     off = np.flatnonzero(mask == 0)
     assert np.array_equal(got[off].view(np.uint32), h0[off].view(np.uint32))
+
+
+# ------------------------------------------------ streaming decode (lookback store)
+
+@pytest.mark.parametrize("with_docs", [False, True])
+def test_history_update_bit_exact(eg, with_docs):
+    # 300 sequences, chunks of 0..9 tokens, random masks (and documents): the
+    # store after the update equals the oracle's, in place.
+    rng = np.random.default_rng(17 + with_docs)
+    n_seqs, depth = 300, 3
+    lens = rng.integers(0, 10, n_seqs)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    cids = rng.integers(0, 1 << 20, T).astype(np.int32)
+    mask = (rng.random(T) > 0.2).astype(np.uint8)
+    docs = None
+    if with_docs:
+        docs = np.concatenate([np.sort(rng.integers(0, 3, n)) for n in lens]).astype(np.int32)
+    hist = rng.integers(0, 1 << 20, (n_seqs, depth)).astype(np.int32)
+    live = (rng.random((n_seqs, depth)) > 0.3).astype(np.uint8)
+    want_h, want_l = oracle.history_update(hist, live, cids, cu, doc_ids=docs, token_mask=mask)
+    tokens = eg.Tokens(tensor(cids, "cuda"), tensor(cu, "cuda"),
+                       None if docs is None else tensor(docs, "cuda"), tensor(mask, "cuda"))
+    h, l = tensor(hist, "cuda"), tensor(live, "cuda")
+    eg.engram_history_update(tokens, h, l)
+    assert np.array_equal(h.cpu().numpy(), want_h)
+    assert np.array_equal(l.cpu().numpy(), want_l)
+
+
+def _stream_batches(rng, seqs, masks, max_chunk):
+    """Split every sequence into random chunks; yield one batch per step."""
+    pos = [0] * len(seqs)
+    while any(p < len(s) for p, s in zip(pos, seqs)):
+        take = [min(int(rng.integers(0, max_chunk + 1)), len(s) - p) for p, s in zip(pos, seqs)]
+        cu = np.concatenate([[0], np.cumsum(take)]).astype(np.int32)
+        cids = np.concatenate([s[p:p + k] for s, p, k in zip(seqs, pos, take)]).astype(np.int32)
+        mask = np.concatenate([m[p:p + k] for m, p, k in zip(masks, pos, take)]).astype(np.uint8)
+        yield cu, cids, mask, take
+        pos = [p + k for p, k in zip(pos, take)]
+
+
+def test_streaming_decode_ids_equal_prefill(eg):
+    # Hash chunk by chunk on the GPU, each batch against the device-resident
+    # store the previous batches left: the ids equal the oracle's ids of each
+    # whole sequence hashed at once (the decode workload's tables and vocab).
+    wl = host(1)
+    hp = wl.hash_params
+    params = eg.HashParams.from_dict(hp)
+    L, cols, depth = len(wl.spec.layer_ids), wl.spec.cols, hp["max_ngram"] - 1
+    rng = np.random.default_rng(5)
+    n_seqs = 64
+    lens = rng.integers(5, 40, n_seqs)
+    seqs = [rng.integers(0, wl.spec.compressed_vocab, n).astype(np.int32) for n in lens]
+    masks = [(rng.random(n) > 0.1).astype(np.uint8) for n in lens]
+    hist = torch.zeros((n_seqs, depth), dtype=torch.int32, device="cuda")
+    live = torch.zeros((n_seqs, depth), dtype=torch.uint8, device="cuda")
+    got = [[] for _ in range(n_seqs)]
+    for cu, cids, mask, take in _stream_batches(rng, seqs, masks, 3):
+        tokens = eg.Tokens(tensor(cids, "cuda"), tensor(cu, "cuda"), None, tensor(mask, "cuda"),
+                           hist, live)
+        ids = torch.empty((len(cids), L, cols), dtype=torch.int32, device="cuda")
+        if len(cids):
+            eg.engram_hash(params, tokens, ids)
+        eg.engram_history_update(tokens, hist, live)
+        ids_np = ids.cpu().numpy()
+        for i in range(n_seqs):
+            got[i].append(ids_np[cu[i]:cu[i + 1]])
+    for i in range(n_seqs):
+        want = oracle.hash_ids(seqs[i], np.array([0, len(seqs[i])]), hp["multipliers"],
+                               hp["primes"], hp["offsets"], hp["max_ngram"], hp["n_heads"],
+                               hp["pad_id"], token_mask=masks[i])
+        assert np.array_equal(np.concatenate(got[i]), want), i
+
+
+def test_decode_graph_replay_matches_eager(eg):
+    # One decode step (engram_forward against the store, then the store
+    # update) captured once in a HIP graph and replayed for several steps,
+    # new tokens copied into the captured input buffer before each replay;
+    # eager steps on separate buffers, with synchronisations in between, must
+    # give the same h and store bit for bit after every replay.
+    c = 1
+    wl, dw = host(c), dev(c)
+    s = wl.spec
+    params = eg.HashParams.from_dict(wl.hash_params)
+    _, _, layers, _ = binding_objs(eg, c)
+    depth = s.max_ngram - 1
+    n_seqs = len(s.seq_lens)
+    cu = dw.cu_seqlens
+    ws = torch.empty(eg.engram_workspace_bytes(s.T, len(s.layer_ids), s.cols, s.hc, s.dim),
+                     dtype=torch.uint8, device="cuda")
+    ws_e = torch.empty_like(ws)
+
+    def state():
+        return (dw.h.clone(), dw.lookback.clone(),
+                torch.ones((n_seqs, depth), dtype=torch.uint8, device="cuda"))
+
+    h_g, hist_g, live_g = state()
+    h_e, hist_e, live_e = state()
+    cids_g = dw.cids.clone()
+    tok_g = eg.Tokens(cids_g, cu, None, None, hist_g, live_g)
+
+    def step(tokens, h, hist, live, w):
+        eg.engram_forward(params, tokens, layers, h, s.hc, s.dim, s.eps, s.clamp, s.dot_scale, w)
+        eg.engram_history_update(tokens, hist, live)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                    # warm-up outside the capture
+        step(tok_g, h_g.clone(), hist_g.clone(), live_g.clone(), ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(tok_g, h_g, hist_g, live_g, ws)
+    torch.cuda.synchronize()
+    # the capture itself ran nothing: restore the starting state
+    h_g.copy_(dw.h)
+    hist_g.copy_(dw.lookback)
+    live_g.fill_(1)
+    rng = np.random.default_rng(11)
+    for k in range(4):
+        new = tensor(rng.integers(0, s.compressed_vocab, s.T).astype(np.int32), "cuda")
+        cids_g.copy_(new)
+        g.replay()
+        tok_e = eg.Tokens(new, cu, None, None, hist_e, live_e)
+        step(tok_e, h_e, hist_e, live_e, ws_e)
+        torch.cuda.synchronize()
+        assert torch.equal(h_g.view(torch.int32), h_e.view(torch.int32)), k
+        assert torch.equal(hist_g, hist_e) and torch.equal(live_g, live_e), k
