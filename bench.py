@@ -133,6 +133,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--overlap", action="store_true",
+                    help="several layers: project every layer after the first on a second "
+                         "stream while the first layer's projection and gate run")
     ap.add_argument("--mxfp8", action="store_true",
                     help="FP8 tables: project the raw rows in MXFP8 against an MXFP8 copy "
                          "of wkv (engram_project_mxfp8)")
@@ -190,6 +193,12 @@ def main() -> int:
     ids = torch.empty((s.T, L, s.cols), dtype=torch.int32, device="cuda")
     rows = torch.empty((s.T, s.K), dtype=torch.int16, device="cuda")
     kv = torch.empty((s.T, s.N), dtype=torch.int16, device="cuda")
+    # --overlap: one kv buffer per layer, layers after the first projected on
+    # a second stream (the projection does not depend on h; only the gates
+    # are ordered).
+    overlap = args.overlap and len(s.layer_ids) > 1
+    kvs = [kv] + [torch.empty_like(kv) for _ in range(len(s.layer_ids) - 1)] if overlap else [kv] * len(s.layer_ids)
+    side = torch.cuda.Stream() if overlap else None
     num_rows = [l.table.numel() // (84 if fmt == eg.ENGRAM_ROWS_Q2K else 256) for l in dw.layers]
     # The fused Q2_K rows+projection kernel, as engram_forward picks it (more
     # than SKINNY_MAX_TOKENS tokens, table and columns within its limits).
@@ -204,13 +213,13 @@ def main() -> int:
         eg.engram_rows(fmt, dl.table, dl.scales, num_rows[l], layer_ids(l), L * s.cols, s.cols,
                        s.T, rows, None, stream)
 
-    def project_call(l):
-        eg.engram_project(rows, dw.layers[l].wkv, kv, s.T, s.K, s.N, stream)
+    def project_call(l, st=None):
+        eg.engram_project(rows, dw.layers[l].wkv, kvs[l], s.T, s.K, s.N, st or stream)
 
-    def fused_call(l):
+    def fused_call(l, st=None):
         dl = dw.layers[l]
         eg.engram_project_q2k(dl.table, num_rows[l], layer_ids(l), L * s.cols, s.cols, dl.wkv,
-                              kv, s.T, s.N, None, stream)
+                              kvs[l], s.T, s.N, None, st or stream)
 
     def mx_call(l):
         dl = dw.layers[l]
@@ -219,12 +228,36 @@ def main() -> int:
 
     def gate_call(l):
         dl = dw.layers[l]
-        eg.engram_gate(h, kv, dl.q_weight, dl.k_weight, dw.token_mask, s.T, s.hc, s.dim, s.eps,
+        eg.engram_gate(h, kvs[l], dl.q_weight, dl.k_weight, dw.token_mask, s.T, s.hc, s.dim, s.eps,
                        s.clamp, s.dot_scale, stream)
 
     # One step = the launches engram_forward makes, in its order.
     plan = [("hash", lambda: eg.engram_hash(params, tokens, ids, stream))]
-    for l in range(L):
+    if overlap:
+        # hash -> (side stream: layers 1.. projected) || (layer 0 projected, gated);
+        # each later gate waits for its layer's projection.
+        ev_hash = torch.cuda.Event()
+        ev_kv = [torch.cuda.Event() for _ in range(L)]
+        proj = fused_call if fused else None
+        if proj is None:
+            raise SystemExit("--overlap is built for the fused Q2_K projection")
+
+        def side_projections():
+            ev_hash.record(stream)
+            side.wait_event(ev_hash)
+            for l in range(1, L):
+                proj(l, side)
+                ev_kv[l].record(side)
+
+        def gate_after(l):
+            stream.wait_event(ev_kv[l])
+            gate_call(l)
+        plan.append(("side_projections", side_projections))
+        plan.append(("rows_project", lambda: proj(0)))
+        plan.append(("gate", lambda: gate_call(0)))
+        for l in range(1, L):
+            plan.append(("gate", lambda l=l: gate_after(l)))
+    for l in range(L if not overlap else 0):
         if mx:
             plan.append(("rows_project", lambda l=l: mx_call(l)))
         elif fused:
@@ -393,7 +426,9 @@ def main() -> int:
                                f"{s.num_rows} rows, dim={s.dim}, hc={s.hc}, "
                                f"{s.id_dist} ids",
                    "T": s.T, "K": s.K, "N": s.N, "row_format": s.fmt,
-                   "projection": "mxfp8" if mx else "bf16"},
+                   "projection": "mxfp8" if mx else "bf16",
+                   "schedule": "two streams: later layers projected beside layer 0"
+                               if overlap else "one stream, engram_forward order"},
         "roofline": roofline,
         "stages": stages,
     }

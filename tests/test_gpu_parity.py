@@ -801,3 +801,48 @@ def test_decode_graph_replay_matches_eager(eg):
         torch.cuda.synchronize()
         assert torch.equal(h_g.view(torch.int32), h_e.view(torch.int32)), k
         assert torch.equal(hist_g, hist_e) and torch.equal(live_g, live_e), k
+
+
+# ------------------------------------------------ two layers on two streams
+
+def test_two_stream_schedule_matches_forward(eg):
+    # The projections do not depend on h, so every layer after the first can
+    # be projected on a second stream while the first layer's projection and
+    # gate run; each later gate waits for its layer's kv.  The highway must
+    # equal engram_forward's bit for bit (same kernels, same inputs).
+    c = 3
+    wl, dw = host(c), dev(c)
+    s = wl.spec
+    L = len(s.layer_ids)
+    params, tokens, layers, _ = binding_objs(eg, c)
+    h_ref = dw.h.clone()
+    ws = torch.empty(eg.engram_workspace_bytes(s.T, L, s.cols, s.hc, s.dim), dtype=torch.uint8,
+                     device="cuda")
+    eg.engram_forward(params, tokens, layers, h_ref, s.hc, s.dim, s.eps, s.clamp, s.dot_scale,
+                      ws)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    ids = torch.empty((s.T, L, s.cols), dtype=torch.int32, device="cuda")
+    kvs = [torch.empty((s.T, s.N), dtype=torch.int16, device="cuda") for _ in range(L)]
+    h = dw.h.clone()
+    eg.engram_hash(params, tokens, ids, main)
+    ev_hash = torch.cuda.Event()
+    ev_hash.record(main)
+    side.wait_event(ev_hash)
+    ev = [torch.cuda.Event() for _ in range(L)]
+    for l in range(1, L):
+        dl = dw.layers[l]
+        eg.engram_project_q2k(dl.table, dl.table.numel() // 84, ids.view(-1)[l * s.cols:],
+                              L * s.cols, s.cols, dl.wkv, kvs[l], s.T, s.N, None, side)
+        ev[l].record(side)
+    for l in range(L):
+        dl = dw.layers[l]
+        if l == 0:
+            eg.engram_project_q2k(dl.table, dl.table.numel() // 84, ids.view(-1), L * s.cols,
+                                  s.cols, dl.wkv, kvs[0], s.T, s.N, None, main)
+        else:
+            main.wait_event(ev[l])
+        eg.engram_gate(h, kvs[l], dl.q_weight, dl.k_weight, dw.token_mask, s.T, s.hc, s.dim,
+                       s.eps, s.clamp, s.dot_scale, main)
+    torch.cuda.synchronize()
+    assert torch.equal(h.view(torch.int32), h_ref.view(torch.int32))
