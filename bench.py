@@ -79,6 +79,8 @@ def algorithmic(spec, token_mask) -> dict:
     per_live_gate = 2 * hc * dim * 4 + (hc + 1) * dim * 2
     mask_bytes = 0 if token_mask is None else T
     return {
+        # all layers' gates in one pass: h read and written once, every kv read
+        "gate_pass": live * (2 * hc * dim * 4 + L * (hc + 1) * dim * 2) + mask_bytes,
         "hash": T * 4 + T * L * cols * 4,
         "rows": T * per_tok_rows,                 # per layer
         "project": 2.0 * T * spec.K * spec.N,     # FLOP per layer
@@ -197,7 +199,7 @@ def main() -> int:
     # a second stream (the projection does not depend on h; only the gates
     # are ordered).
     overlap = args.overlap and len(s.layer_ids) > 1
-    kvs = [kv] + [torch.empty_like(kv) for _ in range(len(s.layer_ids) - 1)] if overlap else [kv] * len(s.layer_ids)
+    kvs = [kv] + [torch.empty_like(kv) for _ in range(len(s.layer_ids) - 1)]
     side = torch.cuda.Stream() if overlap else None
     num_rows = [l.table.numel() // (84 if fmt == eg.ENGRAM_ROWS_Q2K else 256) for l in dw.layers]
     # The fused Q2_K rows+projection kernel, as engram_forward picks it (more
@@ -225,6 +227,11 @@ def main() -> int:
         dl = dw.layers[l]
         eg.engram_project_mxfp8(dl.table, dl.scales, num_rows[l], layer_ids(l), L * s.cols,
                                 s.cols, wmx[l][0], wmx[l][1], kv, s.T, s.N, None, stream)
+
+    def gate_pass_call():
+        eg.engram_gate_layers(h, kvs, [dl.q_weight for dl in dw.layers],
+                              [dl.k_weight for dl in dw.layers], dw.token_mask, s.T, s.hc,
+                              s.dim, s.eps, s.clamp, s.dot_scale, stream)
 
     def gate_call(l):
         dl = dw.layers[l]
@@ -264,7 +271,9 @@ def main() -> int:
             plan.append(("rows_project", lambda l=l: fused_call(l)))
         else:
             plan += [("rows", lambda l=l: rows_call(l)), ("project", lambda l=l: project_call(l))]
-        plan.append(("gate", lambda l=l: gate_call(l)))
+    if not overlap:
+        # engram_forward: every projection first, then one gate pass for all layers
+        plan.append(("gate", gate_pass_call if L > 1 else (lambda: gate_call(0))))
 
     def step(ev=None):
         if ev is not None:
@@ -335,8 +344,10 @@ def main() -> int:
     def gbs(nbytes, ms):
         return nbytes / (ms * 1e-3) / 1e9
 
-    gg_ms = per_launch_ms["rows"] + per_launch_ms["gate"]
-    gg_gbs = gbs(alg["rows"] + alg["gate"], gg_ms)
+    gate_pass = L > 1 and not overlap
+    gate_bytes = alg["gate_pass"] if gate_pass else alg["gate"]
+    gg_ms = L * per_launch_ms["rows"] + per_launch_ms["gate"] * (1 if gate_pass or L == 1 else L)
+    gg_gbs = gbs(L * alg["rows"] + (gate_bytes if gate_pass or L == 1 else L * alg["gate"]), gg_ms)
     ms_per_step = elapsed * 1e3 / args.steps
 
     def prof(name):
@@ -395,15 +406,17 @@ def main() -> int:
                          "frac": round(proj_tf / BF16_PEAK_TFLOPS, 4),
                          "traffic": prof("gemm_skinny" if skinny else "gemm_nt"),
                          "in_step": not (fused or mx)}
-    gate_gbs = gbs(alg["gate"], per_launch_ms["gate"])
+    gate_gbs = gbs(gate_bytes, per_launch_ms["gate"])
     stages["gate"] = {"ms": round(per_launch_ms["gate"], 4), "bound": "hbm",
                       "achieved_gbs": round(gate_gbs, 1),
                       "frac": round(gate_gbs / HBM_PEAK_GBS, 4),
-                      "bytes_per_launch": alg["gate"],
+                      "bytes_per_launch": gate_bytes,
+                      "layers_per_launch": L if gate_pass else 1,
                       "traffic": prof("gate")}
     stages["gather_plus_gate"] = {"ms": round(gg_ms, 4), "achieved_gbs": round(gg_gbs, 1),
                                   "frac": round(gg_gbs / HBM_PEAK_GBS, 4),
-                                  "kernels": "engram_rows + engram_gate"}
+                                  "kernels": "engram_rows + engram_gate" +
+                                             (" (one gate pass for all layers)" if gate_pass else "")}
     stages["engram_forward_ms"] = round(forward_ms, 4)
     if graph_ms is not None:
         stages["engram_forward_graph_replay_ms"] = round(graph_ms, 4)

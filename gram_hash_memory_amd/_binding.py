@@ -30,7 +30,7 @@ HEAD_DIM, Q2K_ROW_BYTES, FP8_ROW_BYTES, FP8_SCALE_BYTES = 256, 84, 256, 8
 
 EXPORTS = ("engram_hash", "engram_history_update", "engram_rows", "engram_project", "engram_project_q2k",
            "engram_quantize_mxfp8", "engram_project_mxfp8", "engram_gate",
-           "engram_workspace_bytes", "engram_forward", "engram_last_error")
+           "engram_gate_layers", "engram_workspace_bytes", "engram_forward", "engram_last_error")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python gram_hash_memory_amd/build.py`")
@@ -70,6 +70,9 @@ _lib.engram_project_mxfp8.argtypes = [c_void_p, c_void_p, c_int64, c_void_p, c_i
                                       c_void_p]
 _lib.engram_gate.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                              c_int32, c_int32, c_float, c_float, c_float, c_void_p]
+_lib.engram_gate_layers.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
+                                    c_int32, c_int32, c_int32, c_float, c_float, c_float,
+                                    c_void_p]
 _lib.engram_workspace_bytes.argtypes = [c_int32, c_int32, c_int32, c_int32, c_int32]
 _lib.engram_workspace_bytes.restype = c_size_t
 _lib.engram_forward.argtypes = [_P(_HashParams), _P(_Tokens), _P(_Layer), c_void_p, c_int32,
@@ -77,7 +80,8 @@ _lib.engram_forward.argtypes = [_P(_HashParams), _P(_Tokens), _P(_Layer), c_void
                                 c_void_p, c_void_p]
 _lib.engram_last_error.restype = c_char_p
 for _name in ("engram_hash", "engram_history_update", "engram_rows", "engram_project", "engram_project_q2k",
-              "engram_quantize_mxfp8", "engram_project_mxfp8", "engram_gate", "engram_forward"):
+              "engram_quantize_mxfp8", "engram_project_mxfp8", "engram_gate", "engram_gate_layers",
+              "engram_forward"):
     getattr(_lib, _name).restype = c_int
 
 
@@ -247,6 +251,22 @@ def engram_gate(h, kv, q_weight, k_weight, token_mask, T: int, hc: int, dim: int
                             _dptr(token_mask, torch.uint8, T, "token_mask"), int(T), int(hc),
                             int(dim), float(eps), float(clamp), float(dot_scale),
                             _stream(stream)))
+
+
+def engram_gate_layers(h, kvs, q_weights, k_weights, token_mask, T: int, hc: int, dim: int,
+                       eps: float, clamp: float, dot_scale: float, stream=None) -> None:
+    """Stage 4 for several layers in one pass over h (layer order), as engram_forward runs it."""
+    n = len(kvs)
+    if not (len(q_weights) == len(k_weights) == n):
+        raise ValueError("one kv, q_weight and k_weight per layer")
+    arr = lambda ts, numel, name: (c_void_p * n)(*[_dptr(t, torch.int16, numel, name) for t in ts])
+    kv_a = arr(kvs, T * (hc + 1) * dim, "kv")
+    q_a = arr(q_weights, hc * dim, "q_weight")
+    k_a = arr(k_weights, hc * dim, "k_weight")
+    _check(_lib.engram_gate_layers(_dptr(h, torch.float32, T * hc * dim, "h"), kv_a, q_a, k_a, n,
+                                   _dptr(token_mask, torch.uint8, T, "token_mask"), int(T),
+                                   int(hc), int(dim), float(eps), float(clamp), float(dot_scale),
+                                   _stream(stream)))
 
 
 def engram_workspace_bytes(T: int, n_layers: int, cols: int, hc: int, dim: int) -> int:

@@ -303,13 +303,38 @@ engram_status engram_gate(float *h, const uint16_t *kv, const uint16_t *q_weight
                     "engram_gate launch");
 }
 
+engram_status engram_gate_layers(float *h, const uint16_t *const *kv,
+                                 const uint16_t *const *q_weight,
+                                 const uint16_t *const *k_weight, int32_t n_layers,
+                                 const uint8_t *token_mask, int32_t T, int32_t hc, int32_t dim,
+                                 float eps, float clamp, float dot_scale, hipStream_t stream) {
+  REQUIRE_SUP(n_layers >= 1 && n_layers <= ENGRAM_MAX_LAYERS, "n_layers=%d outside 1..%d",
+              n_layers, ENGRAM_MAX_LAYERS);
+  engram_status st = check_gate_shape(T, hc, dim, eps, clamp);
+  if (st != ENGRAM_OK) return st;
+  if (T == 0) return ENGRAM_OK;
+  REQUIRE(kv && q_weight && k_weight, "kv, q_weight or k_weight array is NULL");
+  engram::GateLayers gl{};
+  gl.n = n_layers;
+  for (int l = 0; l < n_layers; ++l) {
+    if ((st = check_gate_ptrs(h, kv[l], q_weight[l], k_weight[l])) != ENGRAM_OK)
+      return fail_layer(st, l);
+    gl.kv[l] = kv[l];
+    gl.qw[l] = q_weight[l];
+    gl.kw[l] = k_weight[l];
+  }
+  return hip_status(engram::launch_gate_layers(h, gl, token_mask, T, hc, dim, eps, clamp,
+                                               dot_scale, stream),
+                    "engram_gate_layers launch");
+}
+
 size_t engram_workspace_bytes(int32_t T, int32_t n_layers, int32_t cols, int32_t hc,
                               int32_t dim) {
   if (T < 0 || n_layers < 0 || cols < 0 || hc < 0 || dim < 0) return 0;
   const size_t t = size_t(T);
   return align256(t * n_layers * cols * sizeof(int32_t)) +
          align256(t * cols * ENGRAM_HEAD_DIM * sizeof(uint16_t)) +
-         align256(t * (size_t(hc) + 1) * dim * sizeof(uint16_t));
+         size_t(n_layers) * align256(t * (size_t(hc) + 1) * dim * sizeof(uint16_t));
 }
 
 engram_status engram_forward(const engram_hash_params *params, const engram_tokens *tokens,
@@ -348,7 +373,10 @@ engram_status engram_forward(const engram_hash_params *params, const engram_toke
   ws += align256(size_t(T) * L * cols * sizeof(int32_t));
   uint16_t *rows = reinterpret_cast<uint16_t *>(ws);
   ws += align256(size_t(T) * K * sizeof(uint16_t));
-  uint16_t *kv = reinterpret_cast<uint16_t *>(ws);
+  // one kv per layer: every projection runs before the one gate pass
+  uint16_t *kv_all = reinterpret_cast<uint16_t *>(ws);
+  const size_t kv_elems = align256(size_t(T) * N * sizeof(uint16_t)) / sizeof(uint16_t);
+  uint16_t *kv = kv_all;
 
   for (int l = 0; l < L; ++l) {
     const engram_layer &ly = layers[l];
@@ -367,8 +395,14 @@ engram_status engram_forward(const engram_hash_params *params, const engram_toke
   if ((st = hip_status(engram::launch_hash(tab, *tokens, ids, stream), "hash launch")) !=
       ENGRAM_OK)
     return st;
+  engram::GateLayers gl{};
+  gl.n = L;
   for (int l = 0; l < L; ++l) {
     const engram_layer &ly = layers[l];
+    kv = kv_all + l * kv_elems;
+    gl.kv[l] = kv;
+    gl.qw[l] = ly.q_weight;
+    gl.kw[l] = ly.k_weight;
     // Few tokens: rows -> the weight-streaming projection beats the fused
     // 256 x 256 tiles (the dequant is then a few microseconds).
     if (ly.wkv_mx) {
@@ -395,13 +429,12 @@ engram_status engram_forward(const engram_hash_params *params, const engram_toke
                            "project launch")) != ENGRAM_OK)
         return st;
     }
-    if ((st = hip_status(engram::launch_gate(h, kv, ly.q_weight, ly.k_weight,
-                                             tokens->token_mask, T, hc, dim, eps, clamp,
-                                             dot_scale, stream),
-                         "gate launch")) != ENGRAM_OK)
-      return st;
   }
-  return ENGRAM_OK;
+  // The projections do not depend on h; the gates of all layers, in layer
+  // order, then take one pass over the highway.
+  return hip_status(engram::launch_gate_layers(h, gl, tokens->token_mask, T, hc, dim, eps,
+                                               clamp, dot_scale, stream),
+                    "gate launch");
 }
 
 }  // extern "C"

@@ -82,6 +82,17 @@ hipError_t launch_project_mx(const uint8_t *table, const uint8_t *scales, int64_
 hipError_t launch_quantize_mx(const uint16_t *w, int32_t N, int32_t K, uint8_t *codes,
                               uint8_t *scales, hipStream_t stream);
 
+// The gate of several layers in one pass over h (layer order 0..n-1).
+struct GateLayers {
+  const uint16_t *kv[ENGRAM_MAX_LAYERS];
+  const uint16_t *qw[ENGRAM_MAX_LAYERS];
+  const uint16_t *kw[ENGRAM_MAX_LAYERS];
+  int32_t n;
+};
+hipError_t launch_gate_layers(float *h, const GateLayers &ly, const uint8_t *mask, int32_t T,
+                              int32_t hc, int32_t dim, float eps, float clamp, float dot_scale,
+                              hipStream_t stream);
+
 hipError_t launch_gate(float *h, const uint16_t *kv, const uint16_t *qw, const uint16_t *kw,
                        const uint8_t *mask, int32_t T, int32_t hc, int32_t dim, float eps,
                        float clamp, float dot_scale, hipStream_t stream);

@@ -16,6 +16,13 @@
 // writes x + g * v from the registers, so h is read once and written once
 // and the shared value once per token (not once per stream).  Masked tokens
 // return before touching memory, which leaves them bit-for-bit unchanged.
+//
+// Several engram layers that act on the same highway one after the other
+// (the forward's layers, with nothing in between) run in one pass: the
+// streams stay in registers from one layer's gate to the next, so h is read
+// and written once for all of them.  Each layer's arithmetic is the
+// single-layer kernel's, on the same fp32 values, so the result is bit for
+// bit that of separate calls.
 #include "common.hpp"
 
 namespace engram {
@@ -45,9 +52,8 @@ __device__ __forceinline__ void bf16x8_to_f32(const u32x4 w, float *f) {
 // of a few dozen tokens spreads over hc times more workgroups.
 template <int HC, int NCH, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void gate_kernel(
-    float *__restrict__ h, const uint16_t *__restrict__ kv, const uint16_t *__restrict__ qw,
-    const uint16_t *__restrict__ kw, const uint8_t *__restrict__ mask, int32_t dim,
-    int32_t hc, float eps, float clamp, float dot_scale) {
+    float *__restrict__ h, const GateLayers layers, const uint8_t *__restrict__ mask,
+    int32_t dim, int32_t hc, float eps, float clamp, float dot_scale) {
   const int64_t t = SPLIT ? blockIdx.x / hc : blockIdx.x;
   const int s0 = SPLIT ? int(blockIdx.x % hc) : 0;   // first stream of this workgroup
   const int nstreams = SPLIT ? hc : HC;
@@ -55,17 +61,78 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(
   __shared__ float red[kWaves][3 * HC];
 
   float *ht = h + (t * nstreams + s0) * int64_t(dim);
-  const uint16_t *kvt = kv + t * (nstreams + 1) * int64_t(dim);
-  const uint16_t *vt = kvt + nstreams * int64_t(dim);       // the shared value
-  kvt += s0 * int64_t(dim);
-  qw += s0 * int64_t(dim);
-  kw += s0 * int64_t(dim);
-
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const float inv_dim = 1.0f / float(dim);
   float x[HC][NCH][kVec];
   float ssx[HC], ssk[HC], dot[HC];
+
+  // Partial sums of one chunk of one stream against layer l's key and weights.
+  auto accumulate = [&](int l, int c, int s, int i0) {
+    const uint16_t *kvt =
+        layers.kv[l] + t * (nstreams + 1) * int64_t(dim) + (s0 + s) * int64_t(dim);
+    const uint16_t *qw = layers.qw[l] + (s0 + s) * int64_t(dim);
+    const uint16_t *kw = layers.kw[l] + (s0 + s) * int64_t(dim);
+    float key[kVec], q[kVec], k[kVec];
+    bf16x8_to_f32(*reinterpret_cast<const u32x4 *>(kvt + i0), key);
+    bf16x8_to_f32(*reinterpret_cast<const u32x4 *>(qw + i0), q);
+    bf16x8_to_f32(*reinterpret_cast<const u32x4 *>(kw + i0), k);
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+      const float xv = x[s][c][e];
+      ssx[s] += xv * xv;
+      ssk[s] += key[e] * key[e];
+      dot[s] += (xv * q[e]) * (key[e] * k[e]);
+    }
+  };
+  // Reduce the sums over the workgroup, derive the hc gates of layer l and
+  // add gate * value to the streams in registers.
+  auto finish = [&](int l) {
+#pragma unroll
+    for (int s = 0; s < HC; ++s) {
+      const float a = wave_sum(ssx[s]), b = wave_sum(ssk[s]), d = wave_sum(dot[s]);
+      if (lane == 0) {
+        red[wave][3 * s] = a;
+        red[wave][3 * s + 1] = b;
+        red[wave][3 * s + 2] = d;
+      }
+    }
+    __syncthreads();
+    float g[HC];
+#pragma unroll
+    for (int s = 0; s < HC; ++s) {
+      float a = 0.f, b = 0.f, d = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        a += red[w][3 * s];
+        b += red[w][3 * s + 1];
+        d += red[w][3 * s + 2];
+      }
+      const float rx = 1.0f / sqrtf(a * inv_dim + eps);
+      const float rk = 1.0f / sqrtf(b * inv_dim + eps);
+      const float av = dot_scale * d * rx * rk;
+      const float mag = sqrtf(fmaxf(fabsf(av), clamp));
+      const float z = av > 0.f ? mag : (av < 0.f ? -mag : 0.f);
+      g[s] = 1.0f / (1.0f + expf(-z));
+    }
+    const uint16_t *vt =                           // the shared value
+        layers.kv[l] + t * (nstreams + 1) * int64_t(dim) + nstreams * int64_t(dim);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int i0 = (threadIdx.x + c * kThreads) * kVec;
+      if (i0 < dim) {
+        float v[kVec];
+        bf16x8_to_f32(*reinterpret_cast<const u32x4 *>(vt + i0), v);
+#pragma unroll
+        for (int s = 0; s < HC; ++s)
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) x[s][c][e] = x[s][c][e] + g[s] * v[e];
+      }
+    }
+  };
+
+  // Layer 0: the streams are loaded and reduced in the same pass.
 #pragma unroll
   for (int s = 0; s < HC; ++s) ssx[s] = ssk[s] = dot[s] = 0.f;
-
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int i0 = (threadIdx.x + c * kThreads) * kVec;
@@ -79,65 +146,38 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(
           x[s][c][e] = a[e];
           x[s][c][4 + e] = b[e];
         }
-        float key[kVec], q[kVec], k[kVec];
-        bf16x8_to_f32(*reinterpret_cast<const u32x4 *>(kvt + s * dim + i0), key);
-        bf16x8_to_f32(*reinterpret_cast<const u32x4 *>(qw + s * dim + i0), q);
-        bf16x8_to_f32(*reinterpret_cast<const u32x4 *>(kw + s * dim + i0), k);
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) {
-          const float xv = x[s][c][e];
-          ssx[s] += xv * xv;
-          ssk[s] += key[e] * key[e];
-          dot[s] += (xv * q[e]) * (key[e] * k[e]);
-        }
+        accumulate(0, c, s, i0);
       }
     }
   }
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  finish(0);
+  // Later layers read the streams from registers.
+  for (int l = 1; l < layers.n; ++l) {
+    __syncthreads();                               // every thread is done with red
 #pragma unroll
-  for (int s = 0; s < HC; ++s) {
-    const float a = wave_sum(ssx[s]), b = wave_sum(ssk[s]), d = wave_sum(dot[s]);
-    if (lane == 0) {
-      red[wave][3 * s] = a;
-      red[wave][3 * s + 1] = b;
-      red[wave][3 * s + 2] = d;
+    for (int s = 0; s < HC; ++s) ssx[s] = ssk[s] = dot[s] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int i0 = (threadIdx.x + c * kThreads) * kVec;
+      if (i0 < dim) {
+#pragma unroll
+        for (int s = 0; s < HC; ++s) accumulate(l, c, s, i0);
+      }
     }
-  }
-  __syncthreads();
-
-  float g[HC];
-  const float inv_dim = 1.0f / float(dim);
-#pragma unroll
-  for (int s = 0; s < HC; ++s) {
-    float a = 0.f, b = 0.f, d = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      a += red[w][3 * s];
-      b += red[w][3 * s + 1];
-      d += red[w][3 * s + 2];
-    }
-    const float rx = 1.0f / sqrtf(a * inv_dim + eps);
-    const float rk = 1.0f / sqrtf(b * inv_dim + eps);
-    const float av = dot_scale * d * rx * rk;
-    const float mag = sqrtf(fmaxf(fabsf(av), clamp));
-    const float z = av > 0.f ? mag : (av < 0.f ? -mag : 0.f);
-    g[s] = 1.0f / (1.0f + expf(-z));
+    finish(l);
   }
 
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int i0 = (threadIdx.x + c * kThreads) * kVec;
     if (i0 < dim) {
-      float v[kVec];
-      bf16x8_to_f32(*reinterpret_cast<const u32x4 *>(vt + i0), v);
 #pragma unroll
       for (int s = 0; s < HC; ++s) {
         f32x4 a, b;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          a[e] = x[s][c][e] + g[s] * v[e];
-          b[e] = x[s][c][4 + e] + g[s] * v[4 + e];
+          a[e] = x[s][c][e];
+          b[e] = x[s][c][4 + e];
         }
         *reinterpret_cast<f32x4 *>(ht + s * dim + i0) = a;
         *reinterpret_cast<f32x4 *>(ht + s * dim + i0 + 4) = b;
@@ -147,23 +187,22 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(
 }
 
 template <int HC, bool SPLIT>
-hipError_t launch_hc(float *h, const uint16_t *kv, const uint16_t *qw, const uint16_t *kw,
-                     const uint8_t *mask, int32_t T, int32_t hc, int32_t dim, float eps,
-                     float clamp, float dot_scale, hipStream_t stream) {
+hipError_t launch_hc(float *h, const GateLayers &ly, const uint8_t *mask, int32_t T, int32_t hc,
+                     int32_t dim, float eps, float clamp, float dot_scale, hipStream_t stream) {
   const int nch = (dim + kThreads * kVec - 1) / (kThreads * kVec);
   const dim3 grid(SPLIT ? unsigned(T) * unsigned(hc) : unsigned(T)), block(kThreads);
   switch (nch) {
     case 1:
-      hipLaunchKernelGGL((gate_kernel<HC, 1, SPLIT>), grid, block, 0, stream, h, kv, qw, kw,
-                         mask, dim, hc, eps, clamp, dot_scale);
+      hipLaunchKernelGGL((gate_kernel<HC, 1, SPLIT>), grid, block, 0, stream, h, ly, mask, dim,
+                         hc, eps, clamp, dot_scale);
       break;
     case 2:
-      hipLaunchKernelGGL((gate_kernel<HC, 2, SPLIT>), grid, block, 0, stream, h, kv, qw, kw,
-                         mask, dim, hc, eps, clamp, dot_scale);
+      hipLaunchKernelGGL((gate_kernel<HC, 2, SPLIT>), grid, block, 0, stream, h, ly, mask, dim,
+                         hc, eps, clamp, dot_scale);
       break;
     default:
-      hipLaunchKernelGGL((gate_kernel<HC, 4, SPLIT>), grid, block, 0, stream, h, kv, qw, kw,
-                         mask, dim, hc, eps, clamp, dot_scale);
+      hipLaunchKernelGGL((gate_kernel<HC, 4, SPLIT>), grid, block, 0, stream, h, ly, mask, dim,
+                         hc, eps, clamp, dot_scale);
       break;
   }
   return hipGetLastError();
@@ -174,20 +213,30 @@ constexpr int kSplitBelow = 1024;
 
 }  // namespace
 
-hipError_t launch_gate(float *h, const uint16_t *kv, const uint16_t *qw, const uint16_t *kw,
-                       const uint8_t *mask, int32_t T, int32_t hc, int32_t dim, float eps,
-                       float clamp, float dot_scale, hipStream_t stream) {
+hipError_t launch_gate_layers(float *h, const GateLayers &ly, const uint8_t *mask, int32_t T,
+                              int32_t hc, int32_t dim, float eps, float clamp, float dot_scale,
+                              hipStream_t stream) {
   if (T < kSplitBelow && hc > 1)
-    return launch_hc<1, true>(h, kv, qw, kw, mask, T, hc, dim, eps, clamp, dot_scale, stream);
+    return launch_hc<1, true>(h, ly, mask, T, hc, dim, eps, clamp, dot_scale, stream);
   switch (hc) {
 #define ENGRAM_GATE_HC(n) \
-    case n: return launch_hc<n, false>(h, kv, qw, kw, mask, T, hc, dim, eps, clamp, dot_scale, stream);
+    case n: return launch_hc<n, false>(h, ly, mask, T, hc, dim, eps, clamp, dot_scale, stream);
     ENGRAM_GATE_HC(1) ENGRAM_GATE_HC(2) ENGRAM_GATE_HC(3) ENGRAM_GATE_HC(4)
     ENGRAM_GATE_HC(5) ENGRAM_GATE_HC(6) ENGRAM_GATE_HC(7)
 #undef ENGRAM_GATE_HC
-    default: return launch_hc<8, false>(h, kv, qw, kw, mask, T, hc, dim, eps, clamp, dot_scale,
-                                        stream);
+    default: return launch_hc<8, false>(h, ly, mask, T, hc, dim, eps, clamp, dot_scale, stream);
   }
+}
+
+hipError_t launch_gate(float *h, const uint16_t *kv, const uint16_t *qw, const uint16_t *kw,
+                       const uint8_t *mask, int32_t T, int32_t hc, int32_t dim, float eps,
+                       float clamp, float dot_scale, hipStream_t stream) {
+  GateLayers ly{};
+  ly.kv[0] = kv;
+  ly.qw[0] = qw;
+  ly.kw[0] = kw;
+  ly.n = 1;
+  return launch_gate_layers(h, ly, mask, T, hc, dim, eps, clamp, dot_scale, stream);
 }
 
 }  // namespace engram

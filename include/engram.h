@@ -303,13 +303,30 @@ ENGRAM_API engram_status engram_gate(float *h, const uint16_t *kv, const uint16_
                           int32_t hc, int32_t dim, float eps, float clamp, float dot_scale,
                           hipStream_t stream);
 
+/* Stage 4 for several layers in one pass: the gates of layers 0..n_layers-1,
+ * in that order, on the same h (engram_forward's layers, which nothing
+ * separates), with h read and written once.  The result is bit for bit that
+ * of engram_gate called per layer in order.  kv, q_weight, k_weight: HOST
+ * arrays [n_layers] of DEVICE pointers, each as for engram_gate;
+ * 1 <= n_layers <= ENGRAM_MAX_LAYERS.  Other arguments as for engram_gate.
+ */
+ENGRAM_API engram_status engram_gate_layers(float *h, const uint16_t *const *kv,
+                                            const uint16_t *const *q_weight,
+                                            const uint16_t *const *k_weight, int32_t n_layers,
+                                            const uint8_t *token_mask, int32_t T, int32_t hc,
+                                            int32_t dim, float eps, float clamp,
+                                            float dot_scale, hipStream_t stream);
+
 /* Bytes of device workspace engram_forward needs for this shape: the ids,
- * one layer's rows and one layer's kv, each 256-byte aligned. */
+ * one layer's rows and every layer's kv, each 256-byte aligned. */
 ENGRAM_API size_t engram_workspace_bytes(int32_t T, int32_t n_layers, int32_t cols, int32_t hc,
                               int32_t dim);
 
 /* The whole forward ([spark] overview, stages 1-4): hash every layer once,
  * then for each layer in order: rows -> projection -> gate on the same h.
+ * The projections do not read h, so all of them run first, each into its own
+ * kv, and one gate pass then applies the layers' gates in order with h held
+ * in registers (h read and written once; the same bits as per-layer gates).
  * Q2_K layers within the limits of engram_project_q2k run rows -> projection
  * as that fused kernel (same kv bits) when T > 128.  FP8 layers that carry
  * wkv_mx run engram_project_mxfp8 instead of rows -> projection.

@@ -35,7 +35,7 @@ def test_header_declares_the_five_calls_and_helpers():
     names = declared_functions()
     for want in ("engram_hash", "engram_history_update", "engram_rows", "engram_project", "engram_project_q2k",
                  "engram_quantize_mxfp8", "engram_project_mxfp8", "engram_gate",
-                 "engram_forward", "engram_workspace_bytes", "engram_last_error"):
+                 "engram_gate_layers", "engram_forward", "engram_workspace_bytes", "engram_last_error"):
         assert want in names
 
 
@@ -60,6 +60,10 @@ def test_workspace_bytes(eg):
         return (x + 255) // 256 * 256
     T, L, cols, hc, dim = 8192, 1, 24, 4, 4096
     want = a256(T * L * cols * 4) + a256(T * cols * 256 * 2) + a256(T * (hc + 1) * dim * 2)
+    assert eg.engram_workspace_bytes(T, L, cols, hc, dim) == want
+    # several layers: every layer's kv (the gates run in one pass after the projections)
+    L = 2
+    want = a256(T * L * cols * 4) + a256(T * cols * 256 * 2) + L * a256(T * (hc + 1) * dim * 2)
     assert eg.engram_workspace_bytes(T, L, cols, hc, dim) == want
     assert eg.engram_workspace_bytes(0, 1, 24, 4, 4096) == 0
     assert eg.engram_workspace_bytes(-1, 1, 24, 4, 4096) == 0
@@ -105,6 +109,9 @@ def _raw(eg):
                                        ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_void_p, ctypes.c_void_p]
+    lib.engram_gate_layers.argtypes = ([ctypes.c_void_p] * 4 + [ctypes.c_int32, ctypes.c_void_p] +
+                                       [ctypes.c_int32] * 3 + [ctypes.c_float] * 3 +
+                                       [ctypes.c_void_p])
     lib.engram_history_update.argtypes = [ctypes.POINTER(_TK), ctypes.c_int32, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p]
     lib.engram_quantize_mxfp8.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
@@ -235,6 +242,22 @@ class TestValidation:
         empty = _TK(0, 0, 0, None, None, None, None, None, None)
         assert lib.engram_history_update(ctypes.byref(empty), 3, None, None,
                                          None) == eg.ENGRAM_OK
+
+    def test_gate_layers_rejects(self, eg):
+        lib = _raw(eg)
+        P = ctypes.c_void_p * 2
+        good = P(FAKE, FAKE)
+        bad1 = P(FAKE, FAKE + 4)                  # layer 1's kv misaligned
+
+        def call(n=2, kv=good, q=good, k=good, T=8):
+            return lib.engram_gate_layers(FAKE, kv, q, k, n, None, T, 4, 4096, 1e-6, 1e-6,
+                                          1 / 64, None)
+        assert call(n=0) == eg.ENGRAM_ERR_UNSUPPORTED
+        assert call(n=5) == eg.ENGRAM_ERR_UNSUPPORTED
+        assert call(kv=None) == eg.ENGRAM_ERR_ARG
+        assert call(kv=bad1) == eg.ENGRAM_ERR_ARG
+        assert lib.engram_last_error().decode().startswith("layer 1: ")
+        assert call(T=0, kv=None, q=None, k=None) == eg.ENGRAM_OK
 
     def test_quantize_mxfp8_rejects(self, eg):
         lib = _raw(eg)

@@ -846,3 +846,90 @@ def test_two_stream_schedule_matches_forward(eg):
                        s.eps, s.clamp, s.dot_scale, main)
     torch.cuda.synchronize()
     assert torch.equal(h.view(torch.int32), h_ref.view(torch.int32))
+
+
+# ------------------------------------------------------------ limits
+
+def test_hash_at_maximum_sizes(eg):
+    # ENGRAM_MAX_LAYERS layers, orders up to ENGRAM_MAX_NGRAM with 8 heads (56
+    # columns), a full lookback of max_ngram - 1 with dead entries, masks and
+    # documents: bit-exact against the oracle.
+    from oracle.layout import engram_layout, hash_multipliers
+    L, max_ngram, n_heads, V = 4, 8, 8, 70000
+    primes, offsets = engram_layout(L, max_ngram, n_heads, 90001)
+    hp = dict(multipliers=hash_multipliers([1, 5, 9, 14], max_ngram, V), primes=primes,
+              offsets=offsets, max_ngram=max_ngram, n_heads=n_heads, pad_id=3)
+    rng = np.random.default_rng(41)
+    cu = np.array([0, 1, 7, 7, 200, 333], dtype=np.int32)
+    T, n_seqs, depth = int(cu[-1]), len(cu) - 1, max_ngram - 1
+    cids = rng.integers(0, V, T).astype(np.int32)
+    mask = (rng.random(T) > 0.1).astype(np.uint8)
+    docs = np.concatenate([np.sort(rng.integers(0, 3, cu[i + 1] - cu[i]))
+                           for i in range(n_seqs)]).astype(np.int32)
+    lb = rng.integers(0, V, (n_seqs, depth)).astype(np.int32)
+    lb_live = (rng.random((n_seqs, depth)) > 0.2).astype(np.uint8)
+    want = oracle.hash_ids(cids, cu, hp["multipliers"], primes, offsets, max_ngram, n_heads, 3,
+                           doc_ids=docs, token_mask=mask, lookback=lb, lookback_live=lb_live)
+    params = eg.HashParams.from_dict(hp)
+    tokens = eg.Tokens(tensor(cids, "cuda"), tensor(cu, "cuda"), tensor(docs, "cuda"),
+                       tensor(mask, "cuda"), tensor(lb, "cuda"), tensor(lb_live, "cuda"))
+    ids = torch.empty((T, L, (max_ngram - 1) * n_heads), dtype=torch.int32, device="cuda")
+    eg.engram_hash(params, tokens, ids)
+    assert np.array_equal(ids.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("kind,T,cols,N", [("q2k", 300, 32, 512), ("mx", 130, 40, 300)])
+def test_projection_at_many_columns(eg, kind, T, cols, N):
+    # The fused Q2_K projection at its column limit (32) and the MXFP8
+    # projection past it (no column limit), against the oracle.
+    rng = np.random.default_rng(cols)
+    R, K = 999, cols * 256
+    ids_np = rng.integers(0, R, (T, cols)).astype(np.int32)
+    wkv_np = oracle.bf16_bits(oracle.bf16_round(0.02 * rng.standard_normal((N, K))))
+    kv = torch.full((T, N), 0x7777, dtype=torch.int16, device="cuda")
+    if kind == "q2k":
+        table_np = workloads.q2k_table(0, 0, R)
+        eg.engram_project_q2k(tensor(table_np, "cuda"), R, tensor(ids_np, "cuda"), cols, cols,
+                              tensor(wkv_np, "cuda"), kv, T, N)
+        _check_kv(kv.cpu().numpy().view(np.uint16), oracle.rows_q2k(table_np, ids_np), wkv_np)
+    else:
+        table_np, scales_np = workloads.fp8_table(4, 1, R)
+        wc, ws = oracle.quantize_mxfp8(wkv_np)
+        eg.engram_project_mxfp8(tensor(table_np, "cuda"), tensor(scales_np, "cuda"), R,
+                                tensor(ids_np, "cuda"), cols, cols, tensor(wc, "cuda"),
+                                tensor(ws, "cuda"), kv, T, N)
+        a_c, a_s = oracle.rows_fp8_mx(table_np, scales_np, ids_np)
+        _check_kv_mx(kv.cpu().numpy().view(np.uint16), a_c, a_s, wc, ws)
+
+
+@pytest.mark.parametrize("T,masked", [(100, False), (1500, True)])
+def test_gate_layers_equals_gate_per_layer(eg, T, masked):
+    # One pass for two and three layers against engram_gate per layer, in
+    # order, bit for bit (per-stream workgroups below 1024 tokens, per-token
+    # above), and against the oracle's gates in sequence.
+    rng = np.random.default_rng(T)
+    hc, dim, eps, clamp, ds = 4, 512, 1e-6, 1e-6, 1 / np.sqrt(512)
+    h0 = rng.standard_normal((T, hc, dim)).astype(np.float32)
+    mask = (rng.random(T) > 0.2).astype(np.uint8) if masked else None
+    for n in (2, 3):
+        kvs = [oracle.bf16_bits(oracle.bf16_round(rng.standard_normal((T, (hc + 1) * dim))))
+               for _ in range(n)]
+        qs = [oracle.bf16_bits(oracle.bf16_round(1 + 0.1 * rng.standard_normal((hc, dim))))
+              for _ in range(n)]
+        ks = [oracle.bf16_bits(oracle.bf16_round(1 + 0.1 * rng.standard_normal((hc, dim))))
+              for _ in range(n)]
+        kv_d = [tensor(a, "cuda") for a in kvs]
+        q_d = [tensor(a, "cuda") for a in qs]
+        k_d = [tensor(a, "cuda") for a in ks]
+        m_d = None if mask is None else tensor(mask, "cuda")
+        h1 = tensor(h0, "cuda")
+        eg.engram_gate_layers(h1, kv_d, q_d, k_d, m_d, T, hc, dim, eps, clamp, ds)
+        h2 = tensor(h0, "cuda")
+        for l in range(n):
+            eg.engram_gate(h2, kv_d[l], q_d[l], k_d[l], m_d, T, hc, dim, eps, clamp, ds)
+        assert torch.equal(h1.view(torch.int32), h2.view(torch.int32)), n
+        want = h0
+        for l in range(n):
+            want = oracle.gate(want, kvs[l], qs[l], ks[l], mask, eps, clamp, ds)
+        err = np.abs(h1.cpu().numpy() - want) / np.maximum(1.0, np.abs(want))
+        assert err.max() <= 1e-2, err.max()
