@@ -352,7 +352,7 @@ def main() -> int:
 
     def prof(name):
         # Summaries exist for the prefill (T=8192) and decode (T=64) workloads.
-        suffix = {2: "_prefill_T8192.md", 1: "_decode_T64.md",
+        suffix = {2: "_prefill_T8192.md", 1: "_decode_T64.md", 3: "_two_layer_T4096.md",
                   4: "_fp8_T16384.md"}.get(args.config)
         return profiled_traffic(name + suffix) if suffix else None
 
