@@ -1,9 +1,11 @@
 """Benchmark: Engram forward tokens/s on one MI355X, with per-stage roofline fractions.
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline] [--mxfp8]
+                    [--overlap]
 
 A step is one pass of the whole hot path over the batch: the hash for every
-layer, then per layer the row gather, the projection and the gate.  The
+layer, then per layer the row gather and the projection, then the gate of
+every layer (one pass over the highway when there are several).  The
 inputs are resident in HBM before timing starts.  The timed region issues the
 same C-ABI calls that engram_forward makes, in its order, on one stream, and
 records HIP events between them, so each kernel's average duration comes from
@@ -13,7 +15,9 @@ and projection fused into one kernel); the two-kernel path it replaces
 engram_forward itself.  With --mxfp8 (FP8 tables only) the layers carry an
 MXFP8 copy of wkv, made once before timing, and the step runs
 engram_project_mxfp8 (raw FP8 rows on the block-scaled matrix cores) in place
-of rows -> projection.
+of rows -> projection.  With --overlap (several layers) the layers after the
+first are projected on a second stream beside the first layer's projection
+and gate, each later gate waiting for its layer (a comparison schedule).
 
 Prints ONE JSON line: the headline metric, plus `roofline` for the dominant
 kernel (the bf16 MFMA projection), `stages` for every kernel, and
