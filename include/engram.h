@@ -263,8 +263,11 @@ ENGRAM_API engram_status engram_quantize_mxfp8(const uint16_t *w, int32_t N, int
  * bf16(sum_k a[t][k] * w[n][k]), a[t][r*256 + i] = e4m3(table[ids[t][r]][i])
  * * 2^(scales[ids[t][r]][i/32] - 127), w = wkv_codes/wkv_scales likewise.
  * The rows are read raw by the block-scaled matrix cores
- * (v_mfma_scale_f32_32x32x64_f8f6f4) and never dequantised to memory;
- * products accumulate in fp32 and each output is rounded to bf16 once.
+ * (v_mfma_scale_f32_32x32x64_f8f6f4) and never dequantised to memory.  The
+ * matrix cores sum each instruction's 64 products below fp32 precision
+ * (measured: up to 1.7e-4 of the sum of |products| on random e4m3 data); the
+ * instructions' results accumulate in fp32 and each output is rounded to
+ * bf16 once.
  *   table DEVICE [num_rows][256] e4m3fn codes, 16-byte aligned; scales DEVICE
  *   [num_rows][8], 4-byte aligned; ids, ids_token_stride, cols, bad_ids as for
  *   engram_rows (K = cols * 256; an id outside the table contributes 0);

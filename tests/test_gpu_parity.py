@@ -478,14 +478,22 @@ def _gpu_mx_weight(eg, wkv_dev, N, K):
     return codes, scales
 
 
+# The block-scaled matrix cores do not sum a block's products at fp32 precision:
+# on random e4m3 data one v_mfma_scale_*_f8f6f4 is off by up to 1.7e-4 of the
+# sum of its |products| (measured; IEEE fp32 summation of 64 terms stays near
+# 4e-6).  The MXFP8 bar therefore floors the relative term at 2^-12.
+MX_SUM_REL = 2.0 ** -12
+
+
 def _check_kv_mx(got_bits, a_codes, a_scales, w_codes, w_scales):
-    """The projection bar for MXFP8 operands: one bf16 ulp + K * 2^-24 * sum|a||w|
-    against the oracle's exactly summed, once-rounded value."""
+    """The projection bar for MXFP8 operands: one bf16 ulp + max(K 2^-24, 2^-12) *
+    sum|a||w| against the oracle's exactly summed, once-rounded value."""
     want = oracle.bf16_value(oracle.project_mxfp8(a_codes, a_scales, w_codes, w_scales))
     got = oracle.bf16_value(got_bits)
     a, b = oracle.mx_values(a_codes, a_scales), oracle.mx_values(w_codes, w_scales)
     K = a.shape[1]
-    bound = bf16_ulp(np.maximum(np.abs(want), np.abs(got))) + K * 2.0 ** -24 * (np.abs(a) @ np.abs(b).T)
+    rel = max(K * 2.0 ** -24, MX_SUM_REL)
+    bound = bf16_ulp(np.maximum(np.abs(want), np.abs(got))) + rel * (np.abs(a) @ np.abs(b).T)
     err = np.abs(got - want)
     assert (err <= bound).all(), f"max err/bound {np.max(err / bound):.3f}"
     return float(np.mean(got == want))
