@@ -941,3 +941,29 @@ def test_gate_layers_equals_gate_per_layer(eg, T, masked):
             want = oracle.gate(want, kvs[l], qs[l], ks[l], mask, eps, clamp, ds)
         err = np.abs(h1.cpu().numpy() - want) / np.maximum(1.0, np.abs(want))
         assert err.max() <= 1e-2, err.max()
+
+
+def test_project_mxfp8_table_past_4gb(eg):
+    # A table of 17,000,000 FP8 rows (4.35 GB) with ids near its end: the row
+    # offsets pass 2^32 bytes, which the gather reaches through 64-bit
+    # addresses.  The oracle gets the touched rows only, with the ids remapped.
+    R, T, cols, N = 17_000_000, 200, 3, 192
+    assert R * 256 > 2**32
+    g = torch.Generator(device="cuda").manual_seed(5)
+    table = torch.randint(0, 0x7E, (R, 256), dtype=torch.uint8, device="cuda", generator=g)
+    scales = torch.randint(119, 128, (R, 8), dtype=torch.uint8, device="cuda", generator=g)
+    rng = np.random.default_rng(6)
+    ids_np = rng.integers(R - 5000, R, (T, cols)).astype(np.int32)
+    ids_np[::7, 0] = rng.integers(0, R, len(ids_np[::7, 0]))       # and some anywhere
+    K = cols * 256
+    wkv_np = oracle.bf16_bits(oracle.bf16_round(0.05 * rng.standard_normal((N, K))))
+    wc, ws = oracle.quantize_mxfp8(wkv_np)
+    kv = torch.full((T, N), 0x7777, dtype=torch.int16, device="cuda")
+    eg.engram_project_mxfp8(table, scales, R, tensor(ids_np, "cuda"), cols, cols,
+                            tensor(wc, "cuda"), tensor(ws, "cuda"), kv, T, N)
+    uniq, inv = np.unique(ids_np, return_inverse=True)
+    sel = torch.from_numpy(uniq.astype(np.int64)).cuda()
+    sub_t, sub_s = table[sel].cpu().numpy(), scales[sel].cpu().numpy()
+    del table, scales
+    a_c, a_s = oracle.rows_fp8_mx(sub_t, sub_s, inv.reshape(T, cols))
+    _check_kv_mx(kv.cpu().numpy().view(np.uint16), a_c, a_s, wc, ws)
