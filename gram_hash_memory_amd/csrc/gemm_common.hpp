@@ -82,25 +82,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
 }
 
-// Epilogue of a 256 x 256 tile computed by 4 waves of 128 x 128 with
-// v_mfma_f32_32x32x16_bf16 (accumulator r of a 32 x 32 block is row
-// 8 * (r / 4) + 4 * (lane / 32) + r % 4, column lane % 32): the bf16 results go
-// through LDS (row-major, 512 B per row) so that global memory sees 16-byte
-// stores of whole row segments instead of 2-byte stores scattered over rows.
-// `smem` needs 128 KB that no wave reads any more; the caller's barrier
-// before this call guarantees that.
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], uint16_t *smem,
-                                           uint16_t *__restrict__ C, int M, int N, int m0,
-                                           int n0, int wm, int wn, int lane, int tid) {
+// Epilogue of a 256 x 256 tile whose waves hold NI x NJ blocks of 32 x 32
+// from v_mfma_f32_32x32x16_bf16 (accumulator r of a block is row
+// 8 * (r / 4) + 4 * (lane / 32) + r % 4, column lane % 32), the wave's blocks
+// starting at tile row row0 and column col0.  The bf16 results go through LDS
+// (row-major, 512 B per row) so that global memory sees 16-byte stores of
+// whole row segments instead of 2-byte stores scattered over rows.  `smem`
+// needs 128 KB that no wave reads any more; the caller's barrier before this
+// call guarantees that.
+template <int NI, int NJ>
+__device__ __forceinline__ void store_tile_blocks(const f32x16 (&acc)[NI][NJ], uint16_t *smem,
+                                                  uint16_t *__restrict__ C, int M, int N,
+                                                  int m0, int n0, int row0, int col0, int lane,
+                                                  int tid) {
   const int frow = lane & 31, fhalf = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
-        smem[row * BN + wn * 128 + j * 32 + frow] = f32_to_bf16(acc[i][j][r]);
+        const int row = row0 + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
+        smem[row * BN + col0 + j * 32 + frow] = f32_to_bf16(acc[i][j][r]);
       }
   __syncthreads();
   const bool vec = (N % 8) == 0;
@@ -116,6 +119,13 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], uint16_t *
       for (int e = 0; e < 8 && gcol + e < N; ++e) dst[e] = src[e];
     }
   }
+}
+
+// The 2 x 2 wave layout of 128 x 128 per wave (wave (wm, wn)).
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], uint16_t *smem,
+                                           uint16_t *__restrict__ C, int M, int N, int m0,
+                                           int n0, int wm, int wn, int lane, int tid) {
+  store_tile_blocks<4, 4>(acc, smem, C, M, N, m0, n0, wm * 128, wn * 128, lane, tid);
 }
 
 }  // namespace gemm

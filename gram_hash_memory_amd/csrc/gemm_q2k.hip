@@ -3,21 +3,27 @@
 // [spark engram_v41 page, overview stages 2-3]: rows are Q2_K blocks of 84
 // bytes per 256 values (ENGRAM_ROW_BYTES), dequantised to bf16 and
 // multiplied by wkv.  Instead of writing the bf16 rows to HBM and reading
-// them back, the projection reads the blocks themselves.  A is then 84 bytes
-// per 256 values instead of 512, which cuts the bytes each workgroup pulls
-// through L2 by about a third; the bf16 values it multiplies are the same
-// ones engram_rows produces, so kv is bit-identical to rows -> project.
+// them back, the projection reads the blocks themselves: A is 84 bytes per
+// 256 values instead of 512.  The bf16 values it multiplies are the ones
+// engram_rows produces, and every output sums the same MFMAs in the same K
+// order as gemm.hip, so kv is bit-identical to rows -> project.
 //
-// Same tiling as gemm.hip (256 x 256 tile, 4 waves of 128 x 128, two LDS
-// stages of BK = 64).  B goes straight from global memory into its LDS stage
-// (buffer_load ... lds, one stage ahead): that drops the VGPR staging, its LDS
-// stores and their waits, which in this kernel cost more than the LDS-DMA
-// path's lower raw rate.  For A, thread t owns tile row t.  The 84-byte block of row t for table column c (K range
-// 256c .. 256c + 255) sits in 21 VGPRs: it is loaded when column c - 1
-// starts, and its id one column earlier still.  Every stage, each thread
-// decodes its row's 64 values straight into the LDS A tile.  A stage spans
-// values 64q .. 64q + 63 of the block; they need the block's 32 quant bytes of
-// half q / 2 at two bit shifts, its 4 scale/min bytes q * 4 .. q * 4 + 3, and d/dmin.
+// Tile 256 x 256, 4 waves, each wave 64 rows x 256 columns (2 x 8 blocks of
+// v_mfma_f32_32x32x16_bf16, accumulators in AGPRs), K in stages of BK = 64.
+//  - B goes straight from global memory into its LDS stage (buffer_load ...
+//    lds, one stage ahead); every wave reads the whole B stage as fragments.
+//  - A never touches LDS.  A wave owns 64 tile rows, so each row is needed by
+//    exactly one wave, and every lane decodes its own A fragments from the
+//    Q2_K block in registers: lane (r, h) of the 32 x 16 fragment holds row r,
+//    values 8h .. 8h + 7 of the 16-value k-step.  Decoding into LDS instead
+//    would add a 32 KB LDS write per stage next to the fragment reads, and LDS
+//    traffic is what bounds this kernel.
+// Per lane and table column (256 values = 4 stages) a row needs the block's
+// 16 scale/min bytes, d/dmin, and 32 of its 64 quant bytes: value v's quant
+// is byte 32 (v / 128) + v % 32 at bit 2 ((v % 128) / 32), and the lane's
+// values (v % 16 in 8h .. 8h + 7) fall in the four 8-byte pieces at quant
+// bytes 16 p + 8 h, p = 0..3.  The blocks of a column are loaded one column
+// ahead; their ids are resolved into byte offsets once, before the K loop.
 #include "gemm_common.hpp"
 
 namespace engram {
@@ -25,20 +31,27 @@ namespace {
 
 using namespace gemm;
 
-constexpr int kBlockDwords = ENGRAM_Q2K_ROW_BYTES / 4;   // 21
 constexpr uint32_t kNoRow = 0x7FFFFFF0u;   // block offset past the table: loads read 0
+constexpr int kRowsPerLane = 2;            // tile rows w * 64 + 32 i + (lane % 32), i = 0, 1
+constexpr int kNJ = BN / 32;               // 8 column blocks per wave
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h16) {
   return float(__builtin_bit_cast(_Float16, uint16_t(h16)));
 }
+
+// The register copy of the block parts one lane needs for one row.
+struct Q2kPart {
+  u32x4 sc;          // scale/min bytes 0..15 (low nibble scale, high nibble min)
+  u32x2 q[4];        // quant bytes 16 p + 8 h .. + 7 of the 64
+  uint32_t dd;       // fp16 d | fp16 dmin << 16
+};
 
 __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
     const uint8_t *__restrict__ table, int64_t num_rows, const int32_t *__restrict__ ids,
     int64_t ids_stride, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
     int M, int N, int K, int tiles_m, int tiles_n, int32_t *__restrict__ bad_ids) {
   constexpr int BK = 64;
-  constexpr int kStageElems = (BM + BN) * BK;
-  constexpr int kChunks = BK / 8;
+  constexpr int kStageElems = BN * BK;                 // B only: 32 KB
   constexpr int kSegs = BN * BK * 2 / 1024 / kWaves;   // 1 KB B segments per wave per stage: 8
   extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
 
@@ -48,7 +61,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int frow = lane & 31, fhalf = lane >> 5;
   const int cols = K / ENGRAM_HEAD_DIM;
   const int nk = K / BK;
 
@@ -66,7 +79,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
   const uint32_t seg_stride = uint32_t(8 * K) * 2;
   auto dma_b = [&](int stage, int slice) {
     const int k0 = min(slice, nk - 1) * BK;
-    uint16_t *sb = smem + stage * kStageElems + BM * BK;
+    uint16_t *sb = smem + stage * kStageElems;
 #pragma unroll
     for (int i = 0; i < kSegs; ++i) {
       const int seg = wave * kSegs + i;
@@ -76,16 +89,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
     }
   };
 
-  // ---- A: the Q2_K block of tile row `tid`, one table column at a time.
-  // The byte offset of every (row, column) block is resolved once, before the
-  // K loop, into LDS behind the two stages (cols <= ENGRAM_Q2K_FUSED_MAX_COLS):
-  // the loop then reads an offset from LDS instead of an id from global
-  // memory, and ids outside the table are counted here, once.
-  const int arow = m0 + tid;
-  const bool row_ok = arow < M;
+  // ---- A: byte offsets of every (row, column) block, in LDS behind the two
+  // B stages (cols <= ENGRAM_Q2K_FUSED_MAX_COLS).  Thread t resolves tile row
+  // t and counts its ids outside the table, once per (token, column).
   const __amdgpu_buffer_rsrc_t rt = make_rsrc(table, num_rows * ENGRAM_Q2K_ROW_BYTES);
   uint32_t *const offs = reinterpret_cast<uint32_t *>(smem + 2 * kStageElems);
   {
+    const int arow = m0 + tid;
+    const bool row_ok = arow < M;
     const int32_t *id_ptr = ids + int64_t(row_ok ? arow : M - 1) * ids_stride;
     int32_t idv[ENGRAM_Q2K_FUSED_MAX_COLS];
 #pragma unroll
@@ -102,108 +113,87 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
     }
     if (bad && tn == 0 && bad_ids) atomicAdd(bad_ids, bad);
   }
-  uint32_t blk[2][kBlockDwords];
+  __syncthreads();                                  // offsets of other lanes' rows
+
+  Q2kPart blk[2][kRowsPerLane];
   auto load_block = [&](int set, int col) {
-    const uint32_t off = offs[min(col, cols - 1) * kThreads + tid];
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      const u32x4 v = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, off + 16 * i, 0, 0));
+    for (int i = 0; i < kRowsPerLane; ++i) {
+      const uint32_t off = offs[min(col, cols - 1) * kThreads + wave * 64 + 32 * i + frow];
+      blk[set][i].sc = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) blk[set][4 * i + e] = v[e];
+      for (int p = 0; p < 4; ++p)
+        blk[set][i].q[p] = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rt, off + 16 + 16 * p + 8 * fhalf, 0, 0));
+      blk[set][i].dd = __builtin_amdgcn_raw_buffer_load_b32(rt, off + 80, 0, 0);
     }
-    blk[set][20] = __builtin_amdgcn_raw_buffer_load_b32(rt, off + 80, 0, 0);
   };
-  // Values 64q .. 64q + 63 of the block in register set `set` -> LDS A tile of `stage`.
-  //
-  // Inside a 16-value group the scale and min are fixed, so a value takes one
-  // of only four bf16 results, bf16(q * dl - ml) for q = 0..3.  They are
-  // computed once per group (in fp32, with the same fma and rounding as
-  // engram_rows) and kept as two byte planes, lo = the four low bytes and
-  // hi = the four high bytes.  Every output pair is then one v_perm_b32 of
-  // (hi, lo) whose selector bytes are q_a, q_a + 4, q_b, q_b + 4, and the
-  // selectors of four values are two more v_perm_b32 of (m | 0x04040404, m),
-  // m being their four 2-bit quants, one per byte.
-  // Groups g0 .. g1 - 1 of the four 16-value groups of the stage.
-  auto decode_a = [&](int set, const int q, int stage, const int g0, const int g1) {
-    uint16_t *sa = smem + stage * kStageElems;
-    const uint32_t scw = blk[set][q];                    // scale/min bytes 4q .. 4q + 3
-    const float d = half_bits_to_float(blk[set][20] & 0xFFFFu);
-    const float dmin = half_bits_to_float(blk[set][20] >> 16);
-    const int h = q >> 1, s0 = 4 * (q & 1);
+
+  // A fragments of k-step ks of stage qs (values 64 qs + 16 ks .. + 15 of the
+  // block) from register set `set`.  Inside that 16-value group the scale and
+  // min are fixed, so a value takes one of only four bf16 results,
+  // bf16(q * dl - ml) for q = 0..3.  They are computed once (in fp32, with the
+  // same fma and rounding as engram_rows) and kept as two byte planes, lo = the
+  // four low bytes and hi = the four high bytes.  Every output pair is then one
+  // v_perm_b32 of (hi, lo) whose selector bytes are q_a, q_a + 4, q_b, q_b + 4,
+  // and the selectors of four values are two more v_perm_b32 of
+  // (m | 0x04040404, m), m being their four 2-bit quants, one per byte.
+  bf16x8 fa[2][kRowsPerLane], fb[2][kNJ];
+  auto decode_a = [&](int set, const int qs, const int ks, int slot) {
+    const int p = 2 * (qs >> 1) + (ks & 1);
+    const int shift = 4 * (qs & 1) + 2 * (ks >> 1);
 #pragma unroll
-    for (int g = g0; g < g1; ++g) {                      // 16-value group inside the stage
-      const uint32_t sm = (scw >> (8 * g)) & 0xFFu;
+    for (int i = 0; i < kRowsPerLane; ++i) {
+      const Q2kPart &b = blk[set][i];
+      const float d = half_bits_to_float(b.dd & 0xFFFFu);
+      const float dmin = half_bits_to_float(b.dd >> 16);
+      const uint32_t sm = (b.sc[qs] >> (8 * ks)) & 0xFFu;
       const float dl = d * float(sm & 0xFu), ml = dmin * float(sm >> 4);
       const uint32_t p01 = pack_bf16x2(fmaf(0.0f, dl, -ml), fmaf(1.0f, dl, -ml));
       const uint32_t p23 = pack_bf16x2(fmaf(2.0f, dl, -ml), fmaf(3.0f, dl, -ml));
       const uint32_t lo = __builtin_amdgcn_perm(p23, p01, 0x06040200u);
       const uint32_t hi = __builtin_amdgcn_perm(p23, p01, 0x07050301u);
+      u32x4 v;
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {                   // 8-value chunk c of the stage
-        const int c = 2 * g + cc;
-        const int shift = s0 + 2 * (c >> 2);
-        u32x4 v;
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {                    // 4 quants per dword
-          const uint32_t m = (blk[set][4 + 8 * h + 2 * (c & 3) + w] >> shift) & 0x03030303u;
-          const uint32_t m4 = m | 0x04040404u;
-          v[2 * w] = __builtin_amdgcn_perm(hi, lo, __builtin_amdgcn_perm(m4, m, 0x05010400u));
-          v[2 * w + 1] = __builtin_amdgcn_perm(hi, lo, __builtin_amdgcn_perm(m4, m, 0x07030602u));
-        }
-        *reinterpret_cast<u32x4 *>(sa + swz<BK>(tid, c)) = v;
+      for (int w = 0; w < 2; ++w) {                      // 4 quants per dword
+        const uint32_t m = (b.q[p][w] >> shift) & 0x03030303u;
+        const uint32_t m4 = m | 0x04040404u;
+        v[2 * w] = __builtin_amdgcn_perm(hi, lo, __builtin_amdgcn_perm(m4, m, 0x05010400u));
+        v[2 * w + 1] = __builtin_amdgcn_perm(hi, lo, __builtin_amdgcn_perm(m4, m, 0x07030602u));
       }
+      fa[slot][i] = __builtin_bit_cast(bf16x8, v);
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[kRowsPerLane][kNJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kRowsPerLane; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < kNJ; ++j) acc[i][j] = f32x16{};
 
-  const int frow = lane & 31, fhalf = lane >> 5;
-  bf16x8 fa[2][4], fb[2][4];
-  auto load_frags = [&](int stage, int ks, int slot) {
-    const uint16_t *sa = smem + stage * kStageElems;
-    const uint16_t *sb = sa + BM * BK;
+  auto load_b = [&](int stage, int ks, int slot) {
+    const uint16_t *sb = smem + stage * kStageElems;
     const int chunk = 2 * ks + fhalf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      fa[slot][i] =
-          *reinterpret_cast<const bf16x8 *>(sa + swz<BK>(wm * 128 + i * 32 + frow, chunk));
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      fb[slot][j] =
-          *reinterpret_cast<const bf16x8 *>(sb + swz<BK>(wn * 128 + j * 32 + frow, chunk));
+    for (int j = 0; j < kNJ; ++j)
+      fb[slot][j] = *reinterpret_cast<const bf16x8 *>(sb + swz<BK>(j * 32 + frow, chunk));
   };
   auto mfma_block = [&](int slot) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kRowsPerLane; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < kNJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j],
                                                             acc[i][j], 0, 0, 0);
   };
-  auto sched_reads = [&]() {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
-    }
-  };
-  // A sub-step that also decodes half a stage of A (about 85 VALU ops and 4
-  // LDS writes): a wave issues one instruction per cycle, so the VALU work is
-  // spread between the MFMAs, each of which keeps the matrix core busy for
-  // 32 cycles while the next few VALU ops issue.  Bunched up, it would leave
-  // the matrix core idle for the whole burst.
-  auto sched_reads_decode = [&]() {
+  // One k-step: 16 MFMAs (32 cycles of matrix core each), the next step's 8
+  // B fragment reads and its A decode (about 56 VALU ops) spread between them.
+  auto sched_step = [&]() {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       if (r % 2 == 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
-      if (r % 4 == 3) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
     }
   };
 
@@ -211,69 +201,77 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
   // every wave finished reading before the previous barrier; j = kt % 8 fixes
   // the register sets at compile time:
   //  - B slice kt + 1 is requested into its LDS stage first thing;
-  //  - A stage kt + 1 is column (kt + 1) / 4, quarter (kt + 1) % 4, decoded
-  //    from block set ((kt + 1) / 4) % 2;
-  //  - when kt % 4 == 0 (column m = kt / 4 starts), the block of column m + 1
-  //    is requested, after the B segments (6 loads);
-  //  - before the barrier, vmcnt lets only those 6 block loads stay in
+  //  - the MFMAs of stage kt are column kt / 4, quarter kt % 4, from block set
+  //    (kt / 4) % 2;
+  //  - when kt % 4 == 0 (column kt / 4 starts), the blocks of column kt / 4 + 1
+  //    are requested into the other set, after the B segments (12 loads);
+  //  - before the barrier, vmcnt lets only those 12 block loads stay in
   //    flight: the B segments (older) have then landed in LDS.
+  // `prefetch` is false for the last column: nothing would use those blocks,
+  // the compiler drops loads whose results are dead, and a vmcnt that counts
+  // them would then let the B segments stay in flight, so that iteration
+  // waits for everything.
   // Scheduling fences around the loads keep them at the top of the iteration
   // (the compiler would otherwise sink them towards their first use, which
   // shortens the prefetch distance), and keep work of a later iteration (such
   // as the fp16 d of a block still in flight) from being hoisted into this
   // one, where it would wait for the load.
-  auto iteration = [&](int kt, const int j) {
+  auto iteration = [&](int kt, const int j, const bool prefetch) {
     const int stage = j & 1;                         // kt % 2
+    const int set = (j >> 2) & 1, qs = j & 3;
     __builtin_amdgcn_sched_barrier(0);
     dma_b(stage ^ 1, kt + 1);
-    if (j % 4 == 0) load_block(((j / 4) + 1) & 1, kt / 4 + 1);
+    if (qs == 0 && prefetch) load_block(set ^ 1, kt / 4 + 1);
     __builtin_amdgcn_sched_barrier(0);
-    load_frags(stage, 1, 1);
+    load_b(stage, 1, 1);
+    decode_a(set, qs, 1, 1);
     mfma_block(0);
-    decode_a(((j + 1) / 4) & 1, (j + 1) % 4, stage ^ 1, 0, 2);
-    sched_reads_decode();
-    load_frags(stage, 2, 0);
+    sched_step();
+    load_b(stage, 2, 0);
+    decode_a(set, qs, 2, 0);
     mfma_block(1);
-    decode_a(((j + 1) / 4) & 1, (j + 1) % 4, stage ^ 1, 2, 4);
-    sched_reads_decode();
-    load_frags(stage, 3, 1);
+    sched_step();
+    load_b(stage, 3, 1);
+    decode_a(set, qs, 3, 1);
     mfma_block(0);
-    sched_reads();
-    if (j % 4 == 0) stage_barrier<waitcnt(6, 0)>();
+    sched_step();
+    if (qs == 0 && prefetch) stage_barrier<waitcnt(6 * kRowsPerLane, 0)>();
     else stage_barrier<waitcnt(0, 0)>();
-    load_frags(stage ^ 1, 0, 0);
+    load_b(stage ^ 1, 0, 0);
+    decode_a(((j + 1) >> 2) & 1, (j + 1) & 3, 0, 0);
     mfma_block(1);
-    sched_reads();
+    sched_step();
   };
 
-  // Prologue: stage 0 gets B slice 0 and A quarter 0 of column 0.  (Iteration
-  // 0 then requests B slice 1 and the block of column 1.)
+  // Prologue: stage 0 gets B slice 0, the lanes the blocks of column 0 and
+  // the fragments of k-step 0.  (Iteration 0 then requests B slice 1 and the
+  // blocks of column 1.)
   load_block(0, 0);
   dma_b(0, 0);
-  decode_a(0, 0, 0, 0, 4);
   stage_barrier<waitcnt(0, 0)>();
-  load_frags(0, 0, 0);
+  load_b(0, 0, 0);
+  decode_a(0, 0, 0, 0);
 
   int kt = 0;
   for (; kt + 7 < nk; kt += 8) {
-    iteration(kt + 0, 0);
-    iteration(kt + 1, 1);
-    iteration(kt + 2, 2);
-    iteration(kt + 3, 3);
-    iteration(kt + 4, 4);
-    iteration(kt + 5, 5);
-    iteration(kt + 6, 6);
-    iteration(kt + 7, 7);
+    iteration(kt + 0, 0, true);
+    iteration(kt + 1, 1, true);
+    iteration(kt + 2, 2, true);
+    iteration(kt + 3, 3, true);
+    iteration(kt + 4, 4, true);
+    iteration(kt + 5, 5, true);
+    iteration(kt + 6, 6, true);
+    iteration(kt + 7, 7, true);
   }
-  if (kt < nk) {                                   // nk % 8 == 4 (K is a multiple of 256)
-    iteration(kt + 0, 0);
-    iteration(kt + 1, 1);
-    iteration(kt + 2, 2);
-    iteration(kt + 3, 3);
+  if (kt < nk) {              // nk % 8 == 4 (K is a multiple of 256): the last column
+    iteration(kt + 0, 0, false);
+    iteration(kt + 1, 1, false);
+    iteration(kt + 2, 2, false);
+    iteration(kt + 3, 3, false);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
   __syncthreads();                                 // every wave is done with the stages
-  store_tile(acc, smem, C, M, N, m0, n0, wm, wn, lane, tid);
+  store_tile_blocks<kRowsPerLane, kNJ>(acc, smem, C, M, N, m0, n0, wave * 64, 0, lane, tid);
 }
 
 }  // namespace
@@ -292,8 +290,10 @@ hipError_t launch_project_q2k(const uint8_t *table, int64_t num_rows, const int3
                               hipStream_t stream) {
   const int K = cols * ENGRAM_HEAD_DIM;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const size_t lds = size_t(2) * (BM + BN) * 64 * sizeof(uint16_t) +
-                    size_t(cols) * kThreads * sizeof(uint32_t);
+  const size_t lds_loop = size_t(2) * BN * 64 * sizeof(uint16_t) +
+                         size_t(cols) * kThreads * sizeof(uint32_t);
+  const size_t lds_epilogue = size_t(BM) * BN * sizeof(uint16_t);
+  const size_t lds = lds_loop > lds_epilogue ? lds_loop : lds_epilogue;
   const void *fn = reinterpret_cast<const void *>(&gemm_q2k_kernel);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
