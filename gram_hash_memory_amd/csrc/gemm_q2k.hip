@@ -178,11 +178,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
     for (int j = 0; j < kNJ; ++j)
       fb[slot][j] = *reinterpret_cast<const bf16x8 *>(sb + swz<BK>(j * 32 + frow, chunk));
   };
+  // Column-block-major: B fragment j, read during the previous k-step in
+  // order j, is first used 2 j MFMAs into this one, so every read gets the
+  // same 16-MFMA lead (row-major order would give fragment 7 only 9).
   auto mfma_block = [&](int slot) {
 #pragma unroll
-    for (int i = 0; i < kRowsPerLane; ++i)
+    for (int j = 0; j < kNJ; ++j)
 #pragma unroll
-      for (int j = 0; j < kNJ; ++j)
+      for (int i = 0; i < kRowsPerLane; ++i)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j],
                                                             acc[i][j], 0, 0, 0);
   };
