@@ -206,9 +206,11 @@ def main() -> int:
     kvs = [kv] + [torch.empty_like(kv) for _ in range(len(s.layer_ids) - 1)]
     side = torch.cuda.Stream() if overlap else None
     num_rows = [l.table.numel() // (84 if fmt == eg.ENGRAM_ROWS_Q2K else 256) for l in dw.layers]
-    # The fused Q2_K rows+projection kernel, as engram_forward picks it (more
-    # than SKINNY_MAX_TOKENS tokens, table and columns within its limits).
-    fused = (fmt == eg.ENGRAM_ROWS_Q2K and s.T > SKINNY_MAX_TOKENS and s.cols <= 32 and
+    # The fused Q2_K rows+projection, as engram_forward picks it: table and
+    # columns within its limits, and either more than SKINNY_MAX_TOKENS tokens
+    # (256 x 256 tiles) or K quarters of whole table columns (weight streaming).
+    fused = (fmt == eg.ENGRAM_ROWS_Q2K and s.cols <= 32 and
+             (s.T > SKINNY_MAX_TOKENS or s.cols % 4 == 0) and
              all(n * 84 <= Q2K_FUSED_MAX_BYTES for n in num_rows))
 
     def layer_ids(l):
@@ -374,12 +376,19 @@ def main() -> int:
     skinny = s.T <= SKINNY_MAX_TOKENS and not mx
     if skinny:
         # Few tokens: the projection streams wkv once and is bound by HBM.
-        dom_kernel = "gemm_skinny_kernel (engram_project, T <= 128)"
-        dom_bytes = 2.0 * (s.N * s.K + s.T * s.K + s.T * s.N)
+        # Fused, it reads the tokens' Q2_K blocks and ids instead of bf16 rows.
+        if fused:
+            dom_kernel = "gemm_skinny_q2k_kernel (engram_project_q2k, T <= 128)"
+            dom_bytes = 2.0 * s.N * s.K + s.T * s.cols * (84 + 4) + 2.0 * s.T * s.N
+            dom_prof = "gemm_skinny_q2k"
+        else:
+            dom_kernel = "gemm_skinny_kernel (engram_project, T <= 128)"
+            dom_bytes = 2.0 * (s.N * s.K + s.T * s.K + s.T * s.N)
+            dom_prof = "gemm_skinny"
         dom_gbs = gbs(dom_bytes, per_launch_ms[dom_name])
         roofline = {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                    "traffic": prof("gemm_skinny"),
+                    "traffic": prof(dom_prof),
                     "bytes_per_launch": dom_bytes}
     else:
         roofline = {"bound": "mfma", "achieved": round(dom_tf, 1), "peak": dom_peak,
@@ -391,7 +400,12 @@ def main() -> int:
                  "hbm_gbs": round(gbs(alg["hash"], per_launch_ms["hash"]), 1),
                  "traffic": prof("hash")},
     }
-    if fused or mx:
+    if (fused or mx) and skinny:
+        stages["rows_project"] = {
+            "ms": round(per_launch_ms["rows_project"], 4), "bound": "hbm",
+            "achieved_gbs": round(dom_gbs, 1), "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": dom_bytes, "traffic": prof(dom_prof)}
+    elif fused or mx:
         stages["rows_project"] = {
             "ms": round(per_launch_ms["rows_project"], 4), "bound": "mfma",
             "achieved_tflops": round(dom_tf, 1), "frac": round(dom_tf / dom_peak, 4),

@@ -403,8 +403,9 @@ engram_status engram_forward(const engram_hash_params *params, const engram_toke
     gl.kv[l] = kv;
     gl.qw[l] = ly.q_weight;
     gl.kw[l] = ly.k_weight;
-    // Few tokens: rows -> the weight-streaming projection beats the fused
-    // 256 x 256 tiles (the dequant is then a few microseconds).
+    // Q2_K: the fused rows + projection (its weight-streaming form for few
+    // tokens).  Few tokens with cols % 4 != 0: rows -> the weight-streaming
+    // projection, which beats the fused 256 x 256 tiles there.
     if (ly.wkv_mx) {
       if ((st = hip_status(engram::launch_project_mx(ly.table, ly.scales, ly.num_rows,
                                                      ids + l * cols, int64_t(L) * cols, cols,
@@ -412,8 +413,9 @@ engram_status engram_forward(const engram_hash_params *params, const engram_toke
                                                      bad_ids, stream),
                            "MXFP8 rows+project launch")) != ENGRAM_OK)
         return st;
-    } else if (ly.fmt == ENGRAM_ROWS_Q2K && !engram::project_uses_skinny(T) &&
-               engram::project_q2k_supported(ly.num_rows, cols)) {
+    } else if (ly.fmt == ENGRAM_ROWS_Q2K && engram::project_q2k_supported(ly.num_rows, cols) &&
+               (!engram::project_uses_skinny(T) ||
+                engram::project_q2k_skinny_supported(T, cols))) {
       if ((st = hip_status(engram::launch_project_q2k(ly.table, ly.num_rows, ids + l * cols,
                                                       int64_t(L) * cols, cols, ly.wkv, kv, T,
                                                       N, bad_ids, stream),

@@ -67,7 +67,14 @@ hipError_t launch_project_skinny(const uint16_t *a, const uint16_t *w, uint16_t 
                                  int32_t K, int32_t N, hipStream_t stream);
 
 // Rows + projection fused for Q2_K tables (kv bit-identical to rows -> project).
+// launch_project_q2k runs the weight-streaming form (gemm_skinny.hip) where
+// project_q2k_skinny_supported holds, the 256 x 256 tiles otherwise.
 bool project_q2k_supported(int64_t num_rows, int32_t cols);
+bool project_q2k_skinny_supported(int32_t M, int32_t cols);
+hipError_t launch_project_q2k_skinny(const uint8_t *table, int64_t num_rows, const int32_t *ids,
+                                     int64_t ids_token_stride, int32_t cols, const uint16_t *w,
+                                     uint16_t *c, int32_t M, int32_t N, int32_t *bad_ids,
+                                     hipStream_t stream);
 hipError_t launch_project_q2k(const uint8_t *table, int64_t num_rows, const int32_t *ids,
                               int64_t ids_token_stride, int32_t cols, const uint16_t *w,
                               uint16_t *c, int32_t M, int32_t N, int32_t *bad_ids,

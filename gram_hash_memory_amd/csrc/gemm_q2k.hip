@@ -291,6 +291,9 @@ hipError_t launch_project_q2k(const uint8_t *table, int64_t num_rows, const int3
                               int64_t ids_token_stride, int32_t cols, const uint16_t *w,
                               uint16_t *c, int32_t M, int32_t N, int32_t *bad_ids,
                               hipStream_t stream) {
+  if (project_q2k_skinny_supported(M, cols))
+    return launch_project_q2k_skinny(table, num_rows, ids, ids_token_stride, cols, w, c, M, N,
+                                     bad_ids, stream);
   const int K = cols * ENGRAM_HEAD_DIM;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const size_t lds_loop = size_t(2) * BN * 64 * sizeof(uint16_t) +

@@ -146,22 +146,238 @@ hipError_t launch_nsub(const uint16_t *a, const uint16_t *w, uint16_t *c, int32_
   return hipGetLastError();
 }
 
+// Stages 2 + 3 fused for few tokens and a Q2_K table ([spark engram_v41
+// page, overview stages 2-3]): the kernel above with A decoded on chip from
+// the tokens' 84-byte blocks instead of read as bf16 rows.  A workgroup then
+// pulls 64 * cols * 84 bytes of blocks from L2 instead of 64 * cols * 512
+// bytes of rows, and the rows never go to memory.  Same K quarters, same
+// MFMAs in the same order, same reduction: kv is bit-identical to
+// engram_rows followed by the kernel above.  The quarters must be whole
+// table columns (cols % 4 == 0).
+//
+// Lane (r, g) of a 16 x 32 A fragment holds token 16 i + r, values
+// 32 s + 8 g .. + 7 of the column (s = step in the column, 0..7).  Those sit
+// in 16-value group 2 s + g / 2 (scale/min byte of that index) and their
+// quants in bytes 32 (s / 4) + 8 g .. + 7 of the 64 at bit 2 (s % 4).  So per
+// token and column a lane keeps 16 quant bytes, the 16 scale/min bytes and
+// d/dmin (9 dwords), loaded one column ahead; the byte offsets of all the
+// workgroup's blocks are resolved into LDS first.
+constexpr uint32_t kQ2kNoRow = 0x7FFFFFF0u;   // block offset past the table: loads read 0
+
+struct Q2kLaneBlock {
+  u32x4 sc;          // scale/min bytes 0..15
+  u32x2 q[2];        // quant bytes 8 g .. 8 g + 7 and 32 + 8 g .. 32 + 8 g + 7
+  uint32_t dd;       // fp16 d | fp16 dmin << 16
+};
+
+template <int NSUB, int P>
+__global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
+    const uint8_t *__restrict__ table, int64_t num_rows, const int32_t *__restrict__ ids,
+    int64_t ids_stride, const uint16_t *__restrict__ B, uint16_t *__restrict__ C, int M, int N,
+    int K, int32_t *__restrict__ bad_ids) {
+  constexpr int NT = 16 * NSUB;
+  constexpr int RS = red_stride<NSUB>();
+  // [waves][64][RS] partial sums, then the block offsets [cols][64]
+  extern __shared__ __attribute__((aligned(16))) float red[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * NT;
+  const int m0 = blockIdx.y * kSkinnyM;
+  const int mrows = min(kSkinnyM, M - m0);
+  const int cols = K / ENGRAM_HEAD_DIM;
+  const int wcols = cols / kSkinnyWaves;             // table columns of this wave's quarter
+  const int c0 = wave * wcols;
+  const int kbeg = c0 * ENGRAM_HEAD_DIM;
+  const int nsteps = wcols * (ENGRAM_HEAD_DIM / 32);
+
+  // Block offsets; ids outside the table are counted once per (token,
+  // column), by the first column tile.
+  uint32_t *const offs = reinterpret_cast<uint32_t *>(red + kSkinnyWaves * kSkinnyM * RS);
+  {
+    const int t = tid & 63;
+    const bool row_ok = t < mrows;
+    int bad = 0;
+    for (int c = tid >> 6; c < cols; c += kSkinnyWaves) {
+      const int32_t id = row_ok ? ids[int64_t(m0 + t) * ids_stride + c] : 0;
+      const bool ok = id >= 0 && id < num_rows;
+      bad += row_ok && !ok;
+      offs[c * kSkinnyM + t] = row_ok && ok ? uint32_t(id) * ENGRAM_Q2K_ROW_BYTES : kQ2kNoRow;
+    }
+    if (bad && blockIdx.x == 0 && bad_ids) atomicAdd(bad_ids, bad);
+  }
+  __syncthreads();
+
+  const __amdgpu_buffer_rsrc_t rt = make_rsrc(table, num_rows * ENGRAM_Q2K_ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + int64_t(n0) * K, int64_t(N - n0) * K * 2);
+  const int r = lane & 15, kg = lane >> 4;
+  const uint32_t voff = uint32_t(r * K + 8 * kg) * 2;
+  const uint32_t sub_step = uint32_t(16 * K) * 2;       // 16 rows further
+
+  u32x4 fb[P][NSUB];
+  auto load_b = [&](const int slot, int step) {
+    const int k0 = kbeg + min(step, nsteps - 1) * 32;
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j)
+      fb[slot][j] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, voff + j * sub_step, k0 * 2, 0));
+  };
+  Q2kLaneBlock blk[2][4];
+  auto load_blocks = [&](const int set, int c) {          // wave-local column c (clamped)
+    const uint32_t *o = offs + (c0 + min(c, wcols - 1)) * kSkinnyM + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = o[16 * i];
+      blk[set][i].sc = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0));
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        blk[set][i].q[h] = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rt, off + 16 + 32 * h + 8 * kg, 0, 0));
+      blk[set][i].dd = __builtin_amdgcn_raw_buffer_load_b32(rt, off + 80, 0, 0);
+    }
+  };
+  // A fragments of step s of the column from register set `set`.  Per
+  // 16-value group the four possible results bf16(q * dl - ml), q = 0..3, are
+  // computed once (same fma and rounding as engram_rows) and split into a
+  // low-byte and a high-byte plane; each output pair is one v_perm_b32 of the
+  // planes, with selector bytes q_a, q_a + 4, q_b, q_b + 4 made by two more
+  // v_perm_b32 of the 2-bit quants.
+  const int sc_shift = 8 * (kg >> 1);
+  auto decode = [&](const int set, const int s, u32x4 (&fa)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const Q2kLaneBlock &b = blk[set][i];
+      const float d = float(__builtin_bit_cast(_Float16, uint16_t(b.dd & 0xFFFFu)));
+      const float dmin = float(__builtin_bit_cast(_Float16, uint16_t(b.dd >> 16)));
+      const uint32_t sm = (b.sc[s >> 1] >> (16 * (s & 1) + sc_shift)) & 0xFFu;
+      const float dl = d * float(sm & 0xFu), ml = dmin * float(sm >> 4);
+      const uint32_t p01 = pack_bf16x2(fmaf(0.0f, dl, -ml), fmaf(1.0f, dl, -ml));
+      const uint32_t p23 = pack_bf16x2(fmaf(2.0f, dl, -ml), fmaf(3.0f, dl, -ml));
+      const uint32_t lo = __builtin_amdgcn_perm(p23, p01, 0x06040200u);
+      const uint32_t hi = __builtin_amdgcn_perm(p23, p01, 0x07050301u);
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const uint32_t m = (b.q[s >> 2][w] >> (2 * (s & 3))) & 0x03030303u;
+        const uint32_t m4 = m | 0x04040404u;
+        fa[i][2 * w] = __builtin_amdgcn_perm(hi, lo, __builtin_amdgcn_perm(m4, m, 0x05010400u));
+        fa[i][2 * w + 1] = __builtin_amdgcn_perm(hi, lo, __builtin_amdgcn_perm(m4, m, 0x07030602u));
+      }
+    }
+  };
+  f32x4v acc[4][NSUB];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) acc[i][j] = f32x4v{};
+  // One table column: its 8 steps, B of step t + P - 1 requested while step t
+  // multiplies (step t's B sits in slot t % P), and the blocks of the next
+  // column requested at its start.
+  auto column = [&](int c, const int set) {
+    load_blocks(set ^ 1, c + 1);
+#pragma unroll
+    for (int s = 0; s < ENGRAM_HEAD_DIM / 32; ++s) {
+      const int t = c * (ENGRAM_HEAD_DIM / 32) + s;
+      load_b((s + P - 1) % P, t + P - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      u32x4 fa[4];
+      decode(set, s, fa);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NSUB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, fa[i]), __builtin_bit_cast(bf16x8, fb[s % P][j]),
+              acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  load_blocks(0, 0);
+#pragma unroll
+  for (int p = 0; p < P - 1; ++p) load_b(p, p);
+  for (int c = 0; c < wcols; c += 2) {
+    column(c, 0);
+    if (c + 1 < wcols) column(c + 1, 1);
+  }
+
+  // Partial sums -> LDS, then the four quarters added in wave order.
+  float *mine = red + wave * kSkinnyM * RS;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        mine[(16 * i + 4 * kg + e) * RS + 16 * j + r] = acc[i][j][e];
+  __syncthreads();
+  for (int idx = tid; idx < kSkinnyM * NT; idx += kSkinnyWaves * 64) {
+    const int m = idx / NT, n = idx % NT;
+    float sum = red[m * RS + n];
+#pragma unroll
+    for (int w = 1; w < kSkinnyWaves; ++w) sum += red[(w * kSkinnyM + m) * RS + n];
+    if (m < mrows && n0 + n < N) C[int64_t(m0 + m) * N + n0 + n] = f32_to_bf16(sum);
+  }
+}
+
+template <int NSUB>
+hipError_t launch_q2k_nsub(const uint8_t *table, int64_t num_rows, const int32_t *ids,
+                           int64_t ids_stride, const uint16_t *w, uint16_t *c, int32_t M,
+                           int32_t K, int32_t N, int32_t *bad_ids, hipStream_t stream) {
+  constexpr int P = 4;
+  const int cols = K / ENGRAM_HEAD_DIM;
+  const size_t lds = size_t(kSkinnyWaves) * kSkinnyM * red_stride<NSUB>() * sizeof(float) +
+                     size_t(cols) * kSkinnyM * sizeof(uint32_t);
+  const void *fn = reinterpret_cast<const void *>(&gemm_skinny_q2k_kernel<NSUB, P>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (e != hipSuccess) return e;
+  const dim3 grid((N + 16 * NSUB - 1) / (16 * NSUB), (M + kSkinnyM - 1) / kSkinnyM);
+  hipLaunchKernelGGL((gemm_skinny_q2k_kernel<NSUB, P>), grid, dim3(kSkinnyWaves * 64), lds,
+                     stream, table, num_rows, ids, ids_stride, w, c, M, N, K, bad_ids);
+  return hipGetLastError();
+}
+
+int skinny_nsub(int32_t N) {
+  // Column tiles of 16 * NSUB, NSUB as small as lets about one tile per CU
+  // cover N (the wkv stream is what bounds the kernel).
+  const int64_t per_cu = (int64_t(N) + 255) / 256;
+  return int(std::min<int64_t>(5, std::max<int64_t>(1, (per_cu + 15) / 16)));
+}
+
 }  // namespace
 
 bool project_uses_skinny(int32_t M) { return M <= kSkinnyMaxTokens; }
 
 hipError_t launch_project_skinny(const uint16_t *a, const uint16_t *w, uint16_t *c, int32_t M,
                                  int32_t K, int32_t N, hipStream_t stream) {
-  // Column tiles of 16 * NSUB, NSUB as small as lets about one tile per CU
-  // cover N (the wkv stream is what bounds the kernel).
-  const int64_t per_cu = (int64_t(N) + 255) / 256;
-  const int nsub = int(std::min<int64_t>(5, std::max<int64_t>(1, (per_cu + 15) / 16)));
-  switch (nsub) {
+  switch (skinny_nsub(N)) {
     case 1: return launch_nsub<1>(a, w, c, M, K, N, stream);
     case 2: return launch_nsub<2>(a, w, c, M, K, N, stream);
     case 3: return launch_nsub<3>(a, w, c, M, K, N, stream);
     case 4: return launch_nsub<4>(a, w, c, M, K, N, stream);
     default: return launch_nsub<5>(a, w, c, M, K, N, stream);
+  }
+}
+
+}  // namespace engram
+
+namespace engram {
+
+bool project_q2k_skinny_supported(int32_t M, int32_t cols) {
+  return project_uses_skinny(M) && cols % kSkinnyWaves == 0;
+}
+
+hipError_t launch_project_q2k_skinny(const uint8_t *table, int64_t num_rows, const int32_t *ids,
+                                     int64_t ids_token_stride, int32_t cols, const uint16_t *w,
+                                     uint16_t *c, int32_t M, int32_t N, int32_t *bad_ids,
+                                     hipStream_t stream) {
+  const int32_t K = cols * ENGRAM_HEAD_DIM;
+  switch (skinny_nsub(N)) {
+    case 1: return launch_q2k_nsub<1>(table, num_rows, ids, ids_token_stride, w, c, M, K, N, bad_ids, stream);
+    case 2: return launch_q2k_nsub<2>(table, num_rows, ids, ids_token_stride, w, c, M, K, N, bad_ids, stream);
+    case 3: return launch_q2k_nsub<3>(table, num_rows, ids, ids_token_stride, w, c, M, K, N, bad_ids, stream);
+    case 4: return launch_q2k_nsub<4>(table, num_rows, ids, ids_token_stride, w, c, M, K, N, bad_ids, stream);
+    default: return launch_q2k_nsub<5>(table, num_rows, ids, ids_token_stride, w, c, M, K, N, bad_ids, stream);
   }
 }
 

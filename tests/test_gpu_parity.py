@@ -221,12 +221,19 @@ Q2K_CONFIGS = [c for c in CONFIGS if workloads.SPECS[c].fmt == "q2k"]
 SKINNY_MAX_TOKENS = 128     # engram_project streams wkv for at most this many tokens
 
 
+def q2k_same_order(T, cols):
+    # engram_project_q2k sums in engram_project's order: with the 256 x 256
+    # tiles above SKINNY_MAX_TOKENS, and with the weight-streaming kernel's K
+    # quarters at or below it when they are whole table columns.
+    return T > SKINNY_MAX_TOKENS or cols % 4 == 0
+
+
 @pytest.mark.parametrize("c", Q2K_CONFIGS)
 def test_project_q2k_bit_identical_to_rows_then_project(eg, c):
     # Same bf16 operands, same MFMA order: the fused kernel's kv must equal the
     # two-kernel path's bit for bit on the whole output, at the full size --
-    # where engram_project uses the same 256 x 256 tiles (more than 128
-    # tokens); with fewer it sums in another order, and both meet the bound.
+    # with the 256 x 256 tiles (more than 128 tokens) and with the
+    # weight-streaming form (the decode workload: 64 tokens, 24 columns).
     wl = host(c)
     s = wl.spec
     for layer in range(len(s.layer_ids)):
@@ -239,7 +246,7 @@ def test_project_q2k_bit_identical_to_rows_then_project(eg, c):
         eg.engram_project_q2k(L.table, L.table.numel() // 84, ids.view(-1)[layer * s.cols:],
                               len(s.layer_ids) * s.cols, s.cols, L.wkv, kv, s.T, s.N, bad)
         assert bad.item() == 0
-        if s.T > SKINNY_MAX_TOKENS:
+        if q2k_same_order(s.T, s.cols):
             diff = int((kv != kv_two).sum().item())
             assert diff == 0, f"layer {layer}: {diff} kv values differ"
         pick = sample_tokens(wl)
@@ -248,11 +255,15 @@ def test_project_q2k_bit_identical_to_rows_then_project(eg, c):
 
 
 @pytest.mark.parametrize("T,cols,N", [(1, 1, 64), (3, 3, 320), (255, 5, 520), (257, 6, 256),
-                                      (300, 24, 4096), (513, 2, 1000)])
+                                      (300, 24, 4096), (513, 2, 1000),
+                                      (1, 4, 64), (64, 8, 1000), (100, 4, 520), (128, 12, 4096),
+                                      (37, 32, 300), (129, 8, 256)])
 def test_project_q2k_ragged_and_bad_ids(eg, T, cols, N):
-    # Ragged tiles in M and N, an odd column count (the kernel's half-unrolled
-    # tail), and ids outside the table: zero rows, counted once per (token,
-    # column) -- exactly as engram_rows does.
+    # Ragged tiles in M and N, an odd column count (the 256 x 256 kernel's
+    # half-unrolled tail), few tokens with whole-column K quarters (the
+    # weight-streaming form, one or several columns per quarter, an odd
+    # number included), and ids outside the table: zero rows, counted once per
+    # (token, column) -- exactly as engram_rows does.
     rng = np.random.default_rng(7 * T + cols)
     R = 777
     table_np = workloads.q2k_table(0, 0, R)
@@ -270,7 +281,7 @@ def test_project_q2k_ragged_and_bad_ids(eg, T, cols, N):
     kv_two = torch.empty((T, N), dtype=torch.int16, device="cuda")
     eg.engram_project(rows, wkv, kv_two, T, cols * 256, N)
     assert bad.item() == int(bad_mask.sum()) == bad2.item()
-    if T > SKINNY_MAX_TOKENS:
+    if q2k_same_order(T, cols):
         assert torch.equal(kv, kv_two)
     want_rows = oracle.rows_q2k(table_np, ids_np)
     _check_kv(kv.cpu().numpy().view(np.uint16), want_rows, wkv_np)
@@ -391,12 +402,15 @@ def test_forward_against_oracle(eg, c):
         assert np.array_equal(got[off].view(np.uint32), wl.h[off].view(np.uint32))
 
 
-@pytest.mark.parametrize("T,max_ngram,n_heads", [(300, 5, 9), (100, 4, 8)])
+@pytest.mark.parametrize("T,max_ngram,n_heads", [(300, 5, 9), (300, 4, 8), (100, 4, 8),
+                                                  (100, 4, 5)])
 def test_forward_kernel_choices_against_oracle(eg, T, max_ngram, n_heads):
-    # engram_forward picks, per layer, between the fused Q2_K projection (more
-    # than 128 tokens and at most 32 columns), the weight-streaming projection
-    # (at most 128 tokens) and rows -> 256 x 256 tiles (here: 36 columns).
-    # Each choice must give the oracle's forward.
+    # engram_forward picks, per layer, between the fused Q2_K projection (at
+    # most 32 columns: 256 x 256 tiles above 128 tokens, weight streaming at
+    # or below it when the columns split into whole K quarters), rows -> the
+    # weight-streaming projection (at most 128 tokens, here 15 columns) and
+    # rows -> 256 x 256 tiles (here: 36 columns).  Each choice must give the
+    # oracle's forward.
     from oracle.layout import engram_layout, hash_multipliers
     cols = (max_ngram - 1) * n_heads
     V, hc, dim = 5000, 2, 128
