@@ -225,9 +225,11 @@ ENGRAM_API engram_status engram_project(const uint16_t *rows, const uint16_t *wk
 /* Stages 2 + 3 fused for Q2_K tables ([spark] overview stages 2-3): kv =
  * bf16(dequant(table[ids])) x wkv^T without writing the bf16 rows to memory.
  * The projection reads each row's 84-byte block and dequantises it on chip.
- * For T > 128 kv is bit for bit what engram_rows followed by engram_project
- * gives (same values, same fp32 accumulation order); for fewer tokens
- * engram_project streams wkv with another kernel and sums in another order.
+ * kv is bit for bit what engram_rows followed by engram_project gives (same
+ * values, same fp32 accumulation order) for T > 128, and for T <= 128 when
+ * cols % 4 == 0 (then the weight-streaming form runs, whose four K quarters
+ * are whole table columns); for T <= 128 with other column counts the
+ * 256 x 256 tiles run and sum in another order than engram_project.
  *   table DEVICE Q2_K [num_rows][84], 4-byte aligned; ids, ids_token_stride,
  *   cols, bad_ids as for engram_rows (K = cols * 256); wkv DEVICE bf16 [N][K];
  *   kv DEVICE bf16 [T][N], 16-byte aligned, fully overwritten.
