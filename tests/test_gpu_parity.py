@@ -287,15 +287,17 @@ def test_project_q2k_ragged_and_bad_ids(eg, T, cols, N):
     _check_kv(kv.cpu().numpy().view(np.uint16), want_rows, wkv_np)
 
 
-def test_project_q2k_strided_ids_of_second_layer(eg):
+@pytest.mark.parametrize("T", [700, 100, 1])
+def test_project_q2k_strided_ids_of_second_layer(eg, T):
     # ids laid out [T][n_layers][cols]; layer 1 is read with an offset pointer
-    # and stride n_layers * cols, as engram_forward does.
+    # and stride n_layers * cols, as engram_forward does -- by the 256 x 256
+    # tiles (700 tokens, ragged in M) and by the weight-streaming form (100
+    # tokens: two 64-token tiles, the second ragged; a single token).
     c = 3
     wl = host(c)
     s = wl.spec
     ids, rows = gpu_rows(eg, c, 1, eg.ENGRAM_ROWS_Q2K)
     L = dev(c).layers[1]
-    T = 700                                   # a prefix: ragged in M
     kv = torch.empty((T, s.N), dtype=torch.int16, device="cuda")
     eg.engram_project_q2k(L.table, L.table.numel() // 84, ids.view(-1)[s.cols:], 2 * s.cols,
                           s.cols, L.wkv, kv, T, s.N)
