@@ -207,7 +207,8 @@ def engram_project(rows, wkv, kv, T: int, K: int, N: int, stream=None) -> None:
 def engram_project_q2k(table, num_rows: int, ids, ids_token_stride: int, cols: int, wkv, kv,
                        T: int, N: int, bad_ids=None, stream=None) -> None:
     """Stages 2 + 3 fused for a Q2_K table: kv [T, N] from ids, bit-identical
-    to engram_rows followed by engram_project."""
+    to engram_rows followed by engram_project for T > 128, and for T <= 128
+    when cols % 4 == 0 (its weight-streaming form)."""
     K = cols * HEAD_DIM
     need_ids = 0 if T <= 0 else (T - 1) * ids_token_stride + cols
     _check(_lib.engram_project_q2k(
