@@ -25,6 +25,7 @@
 // bytes 16 p + 8 h, p = 0..3.  The blocks of a column are loaded one column
 // ahead; their ids are resolved into byte offsets once, before the K loop.
 #include "gemm_common.hpp"
+#include "q2k_decode.hpp"
 
 namespace engram {
 namespace {
@@ -34,10 +35,6 @@ using namespace gemm;
 constexpr uint32_t kNoRow = 0x7FFFFFF0u;   // block offset past the table: loads read 0
 constexpr int kRowsPerLane = 2;            // tile rows w * 64 + 32 i + (lane % 32), i = 0, 1
 constexpr int kNJ = BN / 32;               // 8 column blocks per wave
-
-__device__ __forceinline__ float half_bits_to_float(uint32_t h16) {
-  return float(__builtin_bit_cast(_Float16, uint16_t(h16)));
-}
 
 // The register copy of the block parts one lane needs for one row.
 struct Q2kPart {
@@ -130,14 +127,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
   };
 
   // A fragments of k-step ks of stage qs (values 64 qs + 16 ks .. + 15 of the
-  // block) from register set `set`.  Inside that 16-value group the scale and
-  // min are fixed, so a value takes one of only four bf16 results,
-  // bf16(q * dl - ml) for q = 0..3.  They are computed once (in fp32, with the
-  // same fma and rounding as engram_rows) and kept as two byte planes, lo = the
-  // four low bytes and hi = the four high bytes.  Every output pair is then one
-  // v_perm_b32 of (hi, lo) whose selector bytes are q_a, q_a + 4, q_b, q_b + 4,
-  // and the selectors of four values are two more v_perm_b32 of
-  // (m | 0x04040404, m), m being their four 2-bit quants, one per byte.
+  // block: 16-value group 4 qs + ks) from register set `set` (q2k_decode.hpp).
   bf16x8 fa[2][kRowsPerLane], fb[2][kNJ];
   auto decode_a = [&](int set, const int qs, const int ks, int slot) {
     const int p = 2 * (qs >> 1) + (ks & 1);
@@ -145,23 +135,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
 #pragma unroll
     for (int i = 0; i < kRowsPerLane; ++i) {
       const Q2kPart &b = blk[set][i];
-      const float d = half_bits_to_float(b.dd & 0xFFFFu);
-      const float dmin = half_bits_to_float(b.dd >> 16);
-      const uint32_t sm = (b.sc[qs] >> (8 * ks)) & 0xFFu;
-      const float dl = d * float(sm & 0xFu), ml = dmin * float(sm >> 4);
-      const uint32_t p01 = pack_bf16x2(fmaf(0.0f, dl, -ml), fmaf(1.0f, dl, -ml));
-      const uint32_t p23 = pack_bf16x2(fmaf(2.0f, dl, -ml), fmaf(3.0f, dl, -ml));
-      const uint32_t lo = __builtin_amdgcn_perm(p23, p01, 0x06040200u);
-      const uint32_t hi = __builtin_amdgcn_perm(p23, p01, 0x07050301u);
-      u32x4 v;
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {                      // 4 quants per dword
-        const uint32_t m = (b.q[p][w] >> shift) & 0x03030303u;
-        const uint32_t m4 = m | 0x04040404u;
-        v[2 * w] = __builtin_amdgcn_perm(hi, lo, __builtin_amdgcn_perm(m4, m, 0x05010400u));
-        v[2 * w + 1] = __builtin_amdgcn_perm(hi, lo, __builtin_amdgcn_perm(m4, m, 0x07030602u));
-      }
-      fa[slot][i] = __builtin_bit_cast(bf16x8, v);
+      const Q2kPlanes pl = q2k_group_planes(b.dd, (b.sc[qs] >> (8 * ks)) & 0xFFu);
+      fa[slot][i] = __builtin_bit_cast(bf16x8, q2k_expand8(pl, b.q[p][0], b.q[p][1], shift));
     }
   };
 

@@ -19,6 +19,7 @@
 #include <algorithm>
 
 #include "gemm_common.hpp"
+#include "q2k_decode.hpp"
 
 namespace engram {
 namespace {
@@ -237,32 +238,16 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
       blk[set][i].dd = __builtin_amdgcn_raw_buffer_load_b32(rt, off + 80, 0, 0);
     }
   };
-  // A fragments of step s of the column from register set `set`.  Per
-  // 16-value group the four possible results bf16(q * dl - ml), q = 0..3, are
-  // computed once (same fma and rounding as engram_rows) and split into a
-  // low-byte and a high-byte plane; each output pair is one v_perm_b32 of the
-  // planes, with selector bytes q_a, q_a + 4, q_b, q_b + 4 made by two more
-  // v_perm_b32 of the 2-bit quants.
+  // A fragments of step s of the column from register set `set`: 16-value
+  // group 2 s + g / 2 (q2k_decode.hpp).
   const int sc_shift = 8 * (kg >> 1);
   auto decode = [&](const int set, const int s, u32x4 (&fa)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const Q2kLaneBlock &b = blk[set][i];
-      const float d = float(__builtin_bit_cast(_Float16, uint16_t(b.dd & 0xFFFFu)));
-      const float dmin = float(__builtin_bit_cast(_Float16, uint16_t(b.dd >> 16)));
-      const uint32_t sm = (b.sc[s >> 1] >> (16 * (s & 1) + sc_shift)) & 0xFFu;
-      const float dl = d * float(sm & 0xFu), ml = dmin * float(sm >> 4);
-      const uint32_t p01 = pack_bf16x2(fmaf(0.0f, dl, -ml), fmaf(1.0f, dl, -ml));
-      const uint32_t p23 = pack_bf16x2(fmaf(2.0f, dl, -ml), fmaf(3.0f, dl, -ml));
-      const uint32_t lo = __builtin_amdgcn_perm(p23, p01, 0x06040200u);
-      const uint32_t hi = __builtin_amdgcn_perm(p23, p01, 0x07050301u);
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const uint32_t m = (b.q[s >> 2][w] >> (2 * (s & 3))) & 0x03030303u;
-        const uint32_t m4 = m | 0x04040404u;
-        fa[i][2 * w] = __builtin_amdgcn_perm(hi, lo, __builtin_amdgcn_perm(m4, m, 0x05010400u));
-        fa[i][2 * w + 1] = __builtin_amdgcn_perm(hi, lo, __builtin_amdgcn_perm(m4, m, 0x07030602u));
-      }
+      const Q2kPlanes pl =
+          q2k_group_planes(b.dd, (b.sc[s >> 1] >> (16 * (s & 1) + sc_shift)) & 0xFFu);
+      fa[i] = q2k_expand8(pl, b.q[s >> 2][0], b.q[s >> 2][1], 2 * (s & 3));
     }
   };
   f32x4v acc[4][NSUB];
