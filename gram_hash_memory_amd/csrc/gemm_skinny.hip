@@ -161,8 +161,11 @@ hipError_t launch_nsub(const uint16_t *a, const uint16_t *w, uint16_t *c, int32_
 // in 16-value group 2 s + g / 2 (scale/min byte of that index) and their
 // quants in bytes 32 (s / 4) + 8 g .. + 7 of the 64 at bit 2 (s % 4).  So per
 // token and column a lane keeps 16 quant bytes, the 16 scale/min bytes and
-// d/dmin (9 dwords), loaded one column ahead; the byte offsets of all the
-// workgroup's blocks are resolved into LDS first.
+// d/dmin (9 dwords).  The byte offsets of all the workgroup's blocks are
+// resolved into LDS first; a column's blocks are then brought into the
+// wave's own LDS area by LDS-DMA one column ahead (whole 84-byte blocks: a
+// fraction of the memory requests of per-lane loads, which would compete with
+// the wkv stream), and each lane reads its 9 dwords per token from there.
 constexpr uint32_t kQ2kNoRow = 0x7FFFFFF0u;   // block offset past the table: loads read 0
 
 struct Q2kLaneBlock {
@@ -225,17 +228,32 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, voff + j * sub_step, k0 * 2, 0));
   };
   Q2kLaneBlock blk[2][4];
-  auto load_blocks = [&](const int set, int c) {          // wave-local column c (clamped)
-    const uint32_t *o = offs + (c0 + min(c, wcols - 1)) * kSkinnyM + r;
+  // A column's 64 blocks go into this wave's LDS area by LDS-DMA, 3 blocks
+  // of 21 dwords per instruction (lane L: block L / 21, dword L % 21; lane 63
+  // reads past the table, i.e. nothing), then each lane reads the 9 dwords
+  // per token it keeps.  The area is the wave's own, so no barrier.
+  constexpr int kDmaPerCol = (kSkinnyM + 2) / 3;           // 22
+  uint32_t *const stage_lds = offs + cols * kSkinnyM + wave * 2 * kDmaPerCol * 64;
+  const int dl_tok = lane / 21, dl_dw = lane % 21;
+  auto dma_blocks = [&](const int buf, int c) {            // wave-local column c (clamped)
+    const uint32_t *o = offs + (c0 + min(c, wcols - 1)) * kSkinnyM;
+#pragma unroll
+    for (int k = 0; k < kDmaPerCol; ++k) {
+      const int t = 3 * k + dl_tok;
+      const uint32_t off = (lane < 63 && t < kSkinnyM) ? o[t] + 4 * dl_dw : kQ2kNoRow;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, stage_lds + (buf * kDmaPerCol + k) * 64, 4,
+                                               off, 0, 0, 0);
+    }
+  };
+  auto read_blocks = [&](const int set, const int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t off = o[16 * i];
-      blk[set][i].sc = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0));
+      const int t = 16 * i + r;
+      const uint32_t *b = stage_lds + (buf * kDmaPerCol + t / 3) * 64 + 21 * (t % 3);
+      blk[set][i].sc = u32x4{b[0], b[1], b[2], b[3]};
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        blk[set][i].q[h] = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rt, off + 16 + 32 * h + 8 * kg, 0, 0));
-      blk[set][i].dd = __builtin_amdgcn_raw_buffer_load_b32(rt, off + 80, 0, 0);
+      for (int h = 0; h < 2; ++h) blk[set][i].q[h] = u32x2{b[4 + 8 * h + 2 * kg], b[5 + 8 * h + 2 * kg]};
+      blk[set][i].dd = b[20];
     }
   };
   // A fragments of step s of the column from register set `set`: 16-value
@@ -259,7 +277,12 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
   // multiplies (step t's B sits in slot t % P), and the blocks of the next
   // column requested at its start.
   auto column = [&](int c, const int set) {
-    load_blocks(set ^ 1, c + 1);
+    // Column c's blocks landed: only the 8 steps' B loads issued since their
+    // DMA (one column ago) may still be in flight.
+    __builtin_amdgcn_s_waitcnt(waitcnt(8 * NSUB, 15));
+    asm volatile("" ::: "memory");
+    read_blocks(set, set);
+    dma_blocks(set ^ 1, c + 1);
 #pragma unroll
     for (int s = 0; s < ENGRAM_HEAD_DIM / 32; ++s) {
       const int t = c * (ENGRAM_HEAD_DIM / 32) + s;
@@ -278,7 +301,9 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
     }
   };
 
-  load_blocks(0, 0);
+  dma_blocks(0, 0);
+  __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
+  asm volatile("" ::: "memory");
 #pragma unroll
   for (int p = 0; p < P - 1; ++p) load_b(p, p);
   for (int c = 0; c < wcols; c += 2) {
@@ -312,7 +337,8 @@ hipError_t launch_q2k_nsub(const uint8_t *table, int64_t num_rows, const int32_t
   constexpr int P = 4;
   const int cols = K / ENGRAM_HEAD_DIM;
   const size_t lds = size_t(kSkinnyWaves) * kSkinnyM * red_stride<NSUB>() * sizeof(float) +
-                     size_t(cols) * kSkinnyM * sizeof(uint32_t);
+                     size_t(cols) * kSkinnyM * sizeof(uint32_t) +
+                     size_t(kSkinnyWaves) * 2 * ((kSkinnyM + 2) / 3) * 64 * sizeof(uint32_t);
   const void *fn = reinterpret_cast<const void *>(&gemm_skinny_q2k_kernel<NSUB, P>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
