@@ -6,8 +6,10 @@
 // is bound by streaming wkv ((hc + 1) * dim rows of cols * 256 bf16, 252 MB
 // in the DeepSeek-V4.1 shape) from HBM once.  This kernel is built for that:
 //
-//  - one workgroup per NT = 16 * NSUB output columns and per 64 tokens, with
-//    NSUB chosen so that the column tiles about fill the 256 CUs;
+//  - one workgroup per NT = 16 * NSUB output columns and per 16 * MI tokens
+//    (MI = 4 up to 64 tokens, else 8), with NSUB chosen so that the column
+//    tiles about fill the 256 CUs: up to 128 tokens, every CU pulls its
+//    share of wkv once;
 //  - its 4 waves split K in four and each streams its quarter of the NT wkv
 //    rows straight from HBM into MFMA B fragments (v_mfma_f32_16x16x32_bf16:
 //    lane l holds 8 consecutive k of row l % 16, starting at k = 8 * (l / 16)),
@@ -15,7 +17,8 @@
 //  - the A fragments (the tokens' rows, a few hundred KB shared by every
 //    workgroup) come from L2 the same way;
 //  - the four partial sums are added in LDS in a fixed order, so results do
-//    not depend on timing, and rounded to bf16 once.
+//    not depend on timing, and rounded to bf16 once.  Each output's sum runs
+//    over the same k in the same order whatever the token tile.
 #include <algorithm>
 
 #include "gemm_common.hpp"
@@ -28,27 +31,87 @@ using namespace gemm;
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-constexpr int kSkinnyM = 64;             // tokens per workgroup
+constexpr int kSkinnyM = 64;             // tokens per workgroup of the Q2_K kernel; reduction pass
 constexpr int kSkinnyWaves = 4;
 constexpr int kSkinnyMaxTokens = 128;    // above this the 256 x 256 tiles of gemm.hip win
 
 template <int NSUB>
 constexpr int red_stride() { return 16 * NSUB + 4; }   // LDS row pitch (floats), bank spread
 
-template <int NSUB, int P>
+// Workgroup -> (column tile, token tile).  The dispatcher hands workgroups to
+// the 8 XCDs in turn (id % 8), each XCD taking its share in id order, so ids
+// L and L + 8 start on one XCD at about the same time.  The token tiles of a
+// column tile get ids 8 apart: after the first, they find most of the tile's
+// wkv rows in that XCD's L2 rather than in HBM.  The grid covers the column
+// tiles rounded up to a multiple of 8; ids past the last tile have nothing
+// to do.
+struct SkinnyTile {
+  int n, m;
+};
+__device__ __forceinline__ SkinnyTile skinny_tile(int tiles_m) {
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  return {(slot / tiles_m) * 8 + xcd, slot % tiles_m};
+}
+
+inline dim3 skinny_grid(int32_t M, int32_t N, int nt, int tm) {
+  const int tiles_n = (N + nt - 1) / nt, tiles_m = (M + tm - 1) / tm;
+  return dim3(((tiles_n + 7) / 8) * 8 * tiles_m);
+}
+
+// 16-token fragments per workgroup of the bf16 kernel.
+inline int skinny_mi(int32_t M) { return M <= 64 ? 4 : 8; }
+
+// The waves' partial sums -> LDS [wave][64][RS], then added in wave order
+// and rounded to bf16 once, 64 tokens at a time.  D of a 16 x 16 block: lane
+// l holds column l % 16 of rows 4 * (l / 16) .. + 3.  Starts with a barrier,
+// so the LDS may still be in use by the K loop.
+template <int MI, int NSUB>
+__device__ __forceinline__ void reduce_store(const f32x4v (&acc)[MI][NSUB], float *red,
+                                             uint16_t *__restrict__ C, int N, int m0, int mrows,
+                                             int n0, int wave, int tid) {
+  constexpr int NT = 16 * NSUB;
+  constexpr int RS = red_stride<NSUB>();
+  const int lane = tid & 63, r = lane & 15, kg = lane >> 4;
+  float *mine = red + wave * kSkinnyM * RS;
+#pragma unroll
+  for (int h = 0; h < MI / 4; ++h) {
+    if (kSkinnyM * h >= mrows) break;                // uniform: no token left
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NSUB; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          mine[(16 * i + 4 * kg + e) * RS + 16 * j + r] = acc[4 * h + i][j][e];
+    __syncthreads();
+    for (int idx = tid; idx < kSkinnyM * NT; idx += kSkinnyWaves * 64) {
+      const int m = idx / NT, n = idx % NT;
+      float sum = red[m * RS + n];
+#pragma unroll
+      for (int w = 1; w < kSkinnyWaves; ++w) sum += red[(w * kSkinnyM + m) * RS + n];
+      const int mm = kSkinnyM * h + m;
+      if (mm < mrows && n0 + n < N) C[int64_t(m0 + mm) * N + n0 + n] = f32_to_bf16(sum);
+    }
+  }
+}
+
+template <int MI, int NSUB, int P>
 __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
     int M, int N, int K) {
   constexpr int NT = 16 * NSUB;
-  constexpr int RS = red_stride<NSUB>();
+  constexpr int TM = 16 * MI;
   extern __shared__ __attribute__((aligned(16))) float red[];   // [waves][64][RS]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n0 = blockIdx.x * NT;
-  const int m0 = blockIdx.y * kSkinnyM;
-  const int mrows = min(kSkinnyM, M - m0);
+  const SkinnyTile tile = skinny_tile((M + TM - 1) / TM);
+  const int n0 = tile.n * NT;
+  if (n0 >= N) return;                               // whole workgroup: grid rounding
+  const int m0 = tile.m * TM;
+  const int mrows = min(TM, M - m0);
 
   // K quarter of this wave, in whole steps of 32 (K % 64 == 0).
   const int kq = ((K / kSkinnyWaves + 31) / 32) * 32;
@@ -63,7 +126,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_kernel(
   const uint32_t voff = uint32_t(r * K + 8 * kg) * 2;
   const uint32_t sub_step = uint32_t(16 * K) * 2;       // 16 rows further
 
-  u32x4 fa[P][4], fb[P][NSUB];
+  u32x4 fa[P][MI], fb[P][NSUB];
   auto load = [&](const int slot, int step) {
     const int k0 = kbeg + min(step, nsteps - 1) * 32;
 #pragma unroll
@@ -71,18 +134,18 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_kernel(
       fb[slot][j] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, voff + j * sub_step, k0 * 2, 0));
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
       fa[slot][i] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, voff + i * sub_step, k0 * 2, 0));
   };
-  f32x4v acc[4][NSUB];
+  f32x4v acc[MI][NSUB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NSUB; ++j) acc[i][j] = f32x4v{};
   auto mma = [&](const int slot) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NSUB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -113,38 +176,28 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_kernel(
       if (s + q < nsteps) mma(q);
   }
 
-  // Partial sums -> LDS [wave][row][col]; D of a 16 x 16 block: lane l holds
-  // column l % 16 of rows 4 * (l / 16) .. + 3.
-  float *mine = red + wave * kSkinnyM * RS;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < NSUB; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        mine[(16 * i + 4 * kg + e) * RS + 16 * j + r] = acc[i][j][e];
-  __syncthreads();
-  for (int idx = tid; idx < kSkinnyM * NT; idx += kSkinnyWaves * 64) {
-    const int m = idx / NT, n = idx % NT;
-    float s = red[m * RS + n];
-#pragma unroll
-    for (int w = 1; w < kSkinnyWaves; ++w) s += red[(w * kSkinnyM + m) * RS + n];
-    if (m < mrows && n0 + n < N) C[int64_t(m0 + m) * N + n0 + n] = f32_to_bf16(s);
-  }
+  reduce_store<MI, NSUB>(acc, red, C, N, m0, mrows, n0, wave, tid);
 }
 
-template <int NSUB>
+template <int MI, int NSUB>
 hipError_t launch_nsub(const uint16_t *a, const uint16_t *w, uint16_t *c, int32_t M, int32_t K,
                        int32_t N, hipStream_t stream) {
   constexpr int P = 4;
   const size_t lds = size_t(kSkinnyWaves) * kSkinnyM * red_stride<NSUB>() * sizeof(float);
-  const void *fn = reinterpret_cast<const void *>(&gemm_skinny_kernel<NSUB, P>);
+  const void *fn = reinterpret_cast<const void *>(&gemm_skinny_kernel<MI, NSUB, P>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
-  const dim3 grid((N + 16 * NSUB - 1) / (16 * NSUB), (M + kSkinnyM - 1) / kSkinnyM);
-  hipLaunchKernelGGL((gemm_skinny_kernel<NSUB, P>), grid, dim3(kSkinnyWaves * 64), lds, stream,
-                     a, w, c, M, N, K);
+  const dim3 grid = skinny_grid(M, N, 16 * NSUB, 16 * MI);
+  hipLaunchKernelGGL((gemm_skinny_kernel<MI, NSUB, P>), grid, dim3(kSkinnyWaves * 64), lds,
+                     stream, a, w, c, M, N, K);
   return hipGetLastError();
+}
+
+template <int NSUB>
+hipError_t launch_mi(const uint16_t *a, const uint16_t *w, uint16_t *c, int32_t M, int32_t K,
+                     int32_t N, hipStream_t stream) {
+  return skinny_mi(M) == 4 ? launch_nsub<4, NSUB>(a, w, c, M, K, N, stream)
+                           : launch_nsub<8, NSUB>(a, w, c, M, K, N, stream);
 }
 
 // Stages 2 + 3 fused for few tokens and a Q2_K table ([spark engram_v41
@@ -166,6 +219,10 @@ hipError_t launch_nsub(const uint16_t *a, const uint16_t *w, uint16_t *c, int32_
 // wave's own LDS area by LDS-DMA one column ahead (whole 84-byte blocks: a
 // fraction of the memory requests of per-lane loads, which would compete with
 // the wkv stream), and each lane reads its 9 dwords per token from there.
+//
+// Its token tile stays at 64 (a 128-token tile needs more than the 512
+// registers of a lane at the widest column tiles); 65-128 tokens run two
+// token tiles per column tile, paired on one XCD by skinny_tile.
 constexpr uint32_t kQ2kNoRow = 0x7FFFFFF0u;   // block offset past the table: loads read 0
 
 struct Q2kLaneBlock {
@@ -187,8 +244,10 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n0 = blockIdx.x * NT;
-  const int m0 = blockIdx.y * kSkinnyM;
+  const SkinnyTile tile = skinny_tile((M + kSkinnyM - 1) / kSkinnyM);
+  const int n0 = tile.n * NT;
+  if (n0 >= N) return;                               // whole workgroup: grid rounding
+  const int m0 = tile.m * kSkinnyM;
   const int mrows = min(kSkinnyM, M - m0);
   const int cols = K / ENGRAM_HEAD_DIM;
   const int wcols = cols / kSkinnyWaves;             // table columns of this wave's quarter
@@ -209,7 +268,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
       bad += row_ok && !ok;
       offs[c * kSkinnyM + t] = row_ok && ok ? uint32_t(id) * ENGRAM_Q2K_ROW_BYTES : kQ2kNoRow;
     }
-    if (bad && blockIdx.x == 0 && bad_ids) atomicAdd(bad_ids, bad);
+    if (bad && tile.n == 0 && bad_ids) atomicAdd(bad_ids, bad);
   }
   __syncthreads();
 
@@ -311,23 +370,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
     if (c + 1 < wcols) column(c + 1, 1);
   }
 
-  // Partial sums -> LDS, then the four quarters added in wave order.
-  float *mine = red + wave * kSkinnyM * RS;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < NSUB; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        mine[(16 * i + 4 * kg + e) * RS + 16 * j + r] = acc[i][j][e];
-  __syncthreads();
-  for (int idx = tid; idx < kSkinnyM * NT; idx += kSkinnyWaves * 64) {
-    const int m = idx / NT, n = idx % NT;
-    float sum = red[m * RS + n];
-#pragma unroll
-    for (int w = 1; w < kSkinnyWaves; ++w) sum += red[(w * kSkinnyM + m) * RS + n];
-    if (m < mrows && n0 + n < N) C[int64_t(m0 + m) * N + n0 + n] = f32_to_bf16(sum);
-  }
+  reduce_store<4, NSUB>(acc, red, C, N, m0, mrows, n0, wave, tid);
 }
 
 template <int NSUB>
@@ -342,7 +385,7 @@ hipError_t launch_q2k_nsub(const uint8_t *table, int64_t num_rows, const int32_t
   const void *fn = reinterpret_cast<const void *>(&gemm_skinny_q2k_kernel<NSUB, P>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
-  const dim3 grid((N + 16 * NSUB - 1) / (16 * NSUB), (M + kSkinnyM - 1) / kSkinnyM);
+  const dim3 grid = skinny_grid(M, N, 16 * NSUB, kSkinnyM);
   hipLaunchKernelGGL((gemm_skinny_q2k_kernel<NSUB, P>), grid, dim3(kSkinnyWaves * 64), lds,
                      stream, table, num_rows, ids, ids_stride, w, c, M, N, K, bad_ids);
   return hipGetLastError();
@@ -362,11 +405,11 @@ bool project_uses_skinny(int32_t M) { return M <= kSkinnyMaxTokens; }
 hipError_t launch_project_skinny(const uint16_t *a, const uint16_t *w, uint16_t *c, int32_t M,
                                  int32_t K, int32_t N, hipStream_t stream) {
   switch (skinny_nsub(N)) {
-    case 1: return launch_nsub<1>(a, w, c, M, K, N, stream);
-    case 2: return launch_nsub<2>(a, w, c, M, K, N, stream);
-    case 3: return launch_nsub<3>(a, w, c, M, K, N, stream);
-    case 4: return launch_nsub<4>(a, w, c, M, K, N, stream);
-    default: return launch_nsub<5>(a, w, c, M, K, N, stream);
+    case 1: return launch_mi<1>(a, w, c, M, K, N, stream);
+    case 2: return launch_mi<2>(a, w, c, M, K, N, stream);
+    case 3: return launch_mi<3>(a, w, c, M, K, N, stream);
+    case 4: return launch_mi<4>(a, w, c, M, K, N, stream);
+    default: return launch_mi<5>(a, w, c, M, K, N, stream);
   }
 }
 

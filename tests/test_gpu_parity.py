@@ -183,11 +183,12 @@ def _check_kv(got_bits, rows_bits, wkv_bits):
     return float(np.mean(got == want))
 
 
-# Few tokens (<= 128) take the weight-streaming kernel, more the 256 x 256 tiles.
+# Few tokens (<= 128) take the weight-streaming kernel (64- or 128-token tiles), more the
+# 256 x 256 tiles.
 @pytest.mark.parametrize("M,N,K", [(1, 64, 64), (300, 520, 512), (257, 256, 1536),
                                    (512, 768, 192), (3, 16, 128), (17, 80, 6144),
                                    (64, 20480, 6144), (65, 1000, 1536), (100, 300, 320),
-                                   (128, 384, 256), (129, 384, 256)])
+                                   (128, 384, 256), (129, 384, 256), (96, 20480, 6144)])
 def test_project_ragged_shapes_full_compare(eg, M, N, K):
     rng = np.random.default_rng(M + N + K)
     a = oracle.bf16_bits(oracle.bf16_round(rng.standard_normal((M, K))))
