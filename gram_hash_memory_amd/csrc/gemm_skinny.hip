@@ -31,20 +31,20 @@ using namespace gemm;
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-constexpr int kSkinnyM = 64;             // tokens per workgroup of the Q2_K kernel; reduction pass
+constexpr int kSkinnyM = 64;             // tokens per pass of the reduction through LDS
 constexpr int kSkinnyWaves = 4;
 constexpr int kSkinnyMaxTokens = 128;    // above this the 256 x 256 tiles of gemm.hip win
 
 template <int NSUB>
 constexpr int red_stride() { return 16 * NSUB + 4; }   // LDS row pitch (floats), bank spread
 
-// Workgroup -> (column tile, token tile).  The dispatcher hands workgroups to
-// the 8 XCDs in turn (id % 8), each XCD taking its share in id order, so ids
-// L and L + 8 start on one XCD at about the same time.  The token tiles of a
-// column tile get ids 8 apart: after the first, they find most of the tile's
-// wkv rows in that XCD's L2 rather than in HBM.  The grid covers the column
-// tiles rounded up to a multiple of 8; ids past the last tile have nothing
-// to do.
+// Workgroup -> (column tile, token tile).  Up to 128 tokens there is one
+// token tile; should a column tile have several, their ids are 8 apart: the
+// dispatcher hands workgroups to the 8 XCDs in turn (id % 8), each XCD taking
+// its share in id order, so they start together on one XCD and all but the
+// first find most of the tile's wkv rows in that XCD's L2.  The grid covers
+// the column tiles rounded up to a multiple of 8; ids past the last tile
+// have nothing to do.
 struct SkinnyTile {
   int n, m;
 };
@@ -58,7 +58,7 @@ inline dim3 skinny_grid(int32_t M, int32_t N, int nt, int tm) {
   return dim3(((tiles_n + 7) / 8) * 8 * tiles_m);
 }
 
-// 16-token fragments per workgroup of the bf16 kernel.
+// 16-token fragments per workgroup.
 inline int skinny_mi(int32_t M) { return M <= 64 ? 4 : 8; }
 
 // The waves' partial sums -> LDS [wave][64][RS], then added in wave order
@@ -203,52 +203,54 @@ hipError_t launch_mi(const uint16_t *a, const uint16_t *w, uint16_t *c, int32_t 
 // Stages 2 + 3 fused for few tokens and a Q2_K table ([spark engram_v41
 // page, overview stages 2-3]): the kernel above with A decoded on chip from
 // the tokens' 84-byte blocks instead of read as bf16 rows.  A workgroup then
-// pulls 64 * cols * 84 bytes of blocks from L2 instead of 64 * cols * 512
-// bytes of rows, and the rows never go to memory.  Same K quarters, same
-// MFMAs in the same order, same reduction: kv is bit-identical to
+// pulls TM * cols * 84 bytes of blocks from L2 instead of TM * cols * 512
+// bytes of rows, and the rows never go to memory.  Same token tiles, K
+// quarters, MFMAs in the same order and reduction: kv is bit-identical to
 // engram_rows followed by the kernel above.  The quarters must be whole
 // table columns (cols % 4 == 0).
 //
 // Lane (r, g) of a 16 x 32 A fragment holds token 16 i + r, values
 // 32 s + 8 g .. + 7 of the column (s = step in the column, 0..7).  Those sit
 // in 16-value group 2 s + g / 2 (scale/min byte of that index) and their
-// quants in bytes 32 (s / 4) + 8 g .. + 7 of the 64 at bit 2 (s % 4).  So per
-// token and column a lane keeps 16 quant bytes, the 16 scale/min bytes and
-// d/dmin (9 dwords).  The byte offsets of all the workgroup's blocks are
-// resolved into LDS first; a column's blocks are then brought into the
-// wave's own LDS area by LDS-DMA one column ahead (whole 84-byte blocks: a
-// fraction of the memory requests of per-lane loads, which would compete with
-// the wkv stream), and each lane reads its 9 dwords per token from there.
-//
-// Its token tile stays at 64 (a 128-token tile needs more than the 512
-// registers of a lane at the widest column tiles); 65-128 tokens run two
-// token tiles per column tile, paired on one XCD by skinny_tile.
+// quants in bytes 32 (s / 4) + 8 g .. + 7 of the 64 at bit 2 (s % 4).  The
+// byte offsets of all the workgroup's blocks are resolved into LDS first; a
+// column's blocks are then brought into the wave's own LDS area by LDS-DMA
+// one column ahead (whole 84-byte blocks: a fraction of the memory requests
+// of per-lane loads, which would compete with the wkv stream).  They stay
+// there: each step reads, per token, the scale/min dword and the two quant
+// dwords it decodes (d/dmin once per column), a step ahead.  Holding a
+// column's 9 dwords per token in registers instead does not fit a 128-token
+// tile at the widest column tiles.
 constexpr uint32_t kQ2kNoRow = 0x7FFFFFF0u;   // block offset past the table: loads read 0
 
-struct Q2kLaneBlock {
-  u32x4 sc;          // scale/min bytes 0..15
-  u32x2 q[2];        // quant bytes 8 g .. 8 g + 7 and 32 + 8 g .. 32 + 8 g + 7
-  uint32_t dd;       // fp16 d | fp16 dmin << 16
-};
+template <int MI>
+constexpr int q2k_dma_per_col() { return (16 * MI + 2) / 3; }   // 3 blocks per instruction
 
-template <int NSUB, int P>
+template <int MI>
+size_t q2k_skinny_loop_lds(int cols) {
+  return (size_t(cols) * 16 * MI + size_t(kSkinnyWaves) * 2 * q2k_dma_per_col<MI>() * 64) *
+         sizeof(uint32_t);
+}
+
+template <int MI, int NSUB, int P>
 __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
     const uint8_t *__restrict__ table, int64_t num_rows, const int32_t *__restrict__ ids,
     int64_t ids_stride, const uint16_t *__restrict__ B, uint16_t *__restrict__ C, int M, int N,
     int K, int32_t *__restrict__ bad_ids) {
+  constexpr int TM = 16 * MI;
   constexpr int NT = 16 * NSUB;
-  constexpr int RS = red_stride<NSUB>();
-  // [waves][64][RS] partial sums, then the block offsets [cols][64]
+  // K loop: the block offsets [cols][TM], then each wave's two staging
+  // areas; afterwards the [waves][64][RS] partial sums.
   extern __shared__ __attribute__((aligned(16))) float red[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const SkinnyTile tile = skinny_tile((M + kSkinnyM - 1) / kSkinnyM);
+  const SkinnyTile tile = skinny_tile((M + TM - 1) / TM);
   const int n0 = tile.n * NT;
   if (n0 >= N) return;                               // whole workgroup: grid rounding
-  const int m0 = tile.m * kSkinnyM;
-  const int mrows = min(kSkinnyM, M - m0);
+  const int m0 = tile.m * TM;
+  const int mrows = min(TM, M - m0);
   const int cols = K / ENGRAM_HEAD_DIM;
   const int wcols = cols / kSkinnyWaves;             // table columns of this wave's quarter
   const int c0 = wave * wcols;
@@ -257,16 +259,16 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
 
   // Block offsets; ids outside the table are counted once per (token,
   // column), by the first column tile.
-  uint32_t *const offs = reinterpret_cast<uint32_t *>(red + kSkinnyWaves * kSkinnyM * RS);
+  uint32_t *const offs = reinterpret_cast<uint32_t *>(red);
   {
-    const int t = tid & 63;
-    const bool row_ok = t < mrows;
     int bad = 0;
-    for (int c = tid >> 6; c < cols; c += kSkinnyWaves) {
+    for (int idx = tid; idx < cols * TM; idx += kSkinnyWaves * 64) {
+      const int c = idx / TM, t = idx % TM;
+      const bool row_ok = t < mrows;
       const int32_t id = row_ok ? ids[int64_t(m0 + t) * ids_stride + c] : 0;
       const bool ok = id >= 0 && id < num_rows;
       bad += row_ok && !ok;
-      offs[c * kSkinnyM + t] = row_ok && ok ? uint32_t(id) * ENGRAM_Q2K_ROW_BYTES : kQ2kNoRow;
+      offs[c * TM + t] = row_ok && ok ? uint32_t(id) * ENGRAM_Q2K_ROW_BYTES : kQ2kNoRow;
     }
     if (bad && tile.n == 0 && bad_ids) atomicAdd(bad_ids, bad);
   }
@@ -286,71 +288,87 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
       fb[slot][j] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, voff + j * sub_step, k0 * 2, 0));
   };
-  Q2kLaneBlock blk[2][4];
-  // A column's 64 blocks go into this wave's LDS area by LDS-DMA, 3 blocks
+  // A column's TM blocks go into this wave's LDS area by LDS-DMA, 3 blocks
   // of 21 dwords per instruction (lane L: block L / 21, dword L % 21; lane 63
-  // reads past the table, i.e. nothing), then each lane reads the 9 dwords
-  // per token it keeps.  The area is the wave's own, so no barrier.
-  constexpr int kDmaPerCol = (kSkinnyM + 2) / 3;           // 22
-  uint32_t *const stage_lds = offs + cols * kSkinnyM + wave * 2 * kDmaPerCol * 64;
+  // and blocks past TM read past the table, i.e. nothing), spread over the
+  // column's first kDmaSteps steps.  The area is the wave's own, so no
+  // barrier.
+  constexpr int kDmaPerCol = q2k_dma_per_col<MI>();        // 22 or 43
+  constexpr int kDmaSteps = MI == 8 ? 4 : 1;
+  constexpr int kDmaChunk = (kDmaPerCol + kDmaSteps - 1) / kDmaSteps;
+  uint32_t *const stage_lds = offs + cols * TM + wave * 2 * kDmaPerCol * 64;
   const int dl_tok = lane / 21, dl_dw = lane % 21;
-  auto dma_blocks = [&](const int buf, int c) {            // wave-local column c (clamped)
-    const uint32_t *o = offs + (c0 + min(c, wcols - 1)) * kSkinnyM;
+  auto dma_blocks = [&](const int buf, int c, const int kb, const int ke) {
+    const uint32_t *o = offs + (c0 + min(c, wcols - 1)) * TM;   // wave-local column c, clamped
 #pragma unroll
-    for (int k = 0; k < kDmaPerCol; ++k) {
+    for (int k = kb; k < ke; ++k) {
       const int t = 3 * k + dl_tok;
-      const uint32_t off = (lane < 63 && t < kSkinnyM) ? o[t] + 4 * dl_dw : kQ2kNoRow;
+      const uint32_t ot = o[min(t, TM - 1)];
+      const uint32_t off = (lane < 63 && t < TM) ? ot + 4 * dl_dw : kQ2kNoRow;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, stage_lds + (buf * kDmaPerCol + k) * 64, 4,
                                                off, 0, 0, 0);
     }
   };
-  auto read_blocks = [&](const int set, const int buf) {
+  // The blocks stay in LDS; a step reads per token the scale/min dword and
+  // the two quant dwords it decodes, one step ahead.  Token 16 i + r's block
+  // of buffer `buf` starts at tok[i] + buf * kDmaPerCol * 64.
+  const uint32_t *tok[MI];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 16 * i + r;
-      const uint32_t *b = stage_lds + (buf * kDmaPerCol + t / 3) * 64 + 21 * (t % 3);
-      blk[set][i].sc = u32x4{b[0], b[1], b[2], b[3]};
+  for (int i = 0; i < MI; ++i) {
+    const int t = 16 * i + r;
+    tok[i] = stage_lds + (t / 3) * 64 + 21 * (t % 3);
+  }
+  uint32_t sc[2][MI], dd[MI];
+  u32x2 qq[2][MI];
+  auto read_step = [&](const int buf, const int s) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) blk[set][i].q[h] = u32x2{b[4 + 8 * h + 2 * kg], b[5 + 8 * h + 2 * kg]};
-      blk[set][i].dd = b[20];
+    for (int i = 0; i < MI; ++i) {
+      const uint32_t *b = tok[i] + buf * kDmaPerCol * 64;
+      sc[s & 1][i] = b[s >> 1];
+      qq[s & 1][i] = u32x2{b[4 + 8 * (s >> 2) + 2 * kg], b[5 + 8 * (s >> 2) + 2 * kg]};
     }
   };
-  // A fragments of step s of the column from register set `set`: 16-value
-  // group 2 s + g / 2 (q2k_decode.hpp).
+  // A fragments of step s of the column: 16-value group 2 s + g / 2
+  // (q2k_decode.hpp).
   const int sc_shift = 8 * (kg >> 1);
-  auto decode = [&](const int set, const int s, u32x4 (&fa)[4]) {
+  auto decode = [&](const int s, u32x4 (&fa)[MI]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const Q2kLaneBlock &b = blk[set][i];
+    for (int i = 0; i < MI; ++i) {
       const Q2kPlanes pl =
-          q2k_group_planes(b.dd, (b.sc[s >> 1] >> (16 * (s & 1) + sc_shift)) & 0xFFu);
-      fa[i] = q2k_expand8(pl, b.q[s >> 2][0], b.q[s >> 2][1], 2 * (s & 3));
+          q2k_group_planes(dd[i], (sc[s & 1][i] >> (16 * (s & 1) + sc_shift)) & 0xFFu);
+      fa[i] = q2k_expand8(pl, qq[s & 1][i][0], qq[s & 1][i][1], 2 * (s & 3));
     }
   };
-  f32x4v acc[4][NSUB];
+  f32x4v acc[MI][NSUB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NSUB; ++j) acc[i][j] = f32x4v{};
   // One table column: its 8 steps, B of step t + P - 1 requested while step t
   // multiplies (step t's B sits in slot t % P), and the blocks of the next
-  // column requested at its start.
+  // column requested over its first kDmaSteps steps.
   auto column = [&](int c, const int set) {
-    // Column c's blocks landed: only the 8 steps' B loads issued since their
-    // DMA (one column ago) may still be in flight.
-    __builtin_amdgcn_s_waitcnt(waitcnt(8 * NSUB, 15));
+    // Column c's blocks landed: only the B loads issued after the last of
+    // their DMA instructions (9 - kDmaSteps steps' worth) may be in flight.
+    __builtin_amdgcn_s_waitcnt(waitcnt((9 - kDmaSteps) * NSUB, 15));
     asm volatile("" ::: "memory");
-    read_blocks(set, set);
-    dma_blocks(set ^ 1, c + 1);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) dd[i] = tok[i][set * kDmaPerCol * 64 + 20];
+    read_step(set, 0);
 #pragma unroll
     for (int s = 0; s < ENGRAM_HEAD_DIM / 32; ++s) {
       const int t = c * (ENGRAM_HEAD_DIM / 32) + s;
+      if (s < kDmaSteps) {
+        dma_blocks(set ^ 1, c + 1, s * kDmaChunk, min((s + 1) * kDmaChunk, kDmaPerCol));
+        __builtin_amdgcn_sched_barrier(0);   // the wait above counts the B loads after these
+      }
       load_b((s + P - 1) % P, t + P - 1);
+      if (s + 1 < ENGRAM_HEAD_DIM / 32) read_step(set, s + 1);
       __builtin_amdgcn_sched_barrier(0);
-      u32x4 fa[4];
-      decode(set, s, fa);
+      u32x4 fa[MI];
+      decode(s, fa);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NSUB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -360,7 +378,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
     }
   };
 
-  dma_blocks(0, 0);
+  dma_blocks(0, 0, 0, kDmaPerCol);
   __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
   asm volatile("" ::: "memory");
 #pragma unroll
@@ -370,25 +388,37 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
     if (c + 1 < wcols) column(c + 1, 1);
   }
 
-  reduce_store<4, NSUB>(acc, red, C, N, m0, mrows, n0, wave, tid);
+  // The last column still requested a (clamped) next column: its LDS-DMA
+  // writes must land before the partial sums reuse the staging areas.
+  __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
+  asm volatile("" ::: "memory");
+  reduce_store<MI, NSUB>(acc, red, C, N, m0, mrows, n0, wave, tid);
 }
 
-template <int NSUB>
+template <int MI, int NSUB>
 hipError_t launch_q2k_nsub(const uint8_t *table, int64_t num_rows, const int32_t *ids,
                            int64_t ids_stride, const uint16_t *w, uint16_t *c, int32_t M,
                            int32_t K, int32_t N, int32_t *bad_ids, hipStream_t stream) {
   constexpr int P = 4;
   const int cols = K / ENGRAM_HEAD_DIM;
-  const size_t lds = size_t(kSkinnyWaves) * kSkinnyM * red_stride<NSUB>() * sizeof(float) +
-                     size_t(cols) * kSkinnyM * sizeof(uint32_t) +
-                     size_t(kSkinnyWaves) * 2 * ((kSkinnyM + 2) / 3) * 64 * sizeof(uint32_t);
-  const void *fn = reinterpret_cast<const void *>(&gemm_skinny_q2k_kernel<NSUB, P>);
+  const size_t lds = std::max(size_t(kSkinnyWaves) * kSkinnyM * red_stride<NSUB>() * sizeof(float),
+                              q2k_skinny_loop_lds<MI>(cols));
+  const void *fn = reinterpret_cast<const void *>(&gemm_skinny_q2k_kernel<MI, NSUB, P>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
-  const dim3 grid = skinny_grid(M, N, 16 * NSUB, kSkinnyM);
-  hipLaunchKernelGGL((gemm_skinny_q2k_kernel<NSUB, P>), grid, dim3(kSkinnyWaves * 64), lds,
+  const dim3 grid = skinny_grid(M, N, 16 * NSUB, 16 * MI);
+  hipLaunchKernelGGL((gemm_skinny_q2k_kernel<MI, NSUB, P>), grid, dim3(kSkinnyWaves * 64), lds,
                      stream, table, num_rows, ids, ids_stride, w, c, M, N, K, bad_ids);
   return hipGetLastError();
+}
+
+template <int NSUB>
+hipError_t launch_q2k_mi(const uint8_t *table, int64_t num_rows, const int32_t *ids,
+                         int64_t ids_stride, const uint16_t *w, uint16_t *c, int32_t M,
+                         int32_t K, int32_t N, int32_t *bad_ids, hipStream_t stream) {
+  return skinny_mi(M) == 4
+             ? launch_q2k_nsub<4, NSUB>(table, num_rows, ids, ids_stride, w, c, M, K, N, bad_ids, stream)
+             : launch_q2k_nsub<8, NSUB>(table, num_rows, ids, ids_stride, w, c, M, K, N, bad_ids, stream);
 }
 
 int skinny_nsub(int32_t N) {
@@ -427,11 +457,11 @@ hipError_t launch_project_q2k_skinny(const uint8_t *table, int64_t num_rows, con
                                      hipStream_t stream) {
   const int32_t K = cols * ENGRAM_HEAD_DIM;
   switch (skinny_nsub(N)) {
-    case 1: return launch_q2k_nsub<1>(table, num_rows, ids, ids_token_stride, w, c, M, K, N, bad_ids, stream);
-    case 2: return launch_q2k_nsub<2>(table, num_rows, ids, ids_token_stride, w, c, M, K, N, bad_ids, stream);
-    case 3: return launch_q2k_nsub<3>(table, num_rows, ids, ids_token_stride, w, c, M, K, N, bad_ids, stream);
-    case 4: return launch_q2k_nsub<4>(table, num_rows, ids, ids_token_stride, w, c, M, K, N, bad_ids, stream);
-    default: return launch_q2k_nsub<5>(table, num_rows, ids, ids_token_stride, w, c, M, K, N, bad_ids, stream);
+    case 1: return launch_q2k_mi<1>(table, num_rows, ids, ids_token_stride, w, c, M, K, N, bad_ids, stream);
+    case 2: return launch_q2k_mi<2>(table, num_rows, ids, ids_token_stride, w, c, M, K, N, bad_ids, stream);
+    case 3: return launch_q2k_mi<3>(table, num_rows, ids, ids_token_stride, w, c, M, K, N, bad_ids, stream);
+    case 4: return launch_q2k_mi<4>(table, num_rows, ids, ids_token_stride, w, c, M, K, N, bad_ids, stream);
+    default: return launch_q2k_mi<5>(table, num_rows, ids, ids_token_stride, w, c, M, K, N, bad_ids, stream);
   }
 }
 

@@ -258,12 +258,14 @@ def test_project_q2k_bit_identical_to_rows_then_project(eg, c):
 @pytest.mark.parametrize("T,cols,N", [(1, 1, 64), (3, 3, 320), (255, 5, 520), (257, 6, 256),
                                       (300, 24, 4096), (513, 2, 1000),
                                       (1, 4, 64), (64, 8, 1000), (100, 4, 520), (128, 12, 4096),
-                                      (37, 32, 300), (129, 8, 256)])
+                                      (37, 32, 300), (129, 8, 256), (65, 24, 20480),
+                                      (96, 32, 1000)])
 def test_project_q2k_ragged_and_bad_ids(eg, T, cols, N):
     # Ragged tiles in M and N, an odd column count (the 256 x 256 kernel's
     # half-unrolled tail), few tokens with whole-column K quarters (the
-    # weight-streaming form, one or several columns per quarter, an odd
-    # number included), and ids outside the table: zero rows, counted once per
+    # weight-streaming form with 64- and 128-token tiles, one or several
+    # columns per quarter, an odd number included, the widest column tiles at
+    # N = 20480), and ids outside the table: zero rows, counted once per
     # (token, column) -- exactly as engram_rows does.
     rng = np.random.default_rng(7 * T + cols)
     R = 777
@@ -293,7 +295,7 @@ def test_project_q2k_strided_ids_of_second_layer(eg, T):
     # ids laid out [T][n_layers][cols]; layer 1 is read with an offset pointer
     # and stride n_layers * cols, as engram_forward does -- by the 256 x 256
     # tiles (700 tokens, ragged in M) and by the weight-streaming form (100
-    # tokens: two 64-token tiles, the second ragged; a single token).
+    # tokens: one ragged 128-token tile; a single token).
     c = 3
     wl = host(c)
     s = wl.spec
