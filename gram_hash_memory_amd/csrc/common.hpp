@@ -81,7 +81,15 @@ hipError_t launch_project_q2k(const uint8_t *table, int64_t num_rows, const int3
                               hipStream_t stream);
 
 // MXFP8 projection for FP8 tables (gemm_mx.hip) and its weight prep (mx_quant.hip).
+// launch_project_mx runs the weight-streaming form (gemm_skinny.hip) where
+// project_mx_skinny_supported holds (up to 64 tokens), the 256 x 256 tiles
+// otherwise.
 bool project_mx_supported(int32_t N, int32_t K);
+bool project_mx_skinny_supported(int32_t M, int32_t cols);
+hipError_t launch_project_mx_skinny(const uint8_t *table, const uint8_t *scales, int64_t num_rows,
+                                    const int32_t *ids, int64_t ids_token_stride, int32_t cols,
+                                    const uint8_t *w_codes, const uint8_t *w_scales, uint16_t *c,
+                                    int32_t M, int32_t N, int32_t *bad_ids, hipStream_t stream);
 hipError_t launch_project_mx(const uint8_t *table, const uint8_t *scales, int64_t num_rows,
                              const int32_t *ids, int64_t ids_token_stride, int32_t cols,
                              const uint8_t *w_codes, const uint8_t *w_scales, uint16_t *c,

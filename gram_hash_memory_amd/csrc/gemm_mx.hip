@@ -293,6 +293,9 @@ hipError_t launch_project_mx(const uint8_t *table, const uint8_t *scales, int64_
                              const int32_t *ids, int64_t ids_token_stride, int32_t cols,
                              const uint8_t *w_codes, const uint8_t *w_scales, uint16_t *c,
                              int32_t M, int32_t N, int32_t *bad_ids, hipStream_t stream) {
+  if (project_mx_skinny_supported(M, cols))
+    return launch_project_mx_skinny(table, scales, num_rows, ids, ids_token_stride, cols,
+                                    w_codes, w_scales, c, M, N, bad_ids, stream);
   const int K = cols * ENGRAM_HEAD_DIM;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const size_t lds = size_t(2) * kStageBytes;

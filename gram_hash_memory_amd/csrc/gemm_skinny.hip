@@ -421,6 +421,174 @@ hipError_t launch_q2k_mi(const uint8_t *table, int64_t num_rows, const int32_t *
              : launch_q2k_nsub<8, NSUB>(table, num_rows, ids, ids_stride, w, c, M, K, N, bad_ids, stream);
 }
 
+// Stages 2 + 3 for few tokens, an FP8 table and an MXFP8 weight ([vLLM
+// engram page, EngramBatch / wkv_input]): the MXFP8 projection of
+// gemm_mx.hip in the weight-streaming form of the kernels above.  Each wave
+// streams its K quarter of the tile's weight rows (1 byte per value plus one
+// E8M0 byte per 32) from HBM into the operands of
+// v_mfma_scale_f32_16x16x128_f8f6f4, and the tokens' FP8 rows come from L2
+// as they are stored: E4M3 codes with one E8M0 scale per 32 values.
+//
+// Operand layout (16x16x128, 8-bit formats): lane 16 g + r holds row (A:
+// token) or column (B: weight row) r, bytes 0..15 = k 16 g .. 16 g + 15 and
+// bytes 16..31 = k 64 + 16 g .. 64 + 16 g + 15 of the instruction's 128; the
+// scale of MX block q (k 32 q .. 32 q + 31) comes from lane group q, byte 0
+// of its scale register (op_sel 0).  A 128-k step is half a table column, so
+// a lane's scale dword for a step holds the step's four blocks and is
+// shifted right by 8 g.
+//
+// Tables may exceed the 4 GB a buffer descriptor spans, so the rows are read
+// through 64-bit addresses; an id outside the table, or a token past T,
+// reads a zero row (zero codes, so the product is exactly 0 whatever the
+// scale, and zero scale bytes, 2^-127, finite).  Token tiles of 64: the
+// operands of P steps in flight leave no room for 128, and two 64-token
+// tiles, which pull the weight twice per CU, lose to the 256 x 256 tiles of
+// gemm_mx.hip, so this form runs up to 64 tokens.
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __attribute__((aligned(256))) const uint8_t kMxZeroRow[ENGRAM_HEAD_DIM] = {};
+constexpr uint32_t kMxNoRow = 0xFFFFFFFFu;
+
+template <int NSUB, int P>
+__global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_mx_kernel(
+    const uint8_t *__restrict__ table, const uint8_t *__restrict__ tscales, int64_t num_rows,
+    const int32_t *__restrict__ ids, int64_t ids_stride, const uint8_t *__restrict__ W,
+    const uint8_t *__restrict__ WS, uint16_t *__restrict__ C, int M, int N, int K,
+    int32_t *__restrict__ bad_ids) {
+  constexpr int MI = 4, TM = 16 * MI;
+  constexpr int NT = 16 * NSUB;
+  constexpr int kStep = 128;                          // k per instruction and step
+  // [waves][64][RS] partial sums, then the row indices [cols][TM]
+  extern __shared__ __attribute__((aligned(16))) float red[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const SkinnyTile tile = skinny_tile((M + TM - 1) / TM);
+  const int n0 = tile.n * NT;
+  if (n0 >= N) return;                               // whole workgroup: grid rounding
+  const int m0 = tile.m * TM;
+  const int mrows = min(TM, M - m0);
+  const int cols = K / ENGRAM_HEAD_DIM;
+  const int wcols = cols / kSkinnyWaves;             // table columns of this wave's quarter
+  const int kbeg = wave * wcols * ENGRAM_HEAD_DIM;
+  const int nsteps = wcols * (ENGRAM_HEAD_DIM / kStep);
+  const int ks = K / 32;                             // scale bytes per weight row
+
+  // Row indices; ids outside the table are counted once per (token,
+  // column), by the first column tile.
+  uint32_t *const rowidx =
+      reinterpret_cast<uint32_t *>(red + kSkinnyWaves * kSkinnyM * red_stride<NSUB>());
+  {
+    int bad = 0;
+    for (int idx = tid; idx < cols * TM; idx += kSkinnyWaves * 64) {
+      const int c = idx / TM, t = idx % TM;
+      const bool row_ok = t < mrows;
+      const int32_t id = row_ok ? ids[int64_t(m0 + t) * ids_stride + c] : 0;
+      const bool ok = id >= 0 && id < num_rows;
+      bad += row_ok && !ok;
+      rowidx[c * TM + t] = row_ok && ok ? uint32_t(id) : kMxNoRow;
+    }
+    if (bad && tile.n == 0 && bad_ids) atomicAdd(bad_ids, bad);
+  }
+  __syncthreads();
+
+  // Weight rows n0 + 16 j + r; rows past N read as zeros (the row is part of
+  // the range-checked VGPR offset, the SGPR offset carries the K position).
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(W + int64_t(n0) * K, int64_t(N - n0) * K);
+  const __amdgpu_buffer_rsrc_t rbs = make_rsrc(WS + int64_t(n0) * ks, int64_t(N - n0) * ks);
+  const int r = lane & 15, g = lane >> 4;
+  const uint32_t voff_b = uint32_t(r * K + 16 * g);
+  const uint32_t voff_bs = uint32_t(r * ks);
+
+  i32x8 fa[P][MI], fb[P][NSUB];
+  uint32_t sa[P][MI], sb[P][NSUB];
+  auto cat = [](u32x4 lo, u32x4 hi) {
+    return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // Operands of step u (clamped to the last) into slot `slot`.
+  auto load = [&](const int slot, int u) {
+    u = min(u, nsteps - 1);
+    const int k0 = kbeg + u * kStep;
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) {
+      const uint32_t vo = voff_b + uint32_t(j * 16 * K);
+      fb[slot][j] = cat(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, vo, k0, 0)),
+                        __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, vo + 64, k0, 0)));
+      sb[slot][j] = __builtin_amdgcn_raw_buffer_load_b32(rbs, voff_bs + uint32_t(j * 16 * ks),
+                                                         k0 / 32, 0);
+    }
+    const int col = k0 / ENGRAM_HEAD_DIM, half = u & 1;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const uint32_t idx = rowidx[col * TM + 16 * i + r];
+      const bool ok = idx != kMxNoRow;
+      const uint8_t *a = (ok ? table + int64_t(idx) * ENGRAM_HEAD_DIM : kMxZeroRow) +
+                         half * kStep + 16 * g;
+      fa[slot][i] = cat(*reinterpret_cast<const u32x4 *>(a),
+                        *reinterpret_cast<const u32x4 *>(a + 64));
+      const uint8_t *sp = ok ? tscales + int64_t(idx) * (ENGRAM_HEAD_DIM / 32) + 4 * half
+                             : kMxZeroRow;
+      sa[slot][i] = *reinterpret_cast<const uint32_t *>(sp);
+    }
+  };
+  f32x4v acc[MI][NSUB];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) acc[i][j] = f32x4v{};
+  auto mma = [&](const int slot) {
+    uint32_t xa[MI], xb[NSUB];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) xa[i] = sa[slot][i] >> (8 * g);
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) xb[j] = sb[slot][j] >> (8 * g);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NSUB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0, xa[i], 0, xb[j]);
+  };
+
+#pragma unroll
+  for (int p = 0; p < P - 1; ++p) load(p, p);
+  int s = 0;
+  for (; s + P <= nsteps; s += P) {
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      load((q + P - 1) % P, s + q + P - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < P - 1; ++q)
+    if (s + q < nsteps) mma(q);
+
+  reduce_store<MI, NSUB>(acc, red, C, N, m0, mrows, n0, wave, tid);
+}
+
+template <int NSUB>
+hipError_t launch_mx_nsub(const uint8_t *table, const uint8_t *scales, int64_t num_rows,
+                          const int32_t *ids, int64_t ids_stride, const uint8_t *w_codes,
+                          const uint8_t *w_scales, uint16_t *c, int32_t M, int32_t K, int32_t N,
+                          int32_t *bad_ids, hipStream_t stream) {
+  constexpr int P = 3;
+  const int cols = K / ENGRAM_HEAD_DIM;
+  const size_t lds = size_t(kSkinnyWaves) * kSkinnyM * red_stride<NSUB>() * sizeof(float) +
+                     size_t(cols) * kSkinnyM * sizeof(uint32_t);
+  const void *fn = reinterpret_cast<const void *>(&gemm_skinny_mx_kernel<NSUB, P>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (e != hipSuccess) return e;
+  const dim3 grid = skinny_grid(M, N, 16 * NSUB, kSkinnyM);
+  hipLaunchKernelGGL((gemm_skinny_mx_kernel<NSUB, P>), grid, dim3(kSkinnyWaves * 64), lds,
+                     stream, table, scales, num_rows, ids, ids_stride, w_codes, w_scales, c, M,
+                     N, K, bad_ids);
+  return hipGetLastError();
+}
+
 int skinny_nsub(int32_t N) {
   // Column tiles of 16 * NSUB, NSUB as small as lets about one tile per CU
   // cover N (the wkv stream is what bounds the kernel).
@@ -463,6 +631,32 @@ hipError_t launch_project_q2k_skinny(const uint8_t *table, int64_t num_rows, con
     case 4: return launch_q2k_mi<4>(table, num_rows, ids, ids_token_stride, w, c, M, K, N, bad_ids, stream);
     default: return launch_q2k_mi<5>(table, num_rows, ids, ids_token_stride, w, c, M, K, N, bad_ids, stream);
   }
+}
+
+}  // namespace engram
+
+namespace engram {
+
+bool project_mx_skinny_supported(int32_t M, int32_t cols) {
+  return M <= kSkinnyM && cols % kSkinnyWaves == 0;
+}
+
+hipError_t launch_project_mx_skinny(const uint8_t *table, const uint8_t *scales, int64_t num_rows,
+                                    const int32_t *ids, int64_t ids_token_stride, int32_t cols,
+                                    const uint8_t *w_codes, const uint8_t *w_scales, uint16_t *c,
+                                    int32_t M, int32_t N, int32_t *bad_ids, hipStream_t stream) {
+  const int32_t K = cols * ENGRAM_HEAD_DIM;
+#define ENGRAM_MX_NSUB(n)                                                                   \
+  return launch_mx_nsub<n>(table, scales, num_rows, ids, ids_token_stride, w_codes, w_scales, \
+                           c, M, K, N, bad_ids, stream)
+  switch (skinny_nsub(N)) {
+    case 1: ENGRAM_MX_NSUB(1);
+    case 2: ENGRAM_MX_NSUB(2);
+    case 3: ENGRAM_MX_NSUB(3);
+    case 4: ENGRAM_MX_NSUB(4);
+    default: ENGRAM_MX_NSUB(5);
+  }
+#undef ENGRAM_MX_NSUB
 }
 
 }  // namespace engram

@@ -264,12 +264,16 @@ ENGRAM_API engram_status engram_quantize_mxfp8(const uint16_t *w, int32_t N, int
  * rows with per-32 E8M0 scales are MX blocks already): kv[t][n] =
  * bf16(sum_k a[t][k] * w[n][k]), a[t][r*256 + i] = e4m3(table[ids[t][r]][i])
  * * 2^(scales[ids[t][r]][i/32] - 127), w = wkv_codes/wkv_scales likewise.
- * The rows are read raw by the block-scaled matrix cores
- * (v_mfma_scale_f32_32x32x64_f8f6f4) and never dequantised to memory.  The
- * matrix cores sum each instruction's 64 products below fp32 precision
- * (measured: up to 1.7e-4 of the sum of |products| on random e4m3 data); the
- * instructions' results accumulate in fp32 and each output is rounded to
- * bf16 once.
+ * The rows are read raw by the block-scaled matrix cores and never
+ * dequantised to memory: 256 x 256 output tiles of
+ * v_mfma_scale_f32_32x32x64_f8f6f4, or, for T <= 64 with cols % 4 == 0, a
+ * kernel that streams the weight once from HBM into
+ * v_mfma_scale_f32_16x16x128_f8f6f4 with K split four ways per workgroup.
+ * The matrix cores sum each instruction's 64 or 128 products below fp32
+ * precision (measured: up to 1.7e-4 of the sum of |products| on random e4m3
+ * data); the instructions' results accumulate in fp32 in a fixed order and
+ * each output is rounded to bf16 once, so the result does not depend on
+ * timing (but differs between the two forms in the last bits).
  *   table DEVICE [num_rows][256] e4m3fn codes, 16-byte aligned; scales DEVICE
  *   [num_rows][8], 4-byte aligned; ids, ids_token_stride, cols, bad_ids as for
  *   engram_rows (K = cols * 256; an id outside the table contributes 0);
