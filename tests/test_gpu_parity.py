@@ -662,11 +662,13 @@ def test_forward_mx_against_oracle(eg, c):
         assert np.array_equal(got[off].view(np.uint32), wl.h[off].view(np.uint32))
 
 
-@pytest.mark.parametrize("T", [100, 300])
-def test_forward_mx_small_full_compare(eg, T):
-    # Two FP8 layers, both in MXFP8, every token checked against oracle.forward.
+@pytest.mark.parametrize("T,n_heads", [(100, 2), (300, 2), (64, 4), (37, 4)])
+def test_forward_mx_small_full_compare(eg, T, n_heads):
+    # Two FP8 layers, both in MXFP8, every token checked against oracle.forward;
+    # with 12 columns and up to 64 tokens the weight-streaming MXFP8 kernel
+    # runs, reading each layer's ids with the forward's stride.
     from oracle.layout import engram_layout, hash_multipliers
-    max_ngram, n_heads, V, hc, dim = 4, 2, 3000, 2, 128
+    max_ngram, V, hc, dim = 4, 3000, 2, 128
     cols = (max_ngram - 1) * n_heads
     primes, offsets = engram_layout(2, max_ngram, n_heads, 4099)
     R = int((offsets + primes).max())
@@ -910,10 +912,12 @@ def test_hash_at_maximum_sizes(eg):
     assert np.array_equal(ids.cpu().numpy(), want)
 
 
-@pytest.mark.parametrize("kind,T,cols,N", [("q2k", 300, 32, 512), ("mx", 130, 40, 300)])
+@pytest.mark.parametrize("kind,T,cols,N", [("q2k", 300, 32, 512), ("mx", 130, 40, 300),
+                                           ("mx", 64, 40, 300)])
 def test_projection_at_many_columns(eg, kind, T, cols, N):
     # The fused Q2_K projection at its column limit (32) and the MXFP8
-    # projection past it (no column limit), against the oracle.
+    # projection past it (no column limit; tiles and the weight-streaming
+    # form), against the oracle.
     rng = np.random.default_rng(cols)
     R, K = 999, cols * 256
     ids_np = rng.integers(0, R, (T, cols)).astype(np.int32)
@@ -970,24 +974,27 @@ def test_gate_layers_equals_gate_per_layer(eg, T, masked):
 def test_project_mxfp8_table_past_4gb(eg):
     # A table of 17,000,000 FP8 rows (4.35 GB) with ids near its end: the row
     # offsets pass 2^32 bytes, which the gather reaches through 64-bit
-    # addresses.  The oracle gets the touched rows only, with the ids remapped.
-    R, T, cols, N = 17_000_000, 200, 3, 192
+    # addresses -- in the 256 x 256 tiles (200 tokens) and in the
+    # weight-streaming form (64 tokens, 4 columns).  The oracle gets the
+    # touched rows only, with the ids remapped.
+    R, N = 17_000_000, 192
     assert R * 256 > 2**32
     g = torch.Generator(device="cuda").manual_seed(5)
     table = torch.randint(0, 0x7E, (R, 256), dtype=torch.uint8, device="cuda", generator=g)
     scales = torch.randint(119, 128, (R, 8), dtype=torch.uint8, device="cuda", generator=g)
     rng = np.random.default_rng(6)
-    ids_np = rng.integers(R - 5000, R, (T, cols)).astype(np.int32)
-    ids_np[::7, 0] = rng.integers(0, R, len(ids_np[::7, 0]))       # and some anywhere
-    K = cols * 256
-    wkv_np = oracle.bf16_bits(oracle.bf16_round(0.05 * rng.standard_normal((N, K))))
-    wc, ws = oracle.quantize_mxfp8(wkv_np)
-    kv = torch.full((T, N), 0x7777, dtype=torch.int16, device="cuda")
-    eg.engram_project_mxfp8(table, scales, R, tensor(ids_np, "cuda"), cols, cols,
-                            tensor(wc, "cuda"), tensor(ws, "cuda"), kv, T, N)
-    uniq, inv = np.unique(ids_np, return_inverse=True)
-    sel = torch.from_numpy(uniq.astype(np.int64)).cuda()
-    sub_t, sub_s = table[sel].cpu().numpy(), scales[sel].cpu().numpy()
+    for T, cols in [(200, 3), (64, 4)]:
+        ids_np = rng.integers(R - 5000, R, (T, cols)).astype(np.int32)
+        ids_np[::7, 0] = rng.integers(0, R, len(ids_np[::7, 0]))       # and some anywhere
+        K = cols * 256
+        wkv_np = oracle.bf16_bits(oracle.bf16_round(0.05 * rng.standard_normal((N, K))))
+        wc, ws = oracle.quantize_mxfp8(wkv_np)
+        kv = torch.full((T, N), 0x7777, dtype=torch.int16, device="cuda")
+        eg.engram_project_mxfp8(table, scales, R, tensor(ids_np, "cuda"), cols, cols,
+                                tensor(wc, "cuda"), tensor(ws, "cuda"), kv, T, N)
+        uniq, inv = np.unique(ids_np, return_inverse=True)
+        sel = torch.from_numpy(uniq.astype(np.int64)).cuda()
+        sub_t, sub_s = table[sel].cpu().numpy(), scales[sel].cpu().numpy()
+        a_c, a_s = oracle.rows_fp8_mx(sub_t, sub_s, inv.reshape(T, cols))
+        _check_kv_mx(kv.cpu().numpy().view(np.uint16), a_c, a_s, wc, ws)
     del table, scales
-    a_c, a_s = oracle.rows_fp8_mx(sub_t, sub_s, inv.reshape(T, cols))
-    _check_kv_mx(kv.cpu().numpy().view(np.uint16), a_c, a_s, wc, ws)
