@@ -426,8 +426,8 @@ hipError_t launch_q2k_mi(const uint8_t *table, int64_t num_rows, const int32_t *
 // gemm_mx.hip in the weight-streaming form of the kernels above.  Each wave
 // streams its K quarter of the tile's weight rows (1 byte per value plus one
 // E8M0 byte per 32) from HBM into the operands of
-// v_mfma_scale_f32_16x16x128_f8f6f4, and the tokens' FP8 rows come from L2
-// as they are stored: E4M3 codes with one E8M0 scale per 32 values.
+// v_mfma_scale_f32_16x16x128_f8f6f4; the tokens' FP8 rows are multiplied as
+// they are stored: E4M3 codes with one E8M0 scale per 32 values.
 //
 // Operand layout (16x16x128, 8-bit formats): lane 16 g + r holds row (A:
 // token) or column (B: weight row) r, bytes 0..15 = k 16 g .. 16 g + 15 and
@@ -437,17 +437,28 @@ hipError_t launch_q2k_mi(const uint8_t *table, int64_t num_rows, const int32_t *
 // a lane's scale dword for a step holds the step's four blocks and is
 // shifted right by 8 g.
 //
-// Tables may exceed the 4 GB a buffer descriptor spans, so the rows are read
-// through 64-bit addresses; an id outside the table, or a token past T,
-// reads a zero row (zero codes, so the product is exactly 0 whatever the
-// scale, and zero scale bytes, 2^-127, finite).  Token tiles of 64: the
-// operands of P steps in flight leave no room for 128, and two 64-token
-// tiles, which pull the weight twice per CU, lose to the 256 x 256 tiles of
-// gemm_mx.hip, so this form runs up to 64 tokens.
+// The weight goes straight into registers, P steps ahead.  A column's 64 FP8
+// rows (and their scale dwords) come into the wave's own LDS stage by
+// LDS-DMA one column ahead, through 64-bit addresses (tables may exceed the
+// 4 GB a buffer descriptor spans): 18 requests per column instead of two
+// 16-byte loads per token and step beside the weight stream.  An id outside
+// the table, or a token past T, reads a zero row (zero codes, so the product
+// is exactly 0 whatever the scale, and zero scale bytes, 2^-127, finite).
+// Token tiles of 64: two 64-token tiles, which pull the weight twice per CU,
+// lose to the 256 x 256 tiles of gemm_mx.hip, so this form runs up to 64
+// tokens, and up to kMxSkinnyMaxCols columns (its LDS).
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 __device__ __attribute__((aligned(256))) const uint8_t kMxZeroRow[ENGRAM_HEAD_DIM] = {};
 constexpr uint32_t kMxNoRow = 0xFFFFFFFFu;
+
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(3))) void *lds_addr(T *p) {
+  return (__attribute__((address_space(3))) void *)(p);
+}
+
+constexpr int kMxStageBytes = 64 * ENGRAM_HEAD_DIM + 64 * 8;   // a column: 64 rows + their scales
+constexpr int kMxSkinnyMaxCols = 64;   // LDS: row indices + 4 waves x 2 stages <= 160 KB
 
 template <int NSUB, int P>
 __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_mx_kernel(
@@ -458,8 +469,10 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_mx_kernel(
   constexpr int MI = 4, TM = 16 * MI;
   constexpr int NT = 16 * NSUB;
   constexpr int kStep = 128;                          // k per instruction and step
-  // [waves][64][RS] partial sums, then the row indices [cols][TM]
-  extern __shared__ __attribute__((aligned(16))) float red[];
+  constexpr int kRowDma = TM * ENGRAM_HEAD_DIM / 1024; // 16-byte LDS-DMA instructions per column: 16
+  // K loop: the row indices [cols][TM], then each wave's two column stages;
+  // afterwards the [waves][64][RS] partial sums.
+  extern __shared__ __attribute__((aligned(1024))) float red[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -469,16 +482,16 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_mx_kernel(
   if (n0 >= N) return;                               // whole workgroup: grid rounding
   const int m0 = tile.m * TM;
   const int mrows = min(TM, M - m0);
-  const int cols = K / ENGRAM_HEAD_DIM;
+  const int cols = K / ENGRAM_HEAD_DIM;              // <= kMxSkinnyMaxCols
   const int wcols = cols / kSkinnyWaves;             // table columns of this wave's quarter
-  const int kbeg = wave * wcols * ENGRAM_HEAD_DIM;
+  const int c0 = wave * wcols;
+  const int kbeg = c0 * ENGRAM_HEAD_DIM;
   const int nsteps = wcols * (ENGRAM_HEAD_DIM / kStep);
   const int ks = K / 32;                             // scale bytes per weight row
 
   // Row indices; ids outside the table are counted once per (token,
   // column), by the first column tile.
-  uint32_t *const rowidx =
-      reinterpret_cast<uint32_t *>(red + kSkinnyWaves * kSkinnyM * red_stride<NSUB>());
+  uint32_t *const rowidx = reinterpret_cast<uint32_t *>(red);
   {
     int bad = 0;
     for (int idx = tid; idx < cols * TM; idx += kSkinnyWaves * 64) {
@@ -501,13 +514,13 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_mx_kernel(
   const uint32_t voff_b = uint32_t(r * K + 16 * g);
   const uint32_t voff_bs = uint32_t(r * ks);
 
-  i32x8 fa[P][MI], fb[P][NSUB];
-  uint32_t sa[P][MI], sb[P][NSUB];
+  i32x8 fb[P][NSUB];
+  uint32_t sb[P][NSUB];
   auto cat = [](u32x4 lo, u32x4 hi) {
     return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  // Operands of step u (clamped to the last) into slot `slot`.
-  auto load = [&](const int slot, int u) {
+  // Weight operands of step u (clamped to the last) into slot `slot`.
+  auto load_b = [&](const int slot, int u) {
     u = min(u, nsteps - 1);
     const int k0 = kbeg + u * kStep;
 #pragma unroll
@@ -518,18 +531,50 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_mx_kernel(
       sb[slot][j] = __builtin_amdgcn_raw_buffer_load_b32(rbs, voff_bs + uint32_t(j * 16 * ks),
                                                          k0 / 32, 0);
     }
-    const int col = k0 / ENGRAM_HEAD_DIM, half = u & 1;
+  };
+  // A column's 64 FP8 rows and their scale bytes go into this wave's LDS
+  // stage by LDS-DMA, one column ahead: instruction k brings rows 4 k ..
+  // 4 k + 3 (lane L: row 4 k + L / 16, physical 16-byte chunk L % 16), then
+  // two bring the scale dwords ([2][64]).  Chunk q of row t is stored at
+  // q ^ (t % 16), so the 16 rows a fragment read touches at one logical
+  // chunk sit in 16 different bank groups.  The stage is the wave's own, so
+  // no barrier.
+  uint8_t *const stage = reinterpret_cast<uint8_t *>(rowidx + cols * TM) +
+                         wave * 2 * kMxStageBytes;
+  auto dma_rows = [&](const int buf, int c) {        // wave-local column c (clamped)
+    const uint32_t *ri = rowidx + (c0 + min(c, wcols - 1)) * TM;
+    uint8_t *st = stage + buf * kMxStageBytes;
+    uint32_t ix[kRowDma];                            // all index reads first: one LDS wait
+#pragma unroll
+    for (int k = 0; k < kRowDma; ++k) ix[k] = ri[4 * k + (lane >> 4)];
+#pragma unroll
+    for (int k = 0; k < kRowDma; ++k) {
+      const int t = 4 * k + (lane >> 4);
+      const uint32_t idx = ix[k];
+      const uint8_t *src = (idx != kMxNoRow ? table + int64_t(idx) * ENGRAM_HEAD_DIM : kMxZeroRow) +
+                           16 * ((lane & 15) ^ (t & 15));
+      __builtin_amdgcn_global_load_lds(src, lds_addr(st + k * 1024), 16, 0, 0);
+    }
+    const uint32_t idx = ri[lane];
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const uint8_t *src = idx != kMxNoRow ? tscales + int64_t(idx) * (ENGRAM_HEAD_DIM / 32) + 4 * d
+                                           : kMxZeroRow;
+      __builtin_amdgcn_global_load_lds(src, lds_addr(st + 64 * ENGRAM_HEAD_DIM + d * 256), 4, 0, 0);
+    }
+  };
+  // A operands of half h of the column in stage `buf`.
+  i32x8 fa[MI];
+  uint32_t sa[MI];
+  auto read_a = [&](const int buf, const int h) {
+    const uint8_t *st = stage + buf * kMxStageBytes;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      const uint32_t idx = rowidx[col * TM + 16 * i + r];
-      const bool ok = idx != kMxNoRow;
-      const uint8_t *a = (ok ? table + int64_t(idx) * ENGRAM_HEAD_DIM : kMxZeroRow) +
-                         half * kStep + 16 * g;
-      fa[slot][i] = cat(*reinterpret_cast<const u32x4 *>(a),
-                        *reinterpret_cast<const u32x4 *>(a + 64));
-      const uint8_t *sp = ok ? tscales + int64_t(idx) * (ENGRAM_HEAD_DIM / 32) + 4 * half
-                             : kMxZeroRow;
-      sa[slot][i] = *reinterpret_cast<const uint32_t *>(sp);
+      const uint8_t *row = st + (16 * i + r) * ENGRAM_HEAD_DIM;
+      fa[i] = cat(*reinterpret_cast<const u32x4 *>(row + 16 * ((8 * h + g) ^ r)),
+                  *reinterpret_cast<const u32x4 *>(row + 16 * ((8 * h + 4 + g) ^ r)));
+      sa[i] = *reinterpret_cast<const uint32_t *>(st + 64 * ENGRAM_HEAD_DIM + h * 256 +
+                                                  4 * (16 * i + r));
     }
   };
   f32x4v acc[MI][NSUB];
@@ -540,7 +585,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_mx_kernel(
   auto mma = [&](const int slot) {
     uint32_t xa[MI], xb[NSUB];
 #pragma unroll
-    for (int i = 0; i < MI; ++i) xa[i] = sa[slot][i] >> (8 * g);
+    for (int i = 0; i < MI; ++i) xa[i] = sa[i] >> (8 * g);
 #pragma unroll
     for (int j = 0; j < NSUB; ++j) xb[j] = sb[slot][j] >> (8 * g);
 #pragma unroll
@@ -548,25 +593,48 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_mx_kernel(
 #pragma unroll
       for (int j = 0; j < NSUB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0, xa[i], 0, xb[j]);
+            fa[i], fb[slot][j], acc[i][j], 0, 0, 0, xa[i], 0, xb[j]);
+  };
+  // Step u = 2 c + h of the wave's quarter: h = 0 waits for column c's rows
+  // (only the weight loads of the two steps issued since their DMA may
+  // still be in flight) and requests column c + 1's; then the weight of
+  // step u + P - 1 is requested and step u multiplies.
+  auto step = [&](int u, const int slot, const int h) {
+    const int c = u >> 1;
+    const int buf = c & 1;
+    if (h == 0) {
+      __builtin_amdgcn_s_waitcnt(waitcnt(2 * 3 * NSUB, 15));
+      asm volatile("" ::: "memory");
+      dma_rows(buf ^ 1, c + 1);
+      __builtin_amdgcn_sched_barrier(0);   // the wait above counts the weight loads after these
+    }
+    load_b((slot + P - 1) % P, u + P - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_a(buf, h);
+    mma(slot);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
+  dma_rows(0, 0);
+  __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
+  asm volatile("" ::: "memory");
 #pragma unroll
-  for (int p = 0; p < P - 1; ++p) load(p, p);
-  int s = 0;
-  for (; s + P <= nsteps; s += P) {
+  for (int p = 0; p < P - 1; ++p) load_b(p, p);
+  // nsteps is even; P steps per group, u % P the slot and u % 2 the half.
+  static_assert(P % 2 == 0, "the group of P steps must keep halves in phase");
+  int u = 0;
+  for (; u + P <= nsteps; u += P) {
 #pragma unroll
-    for (int q = 0; q < P; ++q) {
-      load((q + P - 1) % P, s + q + P - 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(q);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int q = 0; q < P; ++q) step(u + q, q, q & 1);
   }
 #pragma unroll
-  for (int q = 0; q < P - 1; ++q)
-    if (s + q < nsteps) mma(q);
+  for (int q = 0; q < P; ++q)
+    if (u + q < nsteps) step(u + q, q, q & 1);
 
+  // The last column requested a (clamped) next one: its LDS-DMA writes must
+  // land before the partial sums reuse the stages.
+  __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
+  asm volatile("" ::: "memory");
   reduce_store<MI, NSUB>(acc, red, C, N, m0, mrows, n0, wave, tid);
 }
 
@@ -575,10 +643,11 @@ hipError_t launch_mx_nsub(const uint8_t *table, const uint8_t *scales, int64_t n
                           const int32_t *ids, int64_t ids_stride, const uint8_t *w_codes,
                           const uint8_t *w_scales, uint16_t *c, int32_t M, int32_t K, int32_t N,
                           int32_t *bad_ids, hipStream_t stream) {
-  constexpr int P = 3;
+  constexpr int P = 4;
   const int cols = K / ENGRAM_HEAD_DIM;
-  const size_t lds = size_t(kSkinnyWaves) * kSkinnyM * red_stride<NSUB>() * sizeof(float) +
-                     size_t(cols) * kSkinnyM * sizeof(uint32_t);
+  const size_t lds = std::max(size_t(kSkinnyWaves) * kSkinnyM * red_stride<NSUB>() * sizeof(float),
+                              size_t(cols) * kSkinnyM * sizeof(uint32_t) +
+                                  size_t(kSkinnyWaves) * 2 * kMxStageBytes);
   const void *fn = reinterpret_cast<const void *>(&gemm_skinny_mx_kernel<NSUB, P>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
@@ -638,7 +707,7 @@ hipError_t launch_project_q2k_skinny(const uint8_t *table, int64_t num_rows, con
 namespace engram {
 
 bool project_mx_skinny_supported(int32_t M, int32_t cols) {
-  return M <= kSkinnyM && cols % kSkinnyWaves == 0;
+  return M <= kSkinnyM && cols % kSkinnyWaves == 0 && cols <= kMxSkinnyMaxCols;
 }
 
 hipError_t launch_project_mx_skinny(const uint8_t *table, const uint8_t *scales, int64_t num_rows,

@@ -266,8 +266,8 @@ ENGRAM_API engram_status engram_quantize_mxfp8(const uint16_t *w, int32_t N, int
  * * 2^(scales[ids[t][r]][i/32] - 127), w = wkv_codes/wkv_scales likewise.
  * The rows are read raw by the block-scaled matrix cores and never
  * dequantised to memory: 256 x 256 output tiles of
- * v_mfma_scale_f32_32x32x64_f8f6f4, or, for T <= 64 with cols % 4 == 0, a
- * kernel that streams the weight once from HBM into
+ * v_mfma_scale_f32_32x32x64_f8f6f4, or, for T <= 64 with cols % 4 == 0 and
+ * cols <= 64, a kernel that streams the weight once from HBM into
  * v_mfma_scale_f32_16x16x128_f8f6f4 with K split four ways per workgroup.
  * The matrix cores sum each instruction's 64 or 128 products below fp32
  * precision (measured: up to 1.7e-4 of the sum of |products| on random e4m3

@@ -913,11 +913,13 @@ def test_hash_at_maximum_sizes(eg):
 
 
 @pytest.mark.parametrize("kind,T,cols,N", [("q2k", 300, 32, 512), ("mx", 130, 40, 300),
-                                           ("mx", 64, 40, 300)])
+                                           ("mx", 64, 40, 300), ("mx", 50, 64, 200),
+                                           ("mx", 64, 68, 200)])
 def test_projection_at_many_columns(eg, kind, T, cols, N):
     # The fused Q2_K projection at its column limit (32) and the MXFP8
-    # projection past it (no column limit; tiles and the weight-streaming
-    # form), against the oracle.
+    # projection past it (no column limit; the tiles, the weight-streaming
+    # form up to its limit of 64 columns, and the tiles past it at 64
+    # tokens), against the oracle.
     rng = np.random.default_rng(cols)
     R, K = 999, cols * 256
     ids_np = rng.integers(0, R, (T, cols)).astype(np.int32)
