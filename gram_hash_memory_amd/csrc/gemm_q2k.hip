@@ -199,6 +199,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
     const int set = (j >> 2) & 1, qs = j & 3;
     __builtin_amdgcn_sched_barrier(0);
     dma_b(stage ^ 1, kt + 1);
+    __builtin_amdgcn_sched_barrier(0);               // the counted wait needs the DMA first
     if (qs == 0 && prefetch) load_block(set ^ 1, kt / 4 + 1);
     __builtin_amdgcn_sched_barrier(0);
     load_b(stage, 1, 1);
