@@ -337,8 +337,10 @@ ENGRAM_API size_t engram_workspace_bytes(int32_t T, int32_t n_layers, int32_t co
  * kv, and one gate pass then applies the layers' gates in order with h held
  * in registers (h read and written once; the same bits as per-layer gates).
  * Q2_K layers within the limits of engram_project_q2k run rows -> projection
- * as that fused kernel (same kv bits) when T > 128.  FP8 layers that carry
- * wkv_mx run engram_project_mxfp8 instead of rows -> projection.
+ * as that fused kernel (same kv bits) when T > 128, or when T <= 128 and
+ * cols % 4 == 0; other few-token Q2_K layers run rows -> the weight-streaming
+ * projection.  FP8 layers that carry wkv_mx run engram_project_mxfp8 instead
+ * of rows -> projection.
  *   layers: HOST array [params->n_layers] of DEVICE-pointer descriptors.
  *   workspace: DEVICE, at least engram_workspace_bytes(...) bytes, 256-byte
  *   aligned; its contents are scratch.  Every other argument is as for the
