@@ -18,10 +18,10 @@ decoders, closed forms or invariants.  The pins cover the oracle's readings
 of the pages and stop there.  Three things stay "parity unpinned" because
 neither the released model nor its files are available:
 * whether DeepSeek's own hash combines the n-gram terms by XOR (reading A1);
-* whether real GGUF Q2_K files use the quant interleave of reading A10;
-* the exact multiplier draw.  Its properties (odd, overflow bound,
-  per-layer) are pinned, but the stream itself is numpy's generator, which
-  the vLLM page names.
+* whether real GGUF Q2_K files use the quant interleave of reading A10.
+The multiplier draw is pinned by literal values computed from the vLLM
+page's rule and by a second, from-scratch implementation of the generator
+that rule names (tests/test_oracle_multipliers.py).
 """
 
 from .layout import is_prime, next_unused_prime, engram_layout, hash_multipliers

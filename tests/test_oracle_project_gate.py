@@ -164,3 +164,88 @@ def test_forward_composes_the_stages():
         h, oracle.gate(wl.h, kv, wl.layers[0].q_weight, wl.layers[0].k_weight, None,
                        s.eps, s.clamp, s.dot_scale))
     assert np.abs(h - wl.h).max() > 0
+
+
+# ------------------------------------------------------------ forward, two layers
+
+def _two_layer_case():
+    """Two tiny Q2_K layers with the real layout and multipliers of layer ids 1 and 14.
+
+    Primes are unique across the model ([vLLM] EngramLayout), so layer 14's
+    buckets differ from layer 1's and its ids differ too.
+    """
+    import workloads
+    max_ngram, n_heads, vocab, start = 4, 2, 1000, 2713
+    T, hc, dim = 48, 2, 128
+    cols = (max_ngram - 1) * n_heads
+    primes, offsets = oracle.engram_layout(2, max_ngram, n_heads, start)
+    mult = oracle.hash_multipliers((1, 14), max_ngram, vocab)
+    num_rows = int(primes.sum(axis=1).max()) + 7
+    rng = np.random.default_rng(7)
+    cids = rng.integers(0, vocab, size=T).astype(np.int32)
+    cu = np.array([0, 20, T], dtype=np.int32)
+    mask = np.ones(T, dtype=np.uint8)
+    mask[[3, 4, 30]] = 0
+    layers = []
+    for l in range(2):
+        q, k = workloads.norm_weights(900, l, hc, dim)
+        layers.append(dict(fmt="q2k", table=workloads.q2k_table(900, l, num_rows), scales=None,
+                           wkv=workloads.wkv_weight(900, l, (hc + 1) * dim, cols * 256),
+                           q_weight=q, k_weight=k))
+    h = workloads.highway(900, T, hc, dim)
+
+    def params(sel):
+        return dict(multipliers=mult[sel], primes=primes[sel], offsets=offsets[sel],
+                    max_ngram=max_ngram, n_heads=n_heads, pad_id=0)
+    return h, cids, cu, mask, layers, params, hc, dim
+
+
+def _zero_value(layer, hc, dim):
+    out = dict(layer)
+    wkv = layer["wkv"].copy()
+    wkv[hc * dim:] = 0                       # value rows of the projection -> value = 0
+    out["wkv"] = wkv
+    return out
+
+
+def test_forward_two_layers_against_single_layers():
+    # With the value gate-identity pinned above (value 0 leaves h bit for bit),
+    # zeroing one layer's value must leave exactly the other layer's single-
+    # layer forward: this pins that layer l hashes with layer l's multipliers
+    # and buckets (ids[:, l]), gathers from layer l's table and gates with
+    # layer l's weights, in order.
+    h, cids, cu, mask, layers, params, hc, dim = _two_layer_case()
+    args = (1e-6, 1e-6, 1 / np.sqrt(dim))
+    both, ids, _ = oracle.forward(h, cids, cu, params([0, 1]), layers, *args, token_mask=mask,
+                                  return_intermediates=True)
+    assert (ids[:, 0] != ids[:, 1]).any(axis=1).all()
+    only1 = oracle.forward(h, cids, cu, params([0]), layers[:1], *args, token_mask=mask)
+    only2 = oracle.forward(h, cids, cu, params([1]), layers[1:], *args, token_mask=mask)
+    first_only = oracle.forward(h, cids, cu, params([0, 1]),
+                                [layers[0], _zero_value(layers[1], hc, dim)], *args,
+                                token_mask=mask)
+    second_only = oracle.forward(h, cids, cu, params([0, 1]),
+                                 [_zero_value(layers[0], hc, dim), layers[1]], *args,
+                                 token_mask=mask)
+    np.testing.assert_array_equal(first_only.view(np.uint32), only1.view(np.uint32))
+    np.testing.assert_array_equal(second_only.view(np.uint32), only2.view(np.uint32))
+    # the layers really differ, and both act in the full forward
+    assert np.abs(only1 - only2).max() > 1e-3
+    assert np.abs(both - only1).max() > 1e-3 and np.abs(both - only2).max() > 1e-3
+
+
+def test_forward_two_layers_apply_in_order():
+    # Layer 2's gate reads the highway layer 1 left (reading A18): the full
+    # forward equals layer 2's single-layer forward started from layer 1's
+    # output; the other order gives a different highway.
+    h, cids, cu, mask, layers, params, hc, dim = _two_layer_case()
+    args = (1e-6, 1e-6, 1 / np.sqrt(dim))
+    both = oracle.forward(h, cids, cu, params([0, 1]), layers, *args, token_mask=mask)
+    after1 = oracle.forward(h, cids, cu, params([0]), layers[:1], *args, token_mask=mask)
+    then2 = oracle.forward(after1, cids, cu, params([1]), layers[1:], *args, token_mask=mask)
+    np.testing.assert_array_equal(both.view(np.uint32), then2.view(np.uint32))
+    after2 = oracle.forward(h, cids, cu, params([1]), layers[1:], *args, token_mask=mask)
+    then1 = oracle.forward(after2, cids, cu, params([0]), layers[:1], *args, token_mask=mask)
+    assert np.abs(both - then1).max() > 0
+    # masked tokens keep their streams through both layers
+    np.testing.assert_array_equal(both[mask == 0].view(np.uint32), h[mask == 0].view(np.uint32))
