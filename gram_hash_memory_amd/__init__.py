@@ -4,8 +4,9 @@ The package is a thin ctypes binding over libengram.so: a C-ABI library of
 hand-written HIP kernels (hash, row gather + dequant, bf16 MFMA projection,
 the projection fused with the Q2_K row dequant, the MXFP8 projection of raw
 FP8 rows, and the gate) plus their composition.  Build the library with
-`python gram_hash_memory_amd/build.py`.  Importing the package without it
-raises ImportError; there is no CPU fallback.
+`python gram_hash_memory_amd/build.py`.  Importing the package without it,
+or with a library built from other sources than those beside it, raises
+ImportError; there is no CPU fallback.
 """
 
 from ._binding import (  # noqa: F401
@@ -14,4 +15,5 @@ from ._binding import (  # noqa: F401
     FP8_SCALE_BYTES, EXPORTS, LIB_PATH, EngramError, HashParams, Tokens, Layer,
     engram_hash, engram_history_update, engram_rows, engram_project, engram_project_q2k, engram_quantize_mxfp8,
     engram_project_mxfp8, engram_gate, engram_gate_layers, engram_workspace_bytes, engram_forward, engram_last_error,
+    engram_build_id, BUILD_ID,
 )

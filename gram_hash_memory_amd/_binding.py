@@ -30,11 +30,32 @@ HEAD_DIM, Q2K_ROW_BYTES, FP8_ROW_BYTES, FP8_SCALE_BYTES = 256, 84, 256, 8
 
 EXPORTS = ("engram_hash", "engram_history_update", "engram_rows", "engram_project", "engram_project_q2k",
            "engram_quantize_mxfp8", "engram_project_mxfp8", "engram_gate",
-           "engram_gate_layers", "engram_workspace_bytes", "engram_forward", "engram_last_error")
+           "engram_gate_layers", "engram_workspace_bytes", "engram_forward", "engram_last_error",
+           "engram_build_id")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python gram_hash_memory_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
+_lib.engram_build_id.restype = c_char_p
+BUILD_ID = _lib.engram_build_id().decode()
+
+
+def _expected_build_id() -> str | None:
+    # The build script beside this file hashes the sources it builds from.
+    import importlib.util
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "build.py")
+    if not os.path.exists(path):
+        return None
+    spec = importlib.util.spec_from_file_location("_engram_build_ids", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.build_id()
+
+
+_want = _expected_build_id()
+if _want is not None and BUILD_ID != _want:
+    raise ImportError(f"{LIB_PATH} was built from other sources ({BUILD_ID}, sources are "
+                      f"{_want}); rebuild with `python gram_hash_memory_amd/build.py`")
 
 
 class _HashParams(ctypes.Structure):
@@ -93,6 +114,11 @@ class EngramError(RuntimeError):
 
 def engram_last_error() -> str:
     return (_lib.engram_last_error() or b"").decode()
+
+
+def engram_build_id() -> str:
+    """sha256 of the sources the loaded library was built from."""
+    return BUILD_ID
 
 
 def _check(status: int) -> None:

@@ -11,6 +11,7 @@ needed: hipcc cross-compiles the device code for gfx950.
 
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -37,6 +38,40 @@ FLAGS = [
 ]
 
 
+def source_files() -> list[str]:
+    """Every file the library is built from: kernels, headers and this script."""
+    files = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC))
+             if f.endswith((".hip", ".hpp", ".cpp", ".h"))]
+    inc = os.path.join(ROOT, "include")
+    files += [os.path.join(inc, f) for f in sorted(os.listdir(inc)) if f.endswith(".h")]
+    return files + [os.path.abspath(__file__)]
+
+
+def source_hash() -> str:
+    """sha256 over the names and contents of source_files(), as hex."""
+    h = hashlib.sha256()
+    for path in source_files():
+        h.update(os.path.relpath(path, ROOT).encode() + b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+        h.update(b"\0")
+    return h.hexdigest()
+
+
+def build_id() -> str:
+    """What engram_build_id() of a library built from the current sources returns."""
+    return "sha256:" + source_hash()
+
+
+def library_is_current() -> bool:
+    """True if LIB exists and was built from the current sources (read from the
+    file, without loading it)."""
+    if not os.path.exists(LIB):
+        return False
+    with open(LIB, "rb") as f:
+        return (b"engram-build-id " + build_id().encode() + b"\0") in f.read()
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -44,9 +79,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libengram.so)")
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, bid: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), "-x", "hip", *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = [f'-DENGRAM_BUILD_ID="{bid}"'] if src == "api.cpp" else []
+    cmd = [hipcc(), "-x", "hip", *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")
@@ -56,8 +92,12 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every source and link libengram.so; returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
+    for stale in os.listdir(BUILD):          # objects of sources that no longer exist
+        if stale.endswith(".o") and stale[:-2] not in {os.path.splitext(f)[0] for f in SOURCES}:
+            os.remove(os.path.join(BUILD, stale))
+    bid = build_id()
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, bid), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -65,7 +105,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")
     os.replace(tmp, LIB)       # atomic: a process that already loaded the old file keeps it
     if verbose:
-        print("built", LIB)
+        print("built", LIB, bid)
     return LIB
 
 

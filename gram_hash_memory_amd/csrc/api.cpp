@@ -162,6 +162,14 @@ extern "C" {
 
 const char *engram_last_error(void) { return g_error; }
 
+// The marker lets a loader check the file's build id without loading it.
+#ifndef ENGRAM_BUILD_ID
+#define ENGRAM_BUILD_ID "unknown"
+#endif
+static const char g_build_id[] = "engram-build-id " ENGRAM_BUILD_ID;
+
+const char *engram_build_id(void) { return g_build_id + sizeof("engram-build-id ") - 1; }
+
 engram_status engram_hash(const engram_hash_params *params, const engram_tokens *tokens,
                           int32_t *ids, hipStream_t stream) {
   engram::HashTables tab;

@@ -11,10 +11,11 @@
 // Tiling (gfx950: 160 KB LDS per CU, 4 SIMDs): a 256 x 256 output tile per
 // workgroup of 4 waves in a 2 x 2 grid.  Each wave owns 128 x 128 = 4 x 4
 // MFMA tiles, whose 256 fp32 accumulators live in AGPRs.  A and B tiles
-// stream through a ring of LDS stages that are filled straight from global
-// memory (buffer_load ... lds, no VGPR staging), several stages ahead of the
-// matrix cores.  Fragment reads from LDS are interleaved one-for-two with
-// the MFMAs, and the chunk swizzle keeps them free of bank conflicts.
+// stream through two LDS stages, each filled from global memory through
+// VGPRs (raw buffer loads, then ds_write_b128) with its loads issued two
+// iterations ahead of the matrix cores.  Fragment reads from LDS are
+// interleaved one-for-two with the MFMAs, and the chunk swizzle keeps them
+// free of bank conflicts.
 //
 // Tile order: the hardware deals workgroups round-robin to the 8 XCDs, each of
 // which has its own L2.  The block id is remapped so that every XCD gets a

@@ -355,6 +355,11 @@ ENGRAM_API engram_status engram_forward(const engram_hash_params *params, const 
 /* Message for the calling thread's last non-OK status ("" if none). */
 ENGRAM_API const char *engram_last_error(void);
 
+/* Identity of the sources this library was built from: "sha256:" and the
+ * hex digest of the kernel sources, headers and build script ("unknown" for
+ * a build outside the package's build script).  A static string. */
+ENGRAM_API const char *engram_build_id(void);
+
 #ifdef __cplusplus
 }
 #endif

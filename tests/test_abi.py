@@ -338,3 +338,18 @@ def test_binding_refuses_host_tensors(eg):
     h = torch.zeros(4, 2, 8)
     with pytest.raises(TypeError):
         eg.engram_gate(h, h, h, h, None, 4, 2, 8, 1e-6, 1e-6, 0.3, stream=0)
+
+
+def test_library_was_built_from_these_sources(eg):
+    # The library records the sha256 of the sources it was built from; the
+    # binding refuses to load a library whose record differs from the tree.
+    import importlib.util
+    path = os.path.join(ROOT, "gram_hash_memory_amd", "build.py")
+    spec = importlib.util.spec_from_file_location("_engram_build_test", path)
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    assert eg.engram_build_id() == b.build_id()
+    assert eg.BUILD_ID.startswith("sha256:") and len(eg.BUILD_ID) == 7 + 64
+    assert b.library_is_current()
+    b.build_id = lambda: "sha256:" + "0" * 64           # as if a source had changed
+    assert not b.library_is_current()
