@@ -89,6 +89,53 @@ def _compile(src: str, bid: str) -> str:
     return obj
 
 
+# Host-side sanitizers for the ABI tests (the device code is built as usual;
+# GPU sanitizers are not used).  Each flag applies to the host compilation only.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+SANITIZED_LIB = os.path.join(BUILD, "sanitized", "libengram_sanitized.so")
+
+
+def sanitizer_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime to preload into a host process."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "lib", "llvm", "bin",
+                         "clang")
+    if not os.path.exists(clang):
+        clang = shutil.which("clang") or "clang"
+    res = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True)
+    return res.stdout.strip()
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """libengram with AddressSanitizer and UndefinedBehaviorSanitizer in its host
+    code, for running the host-side validation tests under the sanitizers."""
+    out = os.path.dirname(SANITIZED_LIB)
+    os.makedirs(out, exist_ok=True)
+    bid = build_id()
+
+    def comp(src):
+        obj = os.path.join(out, os.path.splitext(src)[0] + ".o")
+        extra = [f'-DENGRAM_BUILD_ID="{bid}"'] if src == "api.cpp" else []
+        cmd = [hipcc(), "-x", "hip", *FLAGS, *SANITIZE, *extra, "-c", os.path.join(CSRC, src),
+               "-o", obj]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}{res.stderr}")
+        return obj
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(comp, SOURCES))
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *SANITIZE, "-shared-libsan",
+           *objs, "-o", SANITIZED_LIB]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")
+    if verbose:
+        print("built", SANITIZED_LIB)
+    return SANITIZED_LIB
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link libengram.so; returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
@@ -110,5 +157,8 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--sanitized" in sys.argv[1:]:
+        build_sanitized(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

@@ -109,14 +109,15 @@ __global__ __launch_bounds__(kThreads) void hash_kernel(
 // first) becomes the position that precedes the sequence's next chunk by
 // depth - j -- a position of this chunk, or an older entry of the store.  The
 // thread reads all of its sequence's old entries before it writes any, so
-// the update can run in place.
+// the update can run in place.  The chunk bounds are clamped to [0, T], so
+// that malformed cu_seqlens cannot move an access outside the token arrays.
 __global__ __launch_bounds__(kThreads) void history_kernel(
-    int32_t n_seqs, int32_t depth, const int32_t *__restrict__ cids,
+    int32_t T, int32_t n_seqs, int32_t depth, const int32_t *__restrict__ cids,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ doc_ids,
     const uint8_t *__restrict__ mask, int32_t *hist, uint8_t *live) {
   const int32_t s = int32_t(blockIdx.x) * kThreads + int32_t(threadIdx.x);
   if (s >= n_seqs) return;
-  const int32_t start = cu[s], end = cu[s + 1];
+  const int32_t start = min(max(cu[s], 0), T), end = min(max(cu[s + 1], 0), T);
   if (end <= start) return;                       // an empty chunk changes nothing
   int32_t *h = hist + int64_t(s) * depth;
   uint8_t *l = live + int64_t(s) * depth;
@@ -163,7 +164,8 @@ hipError_t launch_history_update(const engram_tokens &tok, int32_t depth, int32_
                                  uint8_t *history_live, hipStream_t stream) {
   const int64_t blocks = (int64_t(tok.n_seqs) + kThreads - 1) / kThreads;
   hipLaunchKernelGGL(history_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
-                     tok.n_seqs, depth, tok.cids, tok.cu_seqlens, tok.doc_ids, tok.token_mask,
+                     tok.T, tok.n_seqs, depth, tok.cids, tok.cu_seqlens, tok.doc_ids,
+                     tok.token_mask,
                      history, history_live);
   return hipGetLastError();
 }

@@ -55,14 +55,23 @@ extern "C" {
 #define ENGRAM_API
 #endif
 
-typedef enum engram_status {
+/* In C++ the enums get a fixed 32-bit underlying type, so that any int32
+ * value a C caller passes is a valid value to compare (the checks reject
+ * unknown ones) rather than undefined behaviour; the ABI is an int either way. */
+#ifdef __cplusplus
+#define ENGRAM_ENUM_BASE : int32_t
+#else
+#define ENGRAM_ENUM_BASE
+#endif
+
+typedef enum engram_status ENGRAM_ENUM_BASE {
   ENGRAM_OK = 0,
   ENGRAM_ERR_ARG = 1,          /* invalid argument: null, misaligned, bad size     */
   ENGRAM_ERR_UNSUPPORTED = 2,  /* valid for the method, beyond this build's limits */
   ENGRAM_ERR_HIP = 3           /* a HIP launch or runtime call failed             */
 } engram_status;
 
-typedef enum engram_row_format {
+typedef enum engram_row_format ENGRAM_ENUM_BASE {
   ENGRAM_ROWS_Q2K = 0,             /* one 84-byte Q2_K super-block per row        */
   ENGRAM_ROWS_FP8_E4M3_E8M0 = 1    /* 256 e4m3fn bytes + 8 e8m0 bytes per row     */
 } engram_row_format;

@@ -16,10 +16,31 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "engram.h")
 NO_GPU = not os.path.exists("/dev/kfd")
+# Set by tests/test_abi_sanitized.py: run the validation cases against the
+# host-sanitized build of the library, without importing torch.
+SANITIZED_LIB = os.environ.get("ENGRAM_ABI_SANITIZED_LIB")
+
+
+class _Constants:
+    """The binding's constants and workspace helper, for a process that
+    loads only the sanitized library."""
+    ENGRAM_OK, ENGRAM_ERR_ARG, ENGRAM_ERR_UNSUPPORTED, ENGRAM_ERR_HIP = 0, 1, 2, 3
+    ENGRAM_ROWS_Q2K, ENGRAM_ROWS_FP8_E4M3_E8M0 = 0, 1
+
+    def __init__(self, path):
+        self.LIB_PATH = path
+        self._lib = ctypes.CDLL(path)
+        self._lib.engram_workspace_bytes.argtypes = [ctypes.c_int32] * 5
+        self._lib.engram_workspace_bytes.restype = ctypes.c_size_t
+
+    def engram_workspace_bytes(self, *a):
+        return int(self._lib.engram_workspace_bytes(*a))
 
 
 @pytest.fixture(scope="module")
 def eg():
+    if SANITIZED_LIB:
+        return _Constants(SANITIZED_LIB)
     import __graft_entry__
     __graft_entry__._ensure_built()
     import gram_hash_memory_amd
@@ -97,7 +118,7 @@ FAKE = 0x10000      # aligned, never dereferenced by the host checks
 
 
 def _raw(eg):
-    lib = ctypes.CDLL(eg.LIB_PATH)
+    lib = ctypes.CDLL(SANITIZED_LIB or eg.LIB_PATH)
     lib.engram_last_error.restype = ctypes.c_char_p
     lib.engram_hash.argtypes = [ctypes.POINTER(_HP), ctypes.POINTER(_TK), ctypes.c_void_p,
                                 ctypes.c_void_p]
@@ -316,6 +337,39 @@ class TestValidation:
             assert err.startswith("layer 0: ") and msg in err, (kw, err)
         # without wkv_mx the layer needs the bf16 wkv
         assert call(wkv_mx=None, wkv_mx_scales=None) == eg.ENGRAM_ERR_ARG
+
+    def test_forward_rejects(self, eg):
+        lib = _raw(eg)
+        m, p, o = _tables()                       # 6 columns of 7 rows: rows 0..41
+        T, hc, dim = 16, 2, 64
+        Q = eg.ENGRAM_ROWS_Q2K
+        ws_need = eg.engram_workspace_bytes(T, 1, 6, hc, dim)
+
+        def call(num_rows=42, ws=FAKE, ws_bytes=ws_need, n_layers=1, layers=None, **kw):
+            hp = _hp(m, p, o)
+            tk = _TK(T, 1, 0, FAKE, FAKE, None, None, None, None)
+            d = dict(table=FAKE, wkv=FAKE, q_weight=FAKE, k_weight=FAKE)
+            d.update(kw)
+            ly = _LY(Q, num_rows, d["table"], None, d["wkv"], d["q_weight"], d["k_weight"],
+                     None, None)
+            return lib.engram_forward(ctypes.byref(hp), ctypes.byref(tk),
+                                      None if layers == "null" else ctypes.byref(ly), FAKE, hc,
+                                      dim, 1e-6, 1e-6, 0.125, ws, ws_bytes, None, None)
+        # the hash's buckets must lie inside the table: offsets + primes <= num_rows
+        assert call(num_rows=41) == eg.ENGRAM_ERR_ARG
+        err = lib.engram_last_error().decode()
+        assert "offsets + primes" in err and "42" in err and "41" in err, err
+        # the workspace must hold ids, one layer's rows and every layer's kv
+        assert call(ws_bytes=ws_need - 1) == eg.ENGRAM_ERR_ARG
+        assert "workspace_bytes" in lib.engram_last_error().decode()
+        assert call(ws=None) == eg.ENGRAM_ERR_ARG
+        assert call(ws=FAKE + 128) == eg.ENGRAM_ERR_ARG       # not 256-byte aligned
+        assert "256" in lib.engram_last_error().decode()
+        assert call(layers="null") == eg.ENGRAM_ERR_ARG
+        for kw in (dict(table=None), dict(table=FAKE + 2), dict(wkv=None), dict(wkv=FAKE + 8),
+                   dict(q_weight=None), dict(k_weight=FAKE + 4)):
+            assert call(**kw) == eg.ENGRAM_ERR_ARG, kw
+            assert lib.engram_last_error().decode().startswith("layer 0: "), kw
 
     def test_gate_rejects(self, eg):
         lib = _raw(eg)

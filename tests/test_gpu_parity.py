@@ -10,9 +10,11 @@ Bars:
   region of the signed square root, fp32 reductions over dim elements stay
   far inside that.  Masked tokens must be bit-for-bit unchanged.
 
-Full-size workloads are checked on all outputs where the oracle is cheap
-(ids, rows) and on a sample of tokens otherwise (kv, h), at the exact launch
-configuration the benchmark uses.
+Full-size workloads are checked on every output (ids, rows, kv, h), at the
+exact launch configuration the benchmark uses; the oracle's kv of each
+workload layer is computed once (in token chunks) and shared by the tests.
+Ragged-shape tests put sentinel regions before and after every output
+buffer and check that the kernels left them untouched.
 """
 
 import numpy as np
@@ -73,19 +75,6 @@ def binding_objs(eg, c):
     return params, tokens, layers, fmt
 
 
-def sample_tokens(wl, n=96, seed=0):
-    T = wl.spec.T
-    if T <= 128:
-        return np.arange(T)
-    rng = np.random.default_rng(seed)
-    pick = {0, 1, 2, T - 1, T - 2}
-    pick.update(int(c) for c in wl.cu_seqlens[1:-1])             # chunk starts
-    if wl.token_mask is not None:
-        pick.update(np.flatnonzero(wl.token_mask == 0)[:8].tolist())
-    pick.update(rng.choice(T, n, replace=False).tolist())
-    return np.array(sorted(pick))
-
-
 def gpu_rows(eg, c, layer, fmt):
     wl, dw = host(c), dev(c)
     s = wl.spec
@@ -103,6 +92,105 @@ def gpu_rows(eg, c, layer, fmt):
 def bf16_ulp(x):
     x = np.maximum(np.abs(x), 2.0 ** -126)
     return np.ldexp(1.0, np.floor(np.log2(x)).astype(np.int64) - 7)
+
+
+# ------------------------------------------------------------------ guarded buffers
+
+_GUARD_FILL = {torch.int16: 0x5A5A, torch.int32: -0x3C3C3C3D, torch.uint8: 0xA5,
+               torch.float32: 1234.5}
+
+
+class Guarded:
+    """A GPU buffer of `shape` with sentinel regions before and after it.
+
+    The regions are large enough to catch a tile written past the end (a
+    whole 256-row tile of a wide kv); `check()` asserts both are untouched.
+    """
+
+    def __init__(self, shape, dtype, fill, pad=None):
+        n = int(np.prod(shape))
+        row = int(shape[-1]) if len(shape) > 1 else 1
+        self.pad = int(pad if pad is not None else min(1 << 22, max(4096, 260 * row)))
+        self.pad = (self.pad + 63) // 64 * 64       # keeps the view 256-byte aligned
+        self.n = n
+        self.buf = torch.full((self.pad + n + self.pad,), _GUARD_FILL[dtype], dtype=dtype,
+                              device="cuda")
+        self.buf[self.pad:self.pad + n].fill_(fill)
+        self.t = self.buf[self.pad:self.pad + n].view(*shape)
+
+    def check(self):
+        torch.cuda.synchronize()
+        head, tail = self.buf[:self.pad], self.buf[self.pad + self.n:]
+        want = _GUARD_FILL[self.buf.dtype]
+        assert bool((head == want).all()), "a kernel wrote before the output buffer"
+        assert bool((tail == want).all()), "a kernel wrote past the output buffer"
+
+
+# ------------------------------------------------------------ oracle kv, all tokens
+
+_okv, _okv_mx, _omx_w = {}, {}, {}
+CHUNK = 4096
+
+
+def oracle_rows(c, layer, pick=slice(None)):
+    wl = host(c)
+    L = wl.layers[layer]
+    ids = oracle_ids(c)[pick, layer]
+    if wl.spec.fmt == "q2k":
+        return oracle.rows_q2k(L.table, ids)
+    return oracle.rows_fp8(L.table, L.scales, ids)
+
+
+def oracle_kv(c, layer):
+    """The oracle's kv (bf16 bits [T, N]) of every token of a workload layer."""
+    if (c, layer) not in _okv:
+        wl = host(c)
+        T = wl.spec.T
+        parts = [oracle.project(oracle_rows(c, layer, slice(a, a + CHUNK)), wl.layers[layer].wkv)
+                 for a in range(0, T, CHUNK)]
+        _okv[(c, layer)] = np.concatenate(parts)
+    return _okv[(c, layer)]
+
+
+def oracle_forward_h(c, kv_of_layer):
+    """The oracle's gates of every layer in order, over all tokens, from the given kv."""
+    wl = host(c)
+    s = wl.spec
+    out = np.empty_like(wl.h)
+    for a in range(0, s.T, CHUNK):
+        sl = slice(a, a + CHUNK)
+        h = wl.h[sl]
+        mask = None if wl.token_mask is None else wl.token_mask[sl]
+        for l, L in enumerate(wl.layers):
+            h = oracle.gate(h, kv_of_layer(l)[sl], L.q_weight, L.k_weight, mask, s.eps, s.clamp,
+                            s.dot_scale)
+        out[sl] = h
+    return out
+
+
+def _kv_bound_fails(got_bits, want_bits, rel, pairs_of):
+    """Outputs outside |got - want| <= ulp + rel * sum_k |a||b| (bf16 bits in).
+
+    Equal bits and one-ulp differences need no sum of magnitudes; the few
+    others get theirs computed pair by pair from pairs_of(t, o) -> (a, b).
+    """
+    g, w = got_bits.ravel(), want_bits.ravel()
+    diff = np.flatnonzero(g != w)
+    gv, wv = oracle.bf16_value(g[diff]), oracle.bf16_value(w[diff])
+    err = np.abs(gv - wv)
+    ulp = bf16_ulp(np.maximum(np.abs(gv), np.abs(wv)))
+    sel = err > ulp
+    over, err, ulp = diff[sel], err[sel], ulp[sel]
+    n_out = got_bits.shape[1]
+    bad = []
+    for i in range(0, len(over), 4096):
+        t, o = over[i:i + 4096] // n_out, over[i:i + 4096] % n_out
+        a, b = pairs_of(t, o)
+        lim = ulp[i:i + 4096] + rel * np.einsum("ij,ij->i", np.abs(a), np.abs(b))
+        e = err[i:i + 4096]
+        fail = e > lim
+        bad.extend(zip(t[fail].tolist(), o[fail].tolist(), (e / lim)[fail].tolist()))
+    return bad
 
 
 # ------------------------------------------------------------------------- hash
@@ -163,9 +251,11 @@ def test_rows_ragged_token_counts_and_fp8_small(eg, T):
     codes = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     scales = rng.integers(119, 128, (R, 8)).astype(np.uint8)
     ids_np = rng.integers(-2, R + 2, (T, cols)).astype(np.int32)
-    rows = torch.empty((T, cols * 256), dtype=torch.int16, device="cuda")
+    g = Guarded((T, cols * 256), torch.int16, 0x7777)
+    rows = g.t
     eg.engram_rows(eg.ENGRAM_ROWS_FP8_E4M3_E8M0, tensor(codes, "cuda"), tensor(scales, "cuda"),
                    R, tensor(ids_np, "cuda"), cols, cols, T, rows)
+    g.check()
     want = oracle.rows_fp8(codes, scales, ids_np)
     assert np.array_equal(rows.cpu().numpy().view(np.uint16), want)
 
@@ -193,14 +283,34 @@ def test_project_ragged_shapes_full_compare(eg, M, N, K):
     rng = np.random.default_rng(M + N + K)
     a = oracle.bf16_bits(oracle.bf16_round(rng.standard_normal((M, K))))
     b = oracle.bf16_bits(oracle.bf16_round(0.02 * rng.standard_normal((N, K))))
-    kv = torch.full((M, N), 0x7777, dtype=torch.int16, device="cuda")
+    g = Guarded((M, N), torch.int16, 0x7777)
+    kv = g.t
     eg.engram_project(tensor(a, "cuda"), tensor(b, "cuda"), kv, M, K, N)
+    g.check()
     exact = _check_kv(kv.cpu().numpy().view(np.uint16), a, b)
     assert exact > 0.9
 
 
+def check_kv_full(c, layer, got_bits):
+    """Every kv output of a workload layer against the oracle's (projection bar)."""
+    wl = host(c)
+    wkv = oracle.bf16_value(wl.layers[layer].wkv)
+    ids = oracle_ids(c)[:, layer]
+    L = wl.layers[layer]
+
+    def pairs(t, o):
+        u, inv = np.unique(t, return_inverse=True)
+        rows = (oracle.rows_q2k(L.table, ids[u]) if wl.spec.fmt == "q2k"
+                else oracle.rows_fp8(L.table, L.scales, ids[u]))
+        return oracle.bf16_value(rows)[inv], wkv[o]
+    bad = _kv_bound_fails(got_bits, oracle_kv(c, layer), wl.spec.K * 2.0 ** -24, pairs)
+    assert not bad, f"{len(bad)} kv outside the bar, worst {max(b[2] for b in bad):.3f}: {bad[:3]}"
+    return float(np.mean(got_bits == oracle_kv(c, layer)))
+
+
 @pytest.mark.parametrize("c", CONFIGS)
-def test_project_workloads_sampled(eg, c):
+def test_project_workloads_full(eg, c):
+    # rows -> engram_project at the workload's full size, every output.
     wl = host(c)
     s = wl.spec
     _, _, _, fmt = binding_objs(eg, c)
@@ -208,10 +318,9 @@ def test_project_workloads_sampled(eg, c):
         _, rows = gpu_rows(eg, c, layer, fmt)
         kv = torch.empty((s.T, s.N), dtype=torch.int16, device="cuda")
         eg.engram_project(rows, dev(c).layers[layer].wkv, kv, s.T, s.K, s.N)
-        pick = sample_tokens(wl)
-        rows_np = rows.cpu().numpy().view(np.uint16)[pick]
-        got = kv.cpu().numpy().view(np.uint16)[pick]
-        _check_kv(got, rows_np, wl.layers[layer].wkv)
+        exact = check_kv_full(c, layer, kv.cpu().numpy().view(np.uint16))
+        print(f"config {c} layer {layer}: {exact:.4f} of kv bit-exact", flush=True)
+        assert exact > 0.9
 
 
 # ------------------------------------------------- rows + projection, fused (Q2_K)
@@ -250,9 +359,7 @@ def test_project_q2k_bit_identical_to_rows_then_project(eg, c):
         if q2k_same_order(s.T, s.cols):
             diff = int((kv != kv_two).sum().item())
             assert diff == 0, f"layer {layer}: {diff} kv values differ"
-        pick = sample_tokens(wl)
-        want_rows = oracle.rows_q2k(wl.layers[layer].table, oracle_ids(c)[pick, layer])
-        _check_kv(kv.cpu().numpy().view(np.uint16)[pick], want_rows, wl.layers[layer].wkv)
+        check_kv_full(c, layer, kv.cpu().numpy().view(np.uint16))
 
 
 @pytest.mark.parametrize("T,cols,N", [(1, 1, 64), (3, 3, 320), (255, 5, 520), (257, 6, 256),
@@ -275,14 +382,19 @@ def test_project_q2k_ragged_and_bad_ids(eg, T, cols, N):
     ids_np[bad_mask] = rng.choice([-1, R, R + 5, 2**31 - 1, -(2**31)], int(bad_mask.sum()))
     wkv_np = oracle.bf16_bits(oracle.bf16_round(0.05 * rng.standard_normal((N, cols * 256))))
     table, ids, wkv = tensor(table_np, "cuda"), tensor(ids_np, "cuda"), tensor(wkv_np, "cuda")
-    kv = torch.full((T, N), 0x7777, dtype=torch.int16, device="cuda")
+    g_kv = Guarded((T, N), torch.int16, 0x7777)
+    kv = g_kv.t
     bad = torch.zeros(1, dtype=torch.int32, device="cuda")
     eg.engram_project_q2k(table, R, ids, cols, cols, wkv, kv, T, N, bad)
-    rows = torch.empty((T, cols * 256), dtype=torch.int16, device="cuda")
+    g_rows = Guarded((T, cols * 256), torch.int16, 0x7777)
+    rows = g_rows.t
     bad2 = torch.zeros(1, dtype=torch.int32, device="cuda")
     eg.engram_rows(eg.ENGRAM_ROWS_Q2K, table, None, R, ids, cols, cols, T, rows, bad2)
-    kv_two = torch.empty((T, N), dtype=torch.int16, device="cuda")
+    g_two = Guarded((T, N), torch.int16, 0x7777)
+    kv_two = g_two.t
     eg.engram_project(rows, wkv, kv_two, T, cols * 256, N)
+    for g in (g_kv, g_rows, g_two):
+        g.check()
     assert bad.item() == int(bad_mask.sum()) == bad2.item()
     if q2k_same_order(T, cols):
         assert torch.equal(kv, kv_two)
@@ -313,31 +425,34 @@ def test_project_q2k_strided_ids_of_second_layer(eg, T):
 
 @pytest.mark.parametrize("c", CONFIGS)
 def test_gate_with_oracle_kv(eg, c):
-    # Feed the oracle's kv (same bits) so that only the gate arithmetic differs.
+    # Feed the oracle's kv (same bits) so that only the gate arithmetic
+    # differs; every token of the workload.
     wl = host(c)
     s = wl.spec
-    pick = sample_tokens(wl)
     L = wl.layers[0]
-    ids = oracle_ids(c)[pick, 0]
-    rows = (oracle.rows_q2k(L.table, ids) if s.fmt == "q2k"
-            else oracle.rows_fp8(L.table, L.scales, ids))
-    kv = oracle.project(rows, L.wkv)
-    h0 = wl.h[pick]
-    mask = None if wl.token_mask is None else wl.token_mask[pick]
-    want, a = oracle.gate(h0, kv, L.q_weight, L.k_weight, mask, s.eps, s.clamp, s.dot_scale,
-                          return_preact=True)
-    h = tensor(h0, "cuda")
+    kv = oracle_kv(c, 0)
+    h = dev(c).h.clone()
     eg.engram_gate(h, tensor(kv, "cuda"), dev(c).layers[0].q_weight, dev(c).layers[0].k_weight,
-                   None if mask is None else tensor(mask, "cuda"), len(pick), s.hc, s.dim,
-                   s.eps, s.clamp, s.dot_scale)
+                   dev(c).token_mask, s.T, s.hc, s.dim, s.eps, s.clamp, s.dot_scale)
     got = h.cpu().numpy()
-    err = np.abs(got - want) / np.maximum(1.0, np.abs(want))
-    assert err.max() <= 1e-2
-    steady = np.abs(a) > 1e-2
-    assert err[steady].max() <= 1e-4, f"max err away from a=0: {err[steady].max():.2e}"
-    if mask is not None:
-        off = mask == 0
-        assert np.array_equal(got[off].view(np.uint32), h0[off].view(np.uint32))
+    worst, worst_steady = 0.0, 0.0
+    for a0 in range(0, s.T, CHUNK):
+        sl = slice(a0, a0 + CHUNK)
+        mask = None if wl.token_mask is None else wl.token_mask[sl]
+        want, a = oracle.gate(wl.h[sl], kv[sl], L.q_weight, L.k_weight, mask, s.eps, s.clamp,
+                              s.dot_scale, return_preact=True)
+        err = np.abs(got[sl] - want) / np.maximum(1.0, np.abs(want))
+        worst = max(worst, float(err.max()))
+        steady = np.abs(a) > 1e-2
+        if steady.any():
+            worst_steady = max(worst_steady, float(err[steady].max()))
+    print(f"config {c}: gate max rel err {worst:.2e} ({worst_steady:.2e} away from a = 0)",
+          flush=True)
+    assert worst <= 1e-2
+    assert worst_steady <= 1e-4, f"max err away from a=0: {worst_steady:.2e}"
+    if wl.token_mask is not None:
+        off = wl.token_mask == 0
+        assert np.array_equal(got[off].view(np.uint32), wl.h[off].view(np.uint32))
 
 
 def test_gate_value_zero_and_all_masked_are_identity(eg):
@@ -368,9 +483,12 @@ def test_gate_shapes(eg, hc, dim):
     q = oracle.bf16_bits(oracle.bf16_round(1 + 0.1 * rng.standard_normal((hc, dim))))
     k = oracle.bf16_bits(oracle.bf16_round(1 + 0.1 * rng.standard_normal((hc, dim))))
     want = oracle.gate(h0, kv, q, k, None, 1e-6, 1e-6, dim ** -0.5)
-    h = tensor(h0, "cuda")
+    g = Guarded((T, hc, dim), torch.float32, 0.0)
+    h = g.t
+    h.copy_(tensor(h0, "cuda"))
     eg.engram_gate(h, tensor(kv, "cuda"), tensor(q, "cuda"), tensor(k, "cuda"), None, T, hc,
                    dim, 1e-6, 1e-6, dim ** -0.5)
+    g.check()
     err = np.abs(h.cpu().numpy() - want) / np.maximum(1.0, np.abs(want))
     assert err.max() <= 1e-2
 
@@ -390,17 +508,9 @@ def test_forward_against_oracle(eg, c):
                       bad)
     got = h.cpu().numpy()
     assert bad.item() == 0
-    pick = sample_tokens(wl)
-    ids = oracle_ids(c)[pick]
-    want = wl.h[pick]
-    for l, L in enumerate(wl.layers):
-        rows = (oracle.rows_q2k(L.table, ids[:, l]) if s.fmt == "q2k"
-                else oracle.rows_fp8(L.table, L.scales, ids[:, l]))
-        kv = oracle.project(rows, L.wkv)
-        mask = None if wl.token_mask is None else wl.token_mask[pick]
-        want = oracle.gate(want, kv, L.q_weight, L.k_weight, mask, s.eps, s.clamp, s.dot_scale)
-    err = np.abs(got[pick] - want) / np.maximum(1.0, np.abs(want))
-    print(f"config {c}: max rel err {err.max():.3e} over {len(pick)} tokens", flush=True)
+    want = oracle_forward_h(c, lambda l: oracle_kv(c, l))
+    err = np.abs(got - want) / np.maximum(1.0, np.abs(want))
+    print(f"config {c}: max rel err {err.max():.3e} over all {s.T} tokens", flush=True)
     assert err.max() <= 1e-2
     if wl.token_mask is not None:
         off = np.flatnonzero(wl.token_mask == 0)
@@ -437,11 +547,15 @@ def test_forward_kernel_choices_against_oracle(eg, T, max_ngram, n_heads):
     tokens = eg.Tokens(tensor(cids, "cuda"), tensor(cu, "cuda"))
     layer = eg.Layer(eg.ENGRAM_ROWS_Q2K, tensor(table, "cuda"), None, tensor(wkv, "cuda"),
                      tensor(qw, "cuda"), tensor(kw, "cuda"), hc, dim, cols)
-    h = tensor(h0, "cuda")
-    ws = torch.empty(eg.engram_workspace_bytes(T, 1, cols, hc, dim), dtype=torch.uint8,
-                     device="cuda")
+    g_h = Guarded((T, hc, dim), torch.float32, 0.0)
+    h = g_h.t
+    h.copy_(tensor(h0, "cuda"))
+    nws = eg.engram_workspace_bytes(T, 1, cols, hc, dim)
+    g_ws = Guarded((nws,), torch.uint8, 0, pad=1 << 20)
     bad = torch.zeros(1, dtype=torch.int32, device="cuda")
-    eg.engram_forward(params, tokens, [layer], h, hc, dim, eps, clamp, dot_scale, ws, bad)
+    eg.engram_forward(params, tokens, [layer], h, hc, dim, eps, clamp, dot_scale, g_ws.t, bad)
+    g_h.check()
+    g_ws.check()
     got = h.cpu().numpy()
     want = oracle.forward(h0, cids, cu, hp, [dict(fmt="q2k", table=table, scales=None, wkv=wkv,
                                                   q_weight=qw, k_weight=kw)],
@@ -582,10 +696,12 @@ def test_project_mxfp8_ragged_and_bad_ids(eg, T, cols, N, stride):
     w_codes, w_scales = oracle.quantize_mxfp8(wkv_np)
     table, tscales = tensor(table_np, "cuda"), tensor(scales_np, "cuda")
     ids = tensor(ids_full, "cuda")
-    kv = torch.full((T, N), 0x7777, dtype=torch.int16, device="cuda")
+    g = Guarded((T, N), torch.int16, 0x7777)
+    kv = g.t
     bad = torch.zeros(1, dtype=torch.int32, device="cuda")
     eg.engram_project_mxfp8(table, tscales, R, ids.view(-1)[off:], stride, cols,
                             tensor(w_codes, "cuda"), tensor(w_scales, "cuda"), kv, T, N, bad)
+    g.check()
     assert bad.item() == int(bad_mask[:, off:].sum())
     # the GPU's own MXFP8 copy of the weight is the oracle's, bit for bit
     gc, gs = _gpu_mx_weight(eg, tensor(wkv_np, "cuda"), N, K)
@@ -595,10 +711,35 @@ def test_project_mxfp8_ragged_and_bad_ids(eg, T, cols, N, stride):
     assert exact > 0.9, exact
 
 
+def oracle_mx_weight(c, layer):
+    if (c, layer) not in _omx_w:
+        _omx_w[(c, layer)] = _oracle_mx_weight(host(c).layers[layer].wkv)
+    return _omx_w[(c, layer)]
+
+
+def oracle_kv_mx(c, layer):
+    """The oracle's MXFP8 kv (bf16 bits [T, N]) of every token of an FP8 workload layer."""
+    if (c, layer) not in _okv_mx:
+        wl = host(c)
+        L = wl.layers[layer]
+        wc, ws = oracle_mx_weight(c, layer)
+        parts = []
+        for a in range(0, wl.spec.T, CHUNK):
+            ac, asc = oracle.rows_fp8_mx(L.table, L.scales, oracle_ids(c)[a:a + CHUNK, layer])
+            parts.append(oracle.project_mxfp8(ac, asc, wc, ws))
+        _okv_mx[(c, layer)] = np.concatenate(parts)
+    return _okv_mx[(c, layer)]
+
+
+# At the FP8 workload at least this share of the MXFP8 kv must round to the
+# oracle's exact bf16 value: an error in the kernel that stays under the
+# instruction-precision term of the bar would still lower it.
+MX_EXACT_MIN = 0.98
+
+
 @pytest.mark.parametrize("c", FP8_CONFIGS)
-def test_project_mxfp8_workload_sampled(eg, c):
-    # Full size, the launch the forward makes: every token, every output;
-    # checked on sampled tokens x sampled outputs.
+def test_project_mxfp8_workload_full(eg, c):
+    # Full size, the launch the forward makes: every token, every output.
     wl = host(c)
     s = wl.spec
     for layer in range(len(s.layer_ids)):
@@ -613,15 +754,25 @@ def test_project_mxfp8_workload_sampled(eg, c):
                                 ids.view(-1)[layer * s.cols:], len(s.layer_ids) * s.cols,
                                 s.cols, w_codes, w_scales, kv, s.T, s.N, bad)
         assert bad.item() == 0
-        pick = sample_tokens(wl)
-        outs = np.sort(np.random.default_rng(layer).choice(s.N, 1024, replace=False))
-        outs[0], outs[-1] = 0, s.N - 1
+        got_bits = kv.cpu().numpy().view(np.uint16)
+        want_bits = oracle_kv_mx(c, layer)
         hl = wl.layers[layer]
-        a_codes, a_scales = oracle.rows_fp8_mx(hl.table, hl.scales, oracle_ids(c)[pick, layer])
-        wc, ws = oracle.quantize_mxfp8(hl.wkv[outs])
-        got = kv.cpu().numpy().view(np.uint16)[pick][:, outs]
-        exact = _check_kv_mx(got, a_codes, a_scales, wc, ws)
-        print(f"config {c} layer {layer}: {exact:.4f} of sampled kv bit-exact", flush=True)
+        wc, ws = oracle_mx_weight(c, layer)
+        assert np.array_equal(w_codes.cpu().numpy(), wc)
+        assert np.array_equal(w_scales.cpu().numpy(), ws)
+        wv = oracle.mx_values(wc, ws)
+        ids_l = oracle_ids(c)[:, layer]
+
+        def pairs(t, o):
+            u, inv = np.unique(t, return_inverse=True)
+            ac, asc = oracle.rows_fp8_mx(hl.table, hl.scales, ids_l[u])
+            return oracle.mx_values(ac, asc)[inv], wv[o]
+        rel = max(s.K * 2.0 ** -24, MX_SUM_REL)
+        bad_out = _kv_bound_fails(got_bits, want_bits, rel, pairs)
+        assert not bad_out, f"{len(bad_out)} kv outside the bar: {bad_out[:3]}"
+        exact = float(np.mean(got_bits == want_bits))
+        print(f"config {c} layer {layer}: {exact:.4f} of kv bit-exact (MXFP8)", flush=True)
+        assert exact >= MX_EXACT_MIN, exact
 
 
 def _mx_layer(eg, fmt, dl, hc, dim, cols, wkv_mx):
@@ -646,16 +797,9 @@ def test_forward_mx_against_oracle(eg, c):
                       bad)
     got = h.cpu().numpy()
     assert bad.item() == 0
-    pick = sample_tokens(wl)
-    ids = oracle_ids(c)[pick]
-    want = wl.h[pick]
-    for l, L in enumerate(wl.layers):
-        a_codes, a_scales = oracle.rows_fp8_mx(L.table, L.scales, ids[:, l])
-        kv = oracle.project_mxfp8(a_codes, a_scales, *_oracle_mx_weight(L.wkv))
-        mask = None if wl.token_mask is None else wl.token_mask[pick]
-        want = oracle.gate(want, kv, L.q_weight, L.k_weight, mask, s.eps, s.clamp, s.dot_scale)
-    err = np.abs(got[pick] - want) / np.maximum(1.0, np.abs(want))
-    print(f"config {c} (MXFP8): max rel err {err.max():.3e} over {len(pick)} tokens", flush=True)
+    want = oracle_forward_h(c, lambda l: oracle_kv_mx(c, l))
+    err = np.abs(got - want) / np.maximum(1.0, np.abs(want))
+    print(f"config {c} (MXFP8): max rel err {err.max():.3e} over all {s.T} tokens", flush=True)
     assert err.max() <= 1e-2
     if wl.token_mask is not None:
         off = np.flatnonzero(wl.token_mask == 0)
