@@ -24,6 +24,13 @@
 // values (v % 16 in 8h .. 8h + 7) fall in the four 8-byte pieces at quant
 // bytes 16 p + 8 h, p = 0..3.  The blocks of a column are loaded one column
 // ahead; their ids are resolved into byte offsets once, before the K loop.
+// Values are rounded once for every finite d, dmin (q2k_decode.hpp).  The
+// tiles decode with one fma per value, which is exact unless a block's d and
+// dmin lie far apart; a second, small launch then checks every M-tile's
+// blocks and recomputes, with the exact group decode, the tiles of any
+// M-tile that has such a block (gemm_q2k_exact_kernel).
+#include <algorithm>
+
 #include "gemm_common.hpp"
 #include "q2k_decode.hpp"
 
@@ -43,17 +50,16 @@ struct Q2kPart {
   uint32_t dd;       // fp16 d | fp16 dmin << 16
 };
 
-__global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
+// One 256 x 256 output tile (tm, tn); kExact picks the group decode.
+template <bool kExact>
+__device__ __forceinline__ void q2k_tile(
     const uint8_t *__restrict__ table, int64_t num_rows, const int32_t *__restrict__ ids,
     int64_t ids_stride, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
-    int M, int N, int K, int tiles_m, int tiles_n, int32_t *__restrict__ bad_ids) {
+    int M, int N, int K, int tm, int tn, int32_t *__restrict__ bad_ids, uint16_t *smem) {
   constexpr int BK = 64;
   constexpr int kStageElems = BN * BK;                 // B only: 32 KB
   constexpr int kSegs = BN * BK * 2 / 1024 / kWaves;   // 1 KB B segments per wave per stage: 8
-  extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
 
-  int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -135,7 +141,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
 #pragma unroll
     for (int i = 0; i < kRowsPerLane; ++i) {
       const Q2kPart &b = blk[set][i];
-      const Q2kPlanes pl = q2k_group_planes(b.dd, (b.sc[qs] >> (8 * ks)) & 0xFFu);
+      const uint32_t sm = (b.sc[qs] >> (8 * ks)) & 0xFFu;
+      const Q2kPlanes pl = kExact ? q2k_group_planes_exact(b.dd, sm) : q2k_group_planes(b.dd, sm);
       fa[slot][i] = __builtin_bit_cast(bf16x8, q2k_expand8(pl, b.q[p][0], b.q[p][1], shift));
     }
   };
@@ -253,6 +260,45 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
   store_tile_blocks<kRowsPerLane, kNJ>(acc, smem, C, M, N, m0, n0, wave * 64, 0, lane, tid);
 }
 
+__global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
+    const uint8_t *__restrict__ table, int64_t num_rows, const int32_t *__restrict__ ids,
+    int64_t ids_stride, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
+    int M, int N, int K, int tiles_m, int tiles_n, int32_t *__restrict__ bad_ids) {
+  extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  q2k_tile<false>(table, num_rows, ids, ids_stride, B, C, M, N, K, tm, tn, bad_ids, smem);
+}
+
+// Runs after gemm_q2k_kernel on the same stream.  Workgroup (tm, g) checks
+// the d/dmin of every block of M-tile tm; if any lies outside the one-fma
+// range (q2k_fp32_exact), it recomputes tiles (tm, g), (tm, g + split), ...
+// with the exact group decode, overwriting what the first launch stored.
+// Otherwise it exits after the check.
+__global__ __launch_bounds__(kThreads, 1) void gemm_q2k_exact_kernel(
+    const uint8_t *__restrict__ table, int64_t num_rows, const int32_t *__restrict__ ids,
+    int64_t ids_stride, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
+    int M, int N, int K, int tiles_n, int split) {
+  extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
+  const int tm = int(blockIdx.x) / split, g = int(blockIdx.x) % split;
+  const int cols = K / ENGRAM_HEAD_DIM;
+  const int row = tm * BM + int(threadIdx.x);
+  bool fast = true;
+  if (row < M) {
+    for (int c = 0; c < cols; ++c) {
+      const int32_t id = ids[int64_t(row) * ids_stride + c];
+      if (id >= 0 && id < num_rows)
+        fast &= q2k_fp32_exact(
+            *reinterpret_cast<const uint32_t *>(table + int64_t(id) * ENGRAM_Q2K_ROW_BYTES + 80));
+    }
+  }
+  if (__syncthreads_and(fast)) return;
+  for (int tn = g; tn < tiles_n; tn += split) {
+    __syncthreads();                               // the previous tile is done with the LDS
+    q2k_tile<true>(table, num_rows, ids, ids_stride, B, C, M, N, K, tm, tn, nullptr, smem);
+  }
+}
+
 }  // namespace
 
 static_assert(ENGRAM_Q2K_FUSED_MAX_BYTES + 128 <= int64_t(kNoRow),
@@ -276,12 +322,21 @@ hipError_t launch_project_q2k(const uint8_t *table, int64_t num_rows, const int3
                          size_t(cols) * kThreads * sizeof(uint32_t);
   const size_t lds_epilogue = size_t(BM) * BN * sizeof(uint16_t);
   const size_t lds = lds_loop > lds_epilogue ? lds_loop : lds_epilogue;
-  const void *fn = reinterpret_cast<const void *>(&gemm_q2k_kernel);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-  if (e != hipSuccess) return e;
+  for (const void *fn : {reinterpret_cast<const void *>(&gemm_q2k_kernel),
+                         reinterpret_cast<const void *>(&gemm_q2k_exact_kernel)}) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(gemm_q2k_kernel, dim3(tiles_m * tiles_n), dim3(kThreads), lds, stream,
                      table, num_rows, ids, ids_token_stride, w, c, M, N, K, tiles_m, tiles_n,
                      bad_ids);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // About one checking workgroup per CU; each recomputes every split-th tile
+  // of its M-tile when that M-tile needs the exact decode.
+  const int split = std::max(1, std::min(tiles_n, (256 + tiles_m - 1) / tiles_m));
+  hipLaunchKernelGGL(gemm_q2k_exact_kernel, dim3(tiles_m * split), dim3(kThreads), lds, stream,
+                     table, num_rows, ids, ids_token_stride, w, c, M, N, K, tiles_n, split);
   return hipGetLastError();
 }
 

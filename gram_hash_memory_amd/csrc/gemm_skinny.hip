@@ -232,7 +232,15 @@ size_t q2k_skinny_loop_lds(int cols) {
          sizeof(uint32_t);
 }
 
-template <int MI, int NSUB, int P>
+// How a weight-streaming Q2_K kernel decodes (q2k_decode.hpp): kQ2kVote
+// votes per column and wave between the one-fma and the exact group decode;
+// kQ2kFast always takes the one-fma decode, and kQ2kExactFixup, launched
+// after it, checks its tile's blocks and, only if one needs it, recomputes
+// the tile with the exact decode (for the 128-token tiles, which have no
+// registers to spare for both decodes in one kernel).
+enum Q2kDecode { kQ2kVote, kQ2kFast, kQ2kExactFixup };
+
+template <int MI, int NSUB, int P, Q2kDecode kMode>
 __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
     const uint8_t *__restrict__ table, int64_t num_rows, const int32_t *__restrict__ ids,
     int64_t ids_stride, const uint16_t *__restrict__ B, uint16_t *__restrict__ C, int M, int N,
@@ -260,6 +268,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
   // Block offsets; ids outside the table are counted once per (token,
   // column), by the first column tile.
   uint32_t *const offs = reinterpret_cast<uint32_t *>(red);
+  bool fast = true;
   {
     int bad = 0;
     for (int idx = tid; idx < cols * TM; idx += kSkinnyWaves * 64) {
@@ -269,10 +278,17 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
       const bool ok = id >= 0 && id < num_rows;
       bad += row_ok && !ok;
       offs[c * TM + t] = row_ok && ok ? uint32_t(id) * ENGRAM_Q2K_ROW_BYTES : kQ2kNoRow;
+      if (kMode == kQ2kExactFixup && row_ok && ok)
+        fast &= q2k_fp32_exact(*reinterpret_cast<const uint32_t *>(
+            table + int64_t(id) * ENGRAM_Q2K_ROW_BYTES + 80));
     }
     if (bad && tile.n == 0 && bad_ids) atomicAdd(bad_ids, bad);
   }
-  __syncthreads();
+  if (kMode == kQ2kExactFixup) {
+    if (__syncthreads_and(fast)) return;           // the first launch was exact already
+  } else {
+    __syncthreads();
+  }
 
   const __amdgpu_buffer_rsrc_t rt = make_rsrc(table, num_rows * ENGRAM_Q2K_ROW_BYTES);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + int64_t(n0) * K, int64_t(N - n0) * K * 2);
@@ -281,7 +297,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
   const uint32_t sub_step = uint32_t(16 * K) * 2;       // 16 rows further
 
   u32x4 fb[P][NSUB];
-  auto load_b = [&](const int slot, int step) {
+  auto load_b = [&](const int slot, int step) __attribute__((always_inline)) {
     const int k0 = kbeg + min(step, nsteps - 1) * 32;
 #pragma unroll
     for (int j = 0; j < NSUB; ++j)
@@ -298,7 +314,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
   constexpr int kDmaChunk = (kDmaPerCol + kDmaSteps - 1) / kDmaSteps;
   uint32_t *const stage_lds = offs + cols * TM + wave * 2 * kDmaPerCol * 64;
   const int dl_tok = lane / 21, dl_dw = lane % 21;
-  auto dma_blocks = [&](const int buf, int c, const int kb, const int ke) {
+  auto dma_blocks = [&](const int buf, int c, const int kb, const int ke) __attribute__((always_inline)) {
     const uint32_t *o = offs + (c0 + min(c, wcols - 1)) * TM;   // wave-local column c, clamped
 #pragma unroll
     for (int k = kb; k < ke; ++k) {
@@ -320,7 +336,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
   }
   uint32_t sc[2][MI], dd[MI];
   u32x2 qq[2][MI];
-  auto read_step = [&](const int buf, const int s) {
+  auto read_step = [&](const int buf, const int s) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const uint32_t *b = tok[i] + buf * kDmaPerCol * 64;
@@ -329,14 +345,27 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
     }
   };
   // A fragments of step s of the column: 16-value group 2 s + g / 2
-  // (q2k_decode.hpp).
+  // (q2k_decode.hpp).  When any block of the column on this wave has d and
+  // dmin too far apart for one fma per value (col_fast false, a wave-uniform
+  // vote at the column start), the whole column takes the exact group decode.
   const int sc_shift = 8 * (kg >> 1);
-  auto decode = [&](const int s, u32x4 (&fa)[MI]) {
+  bool col_fast = kMode == kQ2kFast;
+  auto decode = [&](const int s, u32x4 (&fa)[MI]) __attribute__((always_inline)) {
+    if (kMode == kQ2kFast || (kMode == kQ2kVote && col_fast)) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const Q2kPlanes pl =
-          q2k_group_planes(dd[i], (sc[s & 1][i] >> (16 * (s & 1) + sc_shift)) & 0xFFu);
-      fa[i] = q2k_expand8(pl, qq[s & 1][i][0], qq[s & 1][i][1], 2 * (s & 3));
+      for (int i = 0; i < MI; ++i) {
+        const uint32_t sm = (sc[s & 1][i] >> (16 * (s & 1) + sc_shift)) & 0xFFu;
+        fa[i] = q2k_expand8(q2k_group_planes(dd[i], sm), qq[s & 1][i][0], qq[s & 1][i][1],
+                            2 * (s & 3));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {      // one token at a time: few extra registers
+        const uint32_t sm = (sc[s & 1][i] >> (16 * (s & 1) + sc_shift)) & 0xFFu;
+        fa[i] = q2k_expand8(q2k_group_planes_exact(dd[i], sm), qq[s & 1][i][0],
+                            qq[s & 1][i][1], 2 * (s & 3));
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
   f32x4v acc[MI][NSUB];
@@ -347,13 +376,18 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
   // One table column: its 8 steps, B of step t + P - 1 requested while step t
   // multiplies (step t's B sits in slot t % P), and the blocks of the next
   // column requested over its first kDmaSteps steps.
-  auto column = [&](int c, const int set) {
+  auto column = [&](int c, const int set) __attribute__((always_inline)) {
     // Column c's blocks landed: only the B loads issued after the last of
     // their DMA instructions (9 - kDmaSteps steps' worth) may be in flight.
     __builtin_amdgcn_s_waitcnt(waitcnt((9 - kDmaSteps) * NSUB, 15));
     asm volatile("" ::: "memory");
+    bool col_ok = true;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) dd[i] = tok[i][set * kDmaPerCol * 64 + 20];
+    for (int i = 0; i < MI; ++i) {
+      dd[i] = tok[i][set * kDmaPerCol * 64 + 20];
+      col_ok &= q2k_fp32_exact(dd[i]);
+    }
+    if (kMode == kQ2kVote) col_fast = __builtin_amdgcn_ballot_w64(!col_ok) == 0;
     read_step(set, 0);
 #pragma unroll
     for (int s = 0; s < ENGRAM_HEAD_DIM / 32; ++s) {
@@ -395,21 +429,38 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
   reduce_store<MI, NSUB>(acc, red, C, N, m0, mrows, n0, wave, tid);
 }
 
-template <int MI, int NSUB>
-hipError_t launch_q2k_nsub(const uint8_t *table, int64_t num_rows, const int32_t *ids,
+template <int MI, int NSUB, Q2kDecode kMode>
+hipError_t launch_q2k_mode(const uint8_t *table, int64_t num_rows, const int32_t *ids,
                            int64_t ids_stride, const uint16_t *w, uint16_t *c, int32_t M,
                            int32_t K, int32_t N, int32_t *bad_ids, hipStream_t stream) {
   constexpr int P = 4;
   const int cols = K / ENGRAM_HEAD_DIM;
   const size_t lds = std::max(size_t(kSkinnyWaves) * kSkinnyM * red_stride<NSUB>() * sizeof(float),
                               q2k_skinny_loop_lds<MI>(cols));
-  const void *fn = reinterpret_cast<const void *>(&gemm_skinny_q2k_kernel<MI, NSUB, P>);
+  const void *fn = reinterpret_cast<const void *>(&gemm_skinny_q2k_kernel<MI, NSUB, P, kMode>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
   const dim3 grid = skinny_grid(M, N, 16 * NSUB, 16 * MI);
-  hipLaunchKernelGGL((gemm_skinny_q2k_kernel<MI, NSUB, P>), grid, dim3(kSkinnyWaves * 64), lds,
-                     stream, table, num_rows, ids, ids_stride, w, c, M, N, K, bad_ids);
+  hipLaunchKernelGGL((gemm_skinny_q2k_kernel<MI, NSUB, P, kMode>), grid,
+                     dim3(kSkinnyWaves * 64), lds, stream, table, num_rows, ids, ids_stride, w,
+                     c, M, N, K, bad_ids);
   return hipGetLastError();
+}
+
+template <int MI, int NSUB>
+hipError_t launch_q2k_nsub(const uint8_t *table, int64_t num_rows, const int32_t *ids,
+                           int64_t ids_stride, const uint16_t *w, uint16_t *c, int32_t M,
+                           int32_t K, int32_t N, int32_t *bad_ids, hipStream_t stream) {
+  if constexpr (MI == 4) {
+    return launch_q2k_mode<MI, NSUB, kQ2kVote>(table, num_rows, ids, ids_stride, w, c, M, K, N,
+                                               bad_ids, stream);
+  } else {
+    hipError_t e = launch_q2k_mode<MI, NSUB, kQ2kFast>(table, num_rows, ids, ids_stride, w, c,
+                                                       M, K, N, bad_ids, stream);
+    if (e != hipSuccess) return e;
+    return launch_q2k_mode<MI, NSUB, kQ2kExactFixup>(table, num_rows, ids, ids_stride, w, c, M,
+                                                     K, N, nullptr, stream);
+  }
 }
 
 template <int NSUB>

@@ -1,5 +1,17 @@
 // Q2_K dequant straight into bf16 MFMA operands, shared by the fused
-// projections (gemm_q2k.hip, gemm_skinny.hip).
+// projections (gemm_q2k.hip, gemm_skinny.hip), and the exact value rule
+// shared with engram_rows (rows.hip).
+//
+// Every value is y = d*scale*q - dmin*min rounded to bf16 once, for every
+// finite fp16 d and dmin.  d*scale (<= 15 significant bits), q*d*scale (<= 17)
+// and dmin*min (<= 15) are exact in fp32.  When the fp16 exponents of d and
+// dmin (subnormals counted as exponent field 1) differ by -9 .. 7, or one of
+// them is zero, y is 2^min(E) times an integer below 2^24, so one fp32 fma
+// gives y exactly and the bf16 rounding is the only one (q2k_fp32_exact).
+// Other blocks take q2k_exact_odd: the fp32 difference and its exact
+// rounding error (Knuth's TwoSum), the difference rounded to odd with that
+// error, then rounded to bf16 to nearest even -- one rounding of y (rounding
+// to odd at 24 bits then to nearest at 8 <= 24 - 2 bits; Boldo and Melquiond).
 //
 // [spark engram_v41 page, ENGRAM_ROW_BYTES]: a Q2_K row is one 84-byte
 // block; within a 16-value group the scale and min are fixed, so a value
@@ -20,6 +32,28 @@ struct Q2kPlanes {
   uint32_t lo, hi;
 };
 
+// dd = fp16 d | fp16 dmin << 16.  True when one fp32 fma per value is exact
+// for the whole block (see above); non-finite d or dmin also take that path
+// (their values are inf or NaN either way).
+__device__ __forceinline__ bool q2k_fp32_exact(uint32_t dd) {
+  const uint32_t ed = (dd >> 10) & 31u, em = (dd >> 26) & 31u;
+  const int gap = int(ed > 1u ? ed : 1u) - int(em > 1u ? em : 1u);
+  return (dd & 0x7FFFu) == 0 || (dd & 0x7FFF0000u) == 0 || ed == 31u || em == 31u ||
+         (gap >= -9 && gap <= 7);
+}
+
+// a - b rounded to odd at fp32 precision, for exact fp32 a and b: rounding
+// the result to bf16 to nearest even rounds a - b once.
+__device__ __forceinline__ float q2k_exact_odd(float a, float b) {
+  const float s = __fsub_rn(a, b);
+  const float bv = __fsub_rn(s, a);                 // TwoSum of a and -b
+  const float av = __fsub_rn(s, bv);
+  const float e = __fadd_rn(__fsub_rn(a, av), __fsub_rn(-b, bv));
+  uint32_t t = __float_as_uint(s);
+  if (e != 0.0f && (t & 1u) == 0u) t += ((__float_as_uint(e) ^ t) >> 31) ? 0xFFFFFFFFu : 1u;
+  return __uint_as_float(t);
+}
+
 // The group's planes from its scale/min byte sm (low nibble scale, high
 // nibble min) and dd = fp16 d | fp16 dmin << 16.
 __device__ __forceinline__ Q2kPlanes q2k_group_planes(uint32_t dd, uint32_t sm) {
@@ -28,6 +62,16 @@ __device__ __forceinline__ Q2kPlanes q2k_group_planes(uint32_t dd, uint32_t sm) 
   const float dl = d * float(sm & 0xFu), ml = dmin * float(sm >> 4);
   const uint32_t p01 = pack_bf16x2(fmaf(0.0f, dl, -ml), fmaf(1.0f, dl, -ml));
   const uint32_t p23 = pack_bf16x2(fmaf(2.0f, dl, -ml), fmaf(3.0f, dl, -ml));
+  return {__builtin_amdgcn_perm(p23, p01, 0x06040200u), __builtin_amdgcn_perm(p23, p01, 0x07050301u)};
+}
+
+// q2k_group_planes for any finite d, dmin: each of the four values rounded once.
+__device__ __forceinline__ Q2kPlanes q2k_group_planes_exact(uint32_t dd, uint32_t sm) {
+  const float d = float(__builtin_bit_cast(_Float16, uint16_t(dd & 0xFFFFu)));
+  const float dmin = float(__builtin_bit_cast(_Float16, uint16_t(dd >> 16)));
+  const float dl = d * float(sm & 0xFu), ml = dmin * float(sm >> 4);
+  const uint32_t p01 = pack_bf16x2(-ml, q2k_exact_odd(dl, ml));
+  const uint32_t p23 = pack_bf16x2(q2k_exact_odd(2.0f * dl, ml), q2k_exact_odd(3.0f * dl, ml));
   return {__builtin_amdgcn_perm(p23, p01, 0x06040200u), __builtin_amdgcn_perm(p23, p01, 0x07050301u)};
 }
 

@@ -16,6 +16,7 @@
 // flight: it issues all their loads before it dequantises any of them.
 // The random reads are latency-bound; the bf16 write is the bandwidth term.
 #include "common.hpp"
+#include "q2k_decode.hpp"
 
 namespace engram {
 namespace {
@@ -82,10 +83,18 @@ __global__ __launch_bounds__(kThreads) void rows_q2k_kernel(
     const float dl = half_to_float(dd[k] & 0xFFFFu) * float(sm & 0xFu);
     const float ml = half_to_float(dd[k] >> 16) * float(sm >> 4);
     float y[8];
+    // One fma per value is exact for most blocks; the others (d and dmin
+    // far apart) round their difference to odd first (q2k_decode.hpp).
+    float q[8];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const uint32_t byte = ((b < 4 ? q0[k] : q1[k]) >> (8 * (b & 3))) & 0xFFu;
-      y[b] = dl * float((byte >> q_shift) & 3u) - ml;
+    for (int b = 0; b < 8; ++b)
+      q[b] = float(((((b < 4 ? q0[k] : q1[k]) >> (8 * (b & 3))) & 0xFFu) >> q_shift) & 3u);
+    if (q2k_fp32_exact(dd[k])) {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) y[b] = fmaf(q[b], dl, -ml);
+    } else {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) y[b] = q2k_exact_odd(q[b] * dl, ml);
     }
     u32x4 v;
     v[0] = pack_bf16x2(y[0], y[1]);

@@ -206,9 +206,9 @@ ENGRAM_API engram_status engram_history_update(const engram_tokens *tokens, int3
  *   Q2_K value i of a block: bytes 0..15 hold (min << 4 | scale) per 16
  *     values, bytes 16..79 the 2-bit quants (value i: byte
  *     16 + 32*(i/128) + i%32, bits 2*((i%128)/32)), bytes 80..81 fp16 d,
- *     82..83 fp16 dmin; y = d*scale*q - dmin*min in fp32, then bf16.
- *     This equals the exact value whenever d and dmin are within 2^6 of
- *     each other.
+ *     82..83 fp16 dmin; y = d*scale*q - dmin*min, rounded to bf16 once from
+ *     its exact value for every finite d and dmin (non-finite d or dmin give
+ *     unspecified inf/NaN values).
  *   FP8 value i: e4m3fn code times 2^(scales[row][i/32] - 127) (the byte is
  *     placed in the binary32 exponent field, so byte 0 gives 0), then bf16.
  *   An id outside [0, num_rows) yields a zero row; if bad_ids (DEVICE int32,

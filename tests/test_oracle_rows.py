@@ -155,3 +155,71 @@ def test_rows_layout_is_token_major_then_column():
     np.testing.assert_array_equal(rows[0, 256:], single(7))
     np.testing.assert_array_equal(rows[1, :256], single(1))
     np.testing.assert_array_equal(rows[1, 256:], single(3))
+
+
+# ----------------------------------------------- crafted blocks: one rounding for every fp16
+
+def _bf16_of_fraction(x):
+    """Round an exact rational to the nearest bf16 value, ties to even (from the definition)."""
+    from fractions import Fraction
+    if x == 0:
+        return 0.0
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()     # 2^e <= a < 2^(e+2)
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    quantum = Fraction(2) ** (max(e, -126) - 7)                    # 8 significant bits
+    n = a / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * float(fl * quantum)
+
+
+def _crafted_q2k_blocks():
+    """Blocks whose d and dmin lie far apart or at the ends of fp16, where a
+    float32 evaluation of d*scale*q - dmin*min is no longer exact."""
+    rng = np.random.default_rng(8)
+    pairs = [(0x6C00, 0x0001),   # d = 4096, dmin = 2^-24 (smallest subnormal): ratio 2^36
+             (0x5BFF, 0x1C01),   # ratio ~2^12
+             (0x4000, 0x0C00),   # d = 2, dmin = 2^-12: ratio 2^13
+             (0x0200, 0x7BFF),   # d subnormal, dmin = 65504
+             (0x0000, 0x3555),   # d = 0
+             (0x3C00, 0x0000),   # dmin = 0
+             (0xBC00, 0x2000),   # negative d
+             (0x7BFF, 0x83FF),   # largest d, negative subnormal dmin
+             (0x1400, 0x6400)]   # dmin 2^20 times d
+    blocks = []
+    for d_bits, m_bits in pairs:
+        b = rng.integers(0, 256, 84).astype(np.uint8)
+        b[80], b[81] = d_bits & 0xFF, d_bits >> 8
+        b[82], b[83] = m_bits & 0xFF, m_bits >> 8
+        blocks.append(b)
+    for _ in range(40):                       # random finite d, dmin over the whole fp16 range
+        b = rng.integers(0, 256, 84).astype(np.uint8)
+        for k in (80, 82):
+            bits = int(rng.integers(0, 0x7C00)) | (int(rng.integers(0, 2)) << 15)
+            b[k], b[k + 1] = bits & 0xFF, bits >> 8
+        blocks.append(b)
+    return np.stack(blocks)
+
+
+def test_q2k_crafted_blocks_round_once_from_the_exact_value():
+    # The oracle's value for any finite fp16 d, dmin is the exact rational
+    # d*scale*q - dmin*min rounded to bf16 once -- including blocks where d
+    # and dmin are 2^12 .. 2^36 apart, subnormal, zero or negative.
+    from fractions import Fraction
+    blocks = _crafted_q2k_blocks()
+    rows = oracle.bf16_value(oracle.rows_q2k(blocks, np.arange(len(blocks))[:, None]))
+    for r, blk in enumerate(blocks):
+        d = Fraction(float(np.frombuffer(blk[80:82].tobytes(), "<f2")[0]))
+        dm = Fraction(float(np.frombuffer(blk[82:84].tobytes(), "<f2")[0]))
+        for i in range(0, 256, 3):
+            byte = int(blk[16 + 32 * (i // 128) + i % 32])
+            q = (byte >> (2 * ((i % 128) // 32))) & 3
+            sc, mn = int(blk[i // 16]) & 15, int(blk[i // 16]) >> 4
+            assert rows[r, i] == _bf16_of_fraction(d * sc * q - dm * mn), (r, i)
