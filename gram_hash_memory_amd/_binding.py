@@ -31,7 +31,7 @@ HEAD_DIM, Q2K_ROW_BYTES, FP8_ROW_BYTES, FP8_SCALE_BYTES = 256, 84, 256, 8
 EXPORTS = ("engram_hash", "engram_history_update", "engram_rows", "engram_project", "engram_project_q2k",
            "engram_quantize_mxfp8", "engram_project_mxfp8", "engram_gate",
            "engram_gate_layers", "engram_workspace_bytes", "engram_forward", "engram_last_error",
-           "engram_build_id")
+           "engram_build_id", "engram_forward_noalloc")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python gram_hash_memory_amd/build.py`")
@@ -99,10 +99,13 @@ _lib.engram_workspace_bytes.restype = c_size_t
 _lib.engram_forward.argtypes = [_P(_HashParams), _P(_Tokens), _P(_Layer), c_void_p, c_int32,
                                 c_int32, c_float, c_float, c_float, c_void_p, c_size_t,
                                 c_void_p, c_void_p]
+_lib.engram_forward_noalloc.argtypes = [_P(_HashParams), _P(_Tokens), _P(_Layer), c_void_p,
+                                        c_int32, c_int32, c_float, c_float, c_float, c_void_p,
+                                        c_void_p]
 _lib.engram_last_error.restype = c_char_p
 for _name in ("engram_hash", "engram_history_update", "engram_rows", "engram_project", "engram_project_q2k",
               "engram_quantize_mxfp8", "engram_project_mxfp8", "engram_gate", "engram_gate_layers",
-              "engram_forward"):
+              "engram_forward", "engram_forward_noalloc"):
     getattr(_lib, _name).restype = c_int
 
 
@@ -333,3 +336,20 @@ def engram_forward(params: HashParams, tokens: Tokens, layers, h, hc: int, dim: 
                                int(dim), float(eps), float(clamp), float(dot_scale), ws,
                                int(workspace.numel()) if workspace is not None else 0,
                                _dptr(bad_ids, torch.int32, 1, "bad_ids"), _stream(stream)))
+
+
+FORWARD_NOALLOC_MAX_BYTES = 32 << 20
+
+
+def engram_forward_noalloc(params: HashParams, tokens: Tokens, layers, h, hc: int, dim: int,
+                           eps: float, clamp: float, dot_scale: float, bad_ids=None,
+                           stream=None) -> None:
+    """engram_forward on the library's static device workspace (no allocation)."""
+    if len(layers) != params.n_layers:
+        raise ValueError("one Layer per hashed layer is required")
+    arr = (_Layer * len(layers))(*[l.c for l in layers])
+    _check(_lib.engram_forward_noalloc(ctypes.byref(params.c), ctypes.byref(tokens.c), arr,
+                                       _dptr(h, torch.float32, tokens.T * hc * dim, "h"),
+                                       int(hc), int(dim), float(eps), float(clamp),
+                                       float(dot_scale), _dptr(bad_ids, torch.int32, 1, "bad_ids"),
+                                       _stream(stream)))

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "common.hpp"
 
@@ -345,10 +346,16 @@ size_t engram_workspace_bytes(int32_t T, int32_t n_layers, int32_t cols, int32_t
          size_t(n_layers) * align256(t * (size_t(hc) + 1) * dim * sizeof(uint16_t));
 }
 
-engram_status engram_forward(const engram_hash_params *params, const engram_tokens *tokens,
-                             const engram_layer *layers, float *h, int32_t hc, int32_t dim,
-                             float eps, float clamp, float dot_scale, void *workspace,
-                             size_t workspace_bytes, int32_t *bad_ids, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// engram_forward on a given workspace (the caller's, or the static array of
+// engram_forward_noalloc).
+engram_status forward_impl(const engram_hash_params *params, const engram_tokens *tokens,
+                           const engram_layer *layers, float *h, int32_t hc, int32_t dim,
+                           float eps, float clamp, float dot_scale, void *workspace,
+                           size_t workspace_bytes, int32_t *bad_ids, hipStream_t stream) {
   engram::HashTables tab;
   engram_status st = check_hash_params(params, &tab);
   if (st != ENGRAM_OK) return st;
@@ -445,6 +452,76 @@ engram_status engram_forward(const engram_hash_params *params, const engram_toke
   return hip_status(engram::launch_gate_layers(h, gl, tokens->token_mask, T, hc, dim, eps,
                                                clamp, dot_scale, stream),
                     "gate launch");
+}
+
+// ---- The allocation-free forward's workspace.  A file-scope device array,
+// one copy per GPU, held from the module's load until the process ends.  In
+// host code its name is only a host-side stand-in: every use goes through
+// the device address hipGetSymbolAddress returns for the GPU in question,
+// looked up once per device (with that device current) and kept here.
+__device__ __align__(256) uint8_t scratch[ENGRAM_FORWARD_NOALLOC_MAX_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+engram_status scratch_for_stream(hipStream_t stream, void **out) {
+  int cur = 0, dev = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  dev = cur;
+  if (stream) {
+    if ((e = hipStreamGetDevice(stream, &dev)) != hipSuccess)
+      return hip_status(e, "hipStreamGetDevice");
+  }
+  REQUIRE_SUP(dev >= 0 && dev < kMaxDevices, "device %d beyond the %d this library tracks", dev,
+              kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e, "hipSetDevice");
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ENGRAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+engram_status engram_forward(const engram_hash_params *params, const engram_tokens *tokens,
+                             const engram_layer *layers, float *h, int32_t hc, int32_t dim,
+                             float eps, float clamp, float dot_scale, void *workspace,
+                             size_t workspace_bytes, int32_t *bad_ids, hipStream_t stream) {
+  return forward_impl(params, tokens, layers, h, hc, dim, eps, clamp, dot_scale, workspace,
+                      workspace_bytes, bad_ids, stream);
+}
+
+engram_status engram_forward_noalloc(const engram_hash_params *params,
+                                     const engram_tokens *tokens, const engram_layer *layers,
+                                     float *h, int32_t hc, int32_t dim, float eps, float clamp,
+                                     float dot_scale, int32_t *bad_ids, hipStream_t stream) {
+  engram::HashTables tab;
+  engram_status st = check_hash_params(params, &tab);
+  if (st != ENGRAM_OK) return st;
+  if ((st = check_tokens(tokens, params->max_ngram)) != ENGRAM_OK) return st;
+  const int32_t cols = (params->max_ngram - 1) * params->n_heads;
+  const size_t need = engram_workspace_bytes(tokens->T, params->n_layers, cols, hc, dim);
+  REQUIRE_SUP(need <= size_t(ENGRAM_FORWARD_NOALLOC_MAX_BYTES),
+              "this shape needs %zu bytes of workspace, above the %u of the static array "
+              "(use engram_forward with a workspace)",
+              need, unsigned(ENGRAM_FORWARD_NOALLOC_MAX_BYTES));
+  void *ws = nullptr;
+  if (tokens->T > 0 && (st = scratch_for_stream(stream, &ws)) != ENGRAM_OK) return st;
+  return forward_impl(params, tokens, layers, h, hc, dim, eps, clamp, dot_scale, ws,
+                      size_t(ENGRAM_FORWARD_NOALLOC_MAX_BYTES), bad_ids, stream);
 }
 
 }  // extern "C"

@@ -361,6 +361,28 @@ ENGRAM_API engram_status engram_forward(const engram_hash_params *params, const 
                              float eps, float clamp, float dot_scale, void *workspace,
                              size_t workspace_bytes, int32_t *bad_ids, hipStream_t stream);
 
+/* engram_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, checks and results as engram_forward, without workspace
+ * and workspace_bytes: the workspace is a static device array of
+ * ENGRAM_FORWARD_NOALLOC_MAX_BYTES bytes that the library holds on every GPU
+ * it runs on, from the first call there until the process ends (looked up,
+ * not allocated: the call itself allocates nothing).  A shape whose
+ * engram_workspace_bytes exceeds the array returns ENGRAM_ERR_UNSUPPORTED
+ * (32 MiB: e.g. up to 512 tokens at 24 columns, hc = 4, dim = 4096).  The
+ * GPU is the stream's (the current device for the NULL stream).  Every call
+ * on one GPU uses the same array, which keeps the last call's contents:
+ * calls that overlap in time on one GPU (other streams, other threads) race,
+ * and the caller must order them.
+ */
+#define ENGRAM_FORWARD_NOALLOC_MAX_BYTES (32u << 20)
+ENGRAM_API engram_status engram_forward_noalloc(const engram_hash_params *params,
+                                                const engram_tokens *tokens,
+                                                const engram_layer *layers, float *h,
+                                                int32_t hc, int32_t dim, float eps, float clamp,
+                                                float dot_scale, int32_t *bad_ids,
+                                                hipStream_t stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 ENGRAM_API const char *engram_last_error(void);
 

@@ -371,6 +371,39 @@ class TestValidation:
             assert call(**kw) == eg.ENGRAM_ERR_ARG, kw
             assert lib.engram_last_error().decode().startswith("layer 0: "), kw
 
+    def test_forward_noalloc_rejects_shapes_beyond_the_static_array(self, eg):
+        lib = _raw(eg)
+        lib.engram_forward_noalloc.argtypes = [ctypes.POINTER(_HP), ctypes.POINTER(_TK),
+                                               ctypes.POINTER(_LY), ctypes.c_void_p,
+                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                               ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        m, p, o = _tables()
+        hp = _hp(m, p, o)
+        hc, dim = 4, 4096
+        ly = _LY(eg.ENGRAM_ROWS_Q2K, 42, FAKE, None, FAKE, FAKE, FAKE, None, None)
+        limit = 32 << 20
+        for T, st in ((512, None), (1024, eg.ENGRAM_ERR_UNSUPPORTED)):
+            need = eg.engram_workspace_bytes(T, 1, 6, hc, dim)
+            tk = _TK(T, 1, 0, FAKE, FAKE, None, None, None, None)
+            if st is None:
+                assert need <= limit                 # allowed: not called here (no GPU)
+                continue
+            assert need > limit
+            assert lib.engram_forward_noalloc(ctypes.byref(hp), ctypes.byref(tk),
+                                              ctypes.byref(ly), FAKE, hc, dim, 1e-6, 1e-6,
+                                              0.0156, None, None) == st
+            assert "static array" in lib.engram_last_error().decode()
+        # the other checks are engram_forward's, before any workspace is looked up
+        bad = _TK(16, 0, 0, FAKE, FAKE, None, None, None, None)
+        assert lib.engram_forward_noalloc(ctypes.byref(hp), ctypes.byref(bad), ctypes.byref(ly),
+                                          FAKE, hc, dim, 1e-6, 1e-6, 0.0156, None,
+                                          None) == eg.ENGRAM_ERR_ARG
+        empty = _TK(0, 0, 0, None, None, None, None, None, None)
+        assert lib.engram_forward_noalloc(ctypes.byref(hp), ctypes.byref(empty),
+                                          ctypes.byref(ly), None, hc, dim, 1e-6, 1e-6, 0.0156,
+                                          None, None) == eg.ENGRAM_OK
+
     def test_gate_rejects(self, eg):
         lib = _raw(eg)
         ok = [FAKE, FAKE, FAKE, FAKE, None, 8, 4, 4096, 1e-6, 1e-6, 1 / 64]
