@@ -280,18 +280,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_exact_kernel(
     int64_t ids_stride, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
     int M, int N, int K, int tiles_n, int split) {
   extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
-  const int tm = int(blockIdx.x) / split, g = int(blockIdx.x) % split;
+  // Workgroups are dealt round-robin to the 8 XCDs: with tm = id % tiles_m,
+  // the `split` workgroups of an M-tile share an XCD (when tiles_m % 8 == 0)
+  // and so its L2, and fetch the M-tile's d/dmin words from HBM once.
+  const int tiles_m = int(gridDim.x) / split;
+  const int tm = int(blockIdx.x) % tiles_m, g = int(blockIdx.x) / tiles_m;
   const int cols = K / ENGRAM_HEAD_DIM;
+  // Thread t checks tile row t: all its ids, then all its blocks' d/dmin
+  // words, each batch in flight at once (an id outside the table, or a row
+  // past M, reads the word past the table: 0).
   const int row = tm * BM + int(threadIdx.x);
-  bool fast = true;
-  if (row < M) {
-    for (int c = 0; c < cols; ++c) {
-      const int32_t id = ids[int64_t(row) * ids_stride + c];
-      if (id >= 0 && id < num_rows)
-        fast &= q2k_fp32_exact(
-            *reinterpret_cast<const uint32_t *>(table + int64_t(id) * ENGRAM_Q2K_ROW_BYTES + 80));
-    }
+  const bool row_ok = row < M;
+  const int32_t *id_ptr = ids + int64_t(row_ok ? row : 0) * ids_stride;
+  const __amdgpu_buffer_rsrc_t rt = make_rsrc(table, num_rows * ENGRAM_Q2K_ROW_BYTES);
+  int32_t idv[ENGRAM_Q2K_FUSED_MAX_COLS];
+#pragma unroll
+  for (int c = 0; c < ENGRAM_Q2K_FUSED_MAX_COLS; ++c) idv[c] = row_ok && c < cols ? id_ptr[c] : -1;
+  uint32_t ddv[ENGRAM_Q2K_FUSED_MAX_COLS];
+#pragma unroll
+  for (int c = 0; c < ENGRAM_Q2K_FUSED_MAX_COLS; ++c) {
+    const bool ok = idv[c] >= 0 && idv[c] < num_rows;
+    ddv[c] = __builtin_amdgcn_raw_buffer_load_b32(
+        rt, (ok ? uint32_t(idv[c]) * ENGRAM_Q2K_ROW_BYTES : kNoRow) + 80, 0, 0);
   }
+  bool fast = true;
+#pragma unroll
+  for (int c = 0; c < ENGRAM_Q2K_FUSED_MAX_COLS; ++c) fast &= q2k_fp32_exact(ddv[c]);
   if (__syncthreads_and(fast)) return;
   for (int tn = g; tn < tiles_n; tn += split) {
     __syncthreads();                               // the previous tile is done with the LDS

@@ -268,7 +268,6 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
   // Block offsets; ids outside the table are counted once per (token,
   // column), by the first column tile.
   uint32_t *const offs = reinterpret_cast<uint32_t *>(red);
-  bool fast = true;
   {
     int bad = 0;
     for (int idx = tid; idx < cols * TM; idx += kSkinnyWaves * 64) {
@@ -278,19 +277,31 @@ __global__ __launch_bounds__(kSkinnyWaves * 64, 1) void gemm_skinny_q2k_kernel(
       const bool ok = id >= 0 && id < num_rows;
       bad += row_ok && !ok;
       offs[c * TM + t] = row_ok && ok ? uint32_t(id) * ENGRAM_Q2K_ROW_BYTES : kQ2kNoRow;
-      if (kMode == kQ2kExactFixup && row_ok && ok)
-        fast &= q2k_fp32_exact(*reinterpret_cast<const uint32_t *>(
-            table + int64_t(id) * ENGRAM_Q2K_ROW_BYTES + 80));
     }
     if (bad && tile.n == 0 && bad_ids) atomicAdd(bad_ids, bad);
   }
-  if (kMode == kQ2kExactFixup) {
-    if (__syncthreads_and(fast)) return;           // the first launch was exact already
-  } else {
-    __syncthreads();
-  }
+  __syncthreads();
 
   const __amdgpu_buffer_rsrc_t rt = make_rsrc(table, num_rows * ENGRAM_Q2K_ROW_BYTES);
+  if constexpr (kMode == kQ2kExactFixup) {
+    // The d/dmin word of every block of the tile, 8 requests in flight per
+    // thread (missing rows point past the table and read 0); nothing to
+    // redo unless one lies outside the one-fma range.
+    bool fast = true;
+    for (int base = 0; base < cols * TM; base += 8 * kSkinnyWaves * 64) {
+      uint32_t d[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int idx = base + j * kSkinnyWaves * 64 + tid;
+        d[j] = __builtin_amdgcn_raw_buffer_load_b32(
+            rt, (idx < cols * TM ? offs[idx] : kQ2kNoRow) + 80, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fast &= q2k_fp32_exact(d[j]);
+    }
+    if (__syncthreads_and(fast)) return;           // the first launch was exact already
+  }
+
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + int64_t(n0) * K, int64_t(N - n0) * K * 2);
   const int r = lane & 15, kg = lane >> 4;
   const uint32_t voff = uint32_t(r * K + 8 * kg) * 2;
