@@ -375,7 +375,9 @@ def main() -> int:
         dom_name, dom_kernel = "rows_project", "gemm_mx_kernel (engram_project_mxfp8)"
         dom_prof = "gemm_mx"
     elif fused:
-        dom_name, dom_kernel = "rows_project", "gemm_q2k_kernel (engram_project_q2k)"
+        dom_name, dom_kernel = "rows_project", (
+            "gemm_q2k_persistent_kernel" if s.cols % 2 == 0 else "gemm_q2k_kernel") + \
+            " + gemm_q2k_exact_kernel (engram_project_q2k)"
         dom_prof = "gemm_q2k"
     else:
         dom_name, dom_kernel = "project", "gemm_nt_kernel (engram_project)"

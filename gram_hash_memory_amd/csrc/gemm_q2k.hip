@@ -11,7 +11,7 @@
 // Tile 256 x 256, 4 waves, each wave 64 rows x 256 columns (2 x 8 blocks of
 // v_mfma_f32_32x32x16_bf16, accumulators in AGPRs), K in stages of BK = 64.
 //  - B goes straight from global memory into its LDS stage (buffer_load ...
-//    lds, one stage ahead); every wave reads the whole B stage as fragments.
+//    lds); every wave reads the whole B stage as fragments.
 //  - A never touches LDS.  A wave owns 64 tile rows, so each row is needed by
 //    exactly one wave, and every lane decodes its own A fragments from the
 //    Q2_K block in registers: lane (r, h) of the 32 x 16 fragment holds row r,
@@ -23,13 +23,31 @@
 // is byte 32 (v / 128) + v % 32 at bit 2 ((v % 128) / 32), and the lane's
 // values (v % 16 in 8h .. 8h + 7) fall in the four 8-byte pieces at quant
 // bytes 16 p + 8 h, p = 0..3.  The blocks of a column are loaded one column
-// ahead; their ids are resolved into byte offsets once, before the K loop.
+// ahead.
+// Two forms of the same K loop:
+//  - gemm_q2k_persistent_kernel (even column counts): one workgroup per CU
+//    walks its share of the tiles.  The next tile's ids, its first blocks and
+//    its first two B slices are fetched during the current tile's last
+//    column, so the K loop runs on from tile to tile; each B slice is
+//    requested right after the barrier that frees its stage, a whole stage
+//    ahead of its use.  The MFMAs take wkv as their first operand, so a lane
+//    ends with 4 consecutive output columns per block row and writes them to
+//    a wave-private LDS staging area as 8 bytes; the wave then stores whole
+//    128-byte row segments.  No workgroup barrier sits in the epilogue.
+//  - q2k_tile (one tile per workgroup): odd column counts, and the exact
+//    recompute below.
+// Both give every output the same MFMAs in the same K order as gemm.hip
+// (swapping the two operands of an MFMA transposes its output block and
+// leaves each dot product as it is), so kv is bit-identical to rows ->
+// project.
 // Values are rounded once for every finite d, dmin (q2k_decode.hpp).  The
 // tiles decode with one fma per value, which is exact unless a block's d and
 // dmin lie far apart; a second, small launch then checks every M-tile's
-// blocks and recomputes, with the exact group decode, the tiles of any
-// M-tile that has such a block (gemm_q2k_exact_kernel).
+// blocks, counts the ids outside the table, and recomputes, with the exact
+// group decode, the tiles of any M-tile that has such a block
+// (gemm_q2k_exact_kernel).
 #include <algorithm>
+#include <atomic>
 
 #include "gemm_common.hpp"
 #include "q2k_decode.hpp"
@@ -50,16 +68,86 @@ struct Q2kPart {
   uint32_t dd;       // fp16 d | fp16 dmin << 16
 };
 
-// One 256 x 256 output tile (tm, tn); kExact picks the group decode.
+constexpr int BK = 64;
+constexpr int kStageElems = BN * BK;                 // one B stage: 32 KB
+constexpr int kSegs = BN * BK * 2 / 1024 / kWaves;   // 1 KB B segments per wave per stage: 8
+
+// ---- B: global -> LDS by LDS-DMA.  One instruction fills a 1 KB segment (8
+// tile rows); lane L lands at byte 16 L, i.e. row L / 8 of the segment,
+// physical chunk L % 8, and fetches the logical chunk the swizzle keeps
+// there.  For segment s the swizzle key of that row is (L / 8) ^ (s & 1).
+// Rows past N read as zeros (the resource starts at the tile's first row, and
+// the row is part of the VGPR offset, the range-checked part; the SGPR offset
+// only carries the K position).
+struct BSegs {
+  uint32_t voff_even, voff_odd, seg_stride;
+};
+__device__ __forceinline__ BSegs b_segs(int lane, int K) {
+  const int seg_row = lane >> 3;
+  return {uint32_t(seg_row * K + ((lane & 7) ^ seg_row) * 8) * 2,
+          uint32_t(seg_row * K + ((lane & 7) ^ seg_row ^ 1) * 8) * 2, uint32_t(8 * K) * 2};
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t b_rsrc(const uint16_t *B, int N, int K, int tn) {
+  const int n0 = tn * BN;
+  return make_rsrc(B + int64_t(n0) * K, int64_t(N - n0) * K * 2);
+}
+// B slice `slice` (K positions 64 slice ..) of the tile into LDS stage sb.
+__device__ __forceinline__ void dma_b_slice(__amdgpu_buffer_rsrc_t rb, uint16_t *sb,
+                                            const BSegs &g, int wave, int slice) {
+#pragma unroll
+  for (int i = 0; i < kSegs; ++i) {
+    const int seg = wave * kSegs + i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, sb + seg * 512, 16,
+                                             ((i & 1) ? g.voff_odd : g.voff_even) +
+                                                 seg * g.seg_stride,
+                                             slice * BK * 2, 0, 0);
+  }
+}
+// The 8 B fragments of k-step ks of an LDS stage (block j: columns 32 j ..).
+__device__ __forceinline__ void load_b_frags(const uint16_t *sb, int frow, int fhalf, int ks,
+                                             bf16x8 (&fb)[kNJ]) {
+  const int chunk = 2 * ks + fhalf;
+#pragma unroll
+  for (int j = 0; j < kNJ; ++j)
+    fb[j] = *reinterpret_cast<const bf16x8 *>(sb + swz<BK>(j * 32 + frow, chunk));
+}
+// A lane's parts of the block at byte offset `off` of the table.
+__device__ __forceinline__ void load_part(__amdgpu_buffer_rsrc_t rt, uint32_t off, int fhalf,
+                                          Q2kPart &p) {
+  p.sc = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0));
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    p.q[q] = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_raw_buffer_load_b64(rt, off + 16 + 16 * q + 8 * fhalf, 0, 0));
+  p.dd = __builtin_amdgcn_raw_buffer_load_b32(rt, off + 80, 0, 0);
+}
+// The lane's A fragment of k-step ks of stage qs (values 64 qs + 16 ks .. + 15
+// of the block: 16-value group 4 qs + ks), q2k_decode.hpp.
+template <bool kExact>
+__device__ __forceinline__ bf16x8 decode_frag(const Q2kPart &b, const int qs, const int ks) {
+  const int p = 2 * (qs >> 1) + (ks & 1);
+  const int shift = 4 * (qs & 1) + 2 * (ks >> 1);
+  const uint32_t sm = (b.sc[qs] >> (8 * ks)) & 0xFFu;
+  const Q2kPlanes pl = kExact ? q2k_group_planes_exact(b.dd, sm) : q2k_group_planes(b.dd, sm);
+  return __builtin_bit_cast(bf16x8, q2k_expand8(pl, b.q[p][0], b.q[p][1], shift));
+}
+// One k-step: 16 MFMAs (32 cycles of matrix core each), the next step's 8 B
+// fragment reads and its A decode (about 56 VALU ops) spread between them.
+__device__ __forceinline__ void sched_step() {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (r % 2 == 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+  }
+}
+
+// One 256 x 256 output tile (tm, tn) per call; kExact picks the group decode.
 template <bool kExact>
 __device__ __forceinline__ void q2k_tile(
     const uint8_t *__restrict__ table, int64_t num_rows, const int32_t *__restrict__ ids,
     int64_t ids_stride, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
-    int M, int N, int K, int tm, int tn, int32_t *__restrict__ bad_ids, uint16_t *smem) {
-  constexpr int BK = 64;
-  constexpr int kStageElems = BN * BK;                 // B only: 32 KB
-  constexpr int kSegs = BN * BK * 2 / 1024 / kWaves;   // 1 KB B segments per wave per stage: 8
-
+    int M, int N, int K, int tm, int tn, uint16_t *smem) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -68,33 +156,14 @@ __device__ __forceinline__ void q2k_tile(
   const int cols = K / ENGRAM_HEAD_DIM;
   const int nk = K / BK;
 
-  // ---- B: global -> LDS by LDS-DMA.  One instruction fills a 1 KB segment
-  // (8 tile rows); lane L lands at byte 16 L, i.e. row L / 8 of the segment,
-  // physical chunk L % 8, and fetches the logical chunk the swizzle keeps
-  // there.  For segment s the swizzle key of that row is (L / 8) ^ (s & 1).
-  // Rows past N read as zeros (the resource starts at the tile's first row,
-  // and the row is part of the VGPR offset, the range-checked part; the
-  // SGPR offset only carries the K position).
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + int64_t(n0) * K, int64_t(N - n0) * K * 2);
-  const int seg_row = lane >> 3;
-  const uint32_t voff_even = uint32_t(seg_row * K + ((lane & 7) ^ seg_row) * 8) * 2;
-  const uint32_t voff_odd = uint32_t(seg_row * K + ((lane & 7) ^ seg_row ^ 1) * 8) * 2;
-  const uint32_t seg_stride = uint32_t(8 * K) * 2;
+  const __amdgpu_buffer_rsrc_t rb = b_rsrc(B, N, K, tn);
+  const BSegs segs = b_segs(lane, K);
   auto dma_b = [&](int stage, int slice) {
-    const int k0 = min(slice, nk - 1) * BK;
-    uint16_t *sb = smem + stage * kStageElems;
-#pragma unroll
-    for (int i = 0; i < kSegs; ++i) {
-      const int seg = wave * kSegs + i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, sb + seg * 512, 16,
-                                               ((i & 1) ? voff_odd : voff_even) + seg * seg_stride,
-                                               k0 * 2, 0, 0);
-    }
+    dma_b_slice(rb, smem + stage * kStageElems, segs, wave, min(slice, nk - 1));
   };
 
   // ---- A: byte offsets of every (row, column) block, in LDS behind the two
-  // B stages (cols <= ENGRAM_Q2K_FUSED_MAX_COLS).  Thread t resolves tile row
-  // t and counts its ids outside the table, once per (token, column).
+  // B stages (cols <= ENGRAM_Q2K_FUSED_MAX_COLS).  Thread t resolves tile row t.
   const __amdgpu_buffer_rsrc_t rt = make_rsrc(table, num_rows * ENGRAM_Q2K_ROW_BYTES);
   uint32_t *const offs = reinterpret_cast<uint32_t *>(smem + 2 * kStageElems);
   {
@@ -104,47 +173,29 @@ __device__ __forceinline__ void q2k_tile(
     int32_t idv[ENGRAM_Q2K_FUSED_MAX_COLS];
 #pragma unroll
     for (int c = 0; c < ENGRAM_Q2K_FUSED_MAX_COLS; ++c) idv[c] = c < cols ? id_ptr[c] : 0;
-    int bad = 0;
 #pragma unroll
     for (int c = 0; c < ENGRAM_Q2K_FUSED_MAX_COLS; ++c) {
       if (c < cols) {
         const bool ok = idv[c] >= 0 && idv[c] < num_rows;
-        bad += row_ok && !ok;
         offs[c * kThreads + tid] =
             row_ok && ok ? uint32_t(idv[c]) * ENGRAM_Q2K_ROW_BYTES : kNoRow;
       }
     }
-    if (bad && tn == 0 && bad_ids) atomicAdd(bad_ids, bad);
   }
   __syncthreads();                                  // offsets of other lanes' rows
 
   Q2kPart blk[2][kRowsPerLane];
   auto load_block = [&](int set, int col) {
 #pragma unroll
-    for (int i = 0; i < kRowsPerLane; ++i) {
-      const uint32_t off = offs[min(col, cols - 1) * kThreads + wave * 64 + 32 * i + frow];
-      blk[set][i].sc = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0));
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-        blk[set][i].q[p] = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rt, off + 16 + 16 * p + 8 * fhalf, 0, 0));
-      blk[set][i].dd = __builtin_amdgcn_raw_buffer_load_b32(rt, off + 80, 0, 0);
-    }
+    for (int i = 0; i < kRowsPerLane; ++i)
+      load_part(rt, offs[min(col, cols - 1) * kThreads + wave * 64 + 32 * i + frow], fhalf,
+                blk[set][i]);
   };
 
-  // A fragments of k-step ks of stage qs (values 64 qs + 16 ks .. + 15 of the
-  // block: 16-value group 4 qs + ks) from register set `set` (q2k_decode.hpp).
   bf16x8 fa[2][kRowsPerLane], fb[2][kNJ];
   auto decode_a = [&](int set, const int qs, const int ks, int slot) {
-    const int p = 2 * (qs >> 1) + (ks & 1);
-    const int shift = 4 * (qs & 1) + 2 * (ks >> 1);
 #pragma unroll
-    for (int i = 0; i < kRowsPerLane; ++i) {
-      const Q2kPart &b = blk[set][i];
-      const uint32_t sm = (b.sc[qs] >> (8 * ks)) & 0xFFu;
-      const Q2kPlanes pl = kExact ? q2k_group_planes_exact(b.dd, sm) : q2k_group_planes(b.dd, sm);
-      fa[slot][i] = __builtin_bit_cast(bf16x8, q2k_expand8(pl, b.q[p][0], b.q[p][1], shift));
-    }
+    for (int i = 0; i < kRowsPerLane; ++i) fa[slot][i] = decode_frag<kExact>(blk[set][i], qs, ks);
   };
 
   f32x16 acc[kRowsPerLane][kNJ];
@@ -154,11 +205,7 @@ __device__ __forceinline__ void q2k_tile(
     for (int j = 0; j < kNJ; ++j) acc[i][j] = f32x16{};
 
   auto load_b = [&](int stage, int ks, int slot) {
-    const uint16_t *sb = smem + stage * kStageElems;
-    const int chunk = 2 * ks + fhalf;
-#pragma unroll
-    for (int j = 0; j < kNJ; ++j)
-      fb[slot][j] = *reinterpret_cast<const bf16x8 *>(sb + swz<BK>(j * 32 + frow, chunk));
+    load_b_frags(smem + stage * kStageElems, frow, fhalf, ks, fb[slot]);
   };
   // Column-block-major: B fragment j, read during the previous k-step in
   // order j, is first used 2 j MFMAs into this one, so every read gets the
@@ -170,16 +217,6 @@ __device__ __forceinline__ void q2k_tile(
       for (int i = 0; i < kRowsPerLane; ++i)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j],
                                                             acc[i][j], 0, 0, 0);
-  };
-  // One k-step: 16 MFMAs (32 cycles of matrix core each), the next step's 8
-  // B fragment reads and its A decode (about 56 VALU ops) spread between them.
-  auto sched_step = [&]() {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      if (r % 2 == 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
-    }
   };
 
   // Iteration kt multiplies stage kt % 2 and fills stage (kt + 1) % 2, which
@@ -263,22 +300,239 @@ __device__ __forceinline__ void q2k_tile(
 __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
     const uint8_t *__restrict__ table, int64_t num_rows, const int32_t *__restrict__ ids,
     int64_t ids_stride, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
-    int M, int N, int K, int tiles_m, int tiles_n, int32_t *__restrict__ bad_ids) {
+    int M, int N, int K, int tiles_m, int tiles_n) {
   extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  q2k_tile<false>(table, num_rows, ids, ids_stride, B, C, M, N, K, tm, tn, bad_ids, smem);
+  q2k_tile<false>(table, num_rows, ids, ids_stride, B, C, M, N, K, tm, tn, smem);
 }
 
-// Runs after gemm_q2k_kernel on the same stream.  Workgroup (tm, g) checks
-// the d/dmin of every block of M-tile tm; if any lies outside the one-fma
-// range (q2k_fp32_exact), it recomputes tiles (tm, g), (tm, g + split), ...
-// with the exact group decode, overwriting what the first launch stored.
-// Otherwise it exits after the check.
+// Staging row stride of the persistent kernel's epilogue, in bf16: 144 bytes
+// keeps 16-byte alignment and puts rows 16 apart on other banks than rows
+// 0..15 (a 2-way conflict at most for the 8-byte writes).
+constexpr int kStgStride = 72;
+
+// The persistent form (cols even).  Workgroup b runs the tiles whose ids in
+// the XCD-aware order (tile_coords) are b, b + G, b + 2 G, ... (G = grid
+// size, a multiple of 8 when a workgroup has more than one tile, so all of
+// them lie in its XCD's run).  LDS: the two B stages (64 KB), the current
+// tile's ids (cols x 256 int32: each wave's 64 rows are written and read only
+// by that wave), and a 9 KB staging area per wave.
+__global__ __launch_bounds__(kThreads, 1) void gemm_q2k_persistent_kernel(
+    const uint8_t *__restrict__ table, int64_t num_rows, const int32_t *__restrict__ ids,
+    int64_t ids_stride, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
+    int M, int N, int K, int tiles_m, int tiles_n) {
+  extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int frow = lane & 31, fhalf = lane >> 5;
+  const int cols = K / ENGRAM_HEAD_DIM;
+  const int nk = K / BK;
+  const int tiles = tiles_m * tiles_n;
+  int lid = blockIdx.x;
+  if (lid >= tiles) return;
+
+  int32_t *const ids_lds = reinterpret_cast<int32_t *>(smem + 2 * kStageElems);
+  uint16_t *const stg = smem + 2 * kStageElems + cols * kThreads * 2 + wave * 64 * kStgStride;
+  const BSegs segs = b_segs(lane, K);
+  auto dma_b = [&](__amdgpu_buffer_rsrc_t rb, int stage, int slice) {
+    dma_b_slice(rb, smem + stage * kStageElems, segs, wave, slice);
+  };
+  // The ids of tile row m0 + 64 wave + lane, all columns, into ids_lds (one
+  // LDS-DMA instruction per column; rows past M read 0 and are never stored).
+  auto dma_ids = [&](int tm_) {
+    const int m0_ = tm_ * BM;
+    const __amdgpu_buffer_rsrc_t ri =
+        make_rsrc(ids + int64_t(m0_) * ids_stride, int64_t(min(BM, M - m0_)) * ids_stride * 4);
+    const uint32_t voff = uint32_t((wave * 64 + lane) * ids_stride) * 4;
+    for (int c = 0; c < cols; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ri, ids_lds + c * kThreads + wave * 64, 4,
+                                               voff + uint32_t(c) * 4, 0, 0, 0);
+  };
+
+  const __amdgpu_buffer_rsrc_t rt = make_rsrc(table, num_rows * ENGRAM_Q2K_ROW_BYTES);
+  Q2kPart blk[2][kRowsPerLane];
+  // An id outside the table reads the bytes past it: zeros.
+  auto load_block = [&](int set, int col) {
+#pragma unroll
+    for (int i = 0; i < kRowsPerLane; ++i) {
+      const int32_t id = ids_lds[col * kThreads + wave * 64 + 32 * i + frow];
+      const uint32_t off =
+          (id >= 0 && id < num_rows) ? uint32_t(id) * ENGRAM_Q2K_ROW_BYTES : kNoRow;
+      load_part(rt, off, fhalf, blk[set][i]);
+    }
+  };
+
+  bf16x8 fa[2][kRowsPerLane], fb[2][kNJ];
+  auto decode_a = [&](int set, const int qs, const int ks, int slot) {
+#pragma unroll
+    for (int i = 0; i < kRowsPerLane; ++i) fa[slot][i] = decode_frag<false>(blk[set][i], qs, ks);
+  };
+
+  // acc[i][j] holds the transposed 32 x 32 output block: accumulator r of
+  // lane (t, h) is tile row 32 i + t, column 32 j + 8 (r / 4) + 4 h + r % 4.
+  f32x16 acc[kRowsPerLane][kNJ];
+#pragma unroll
+  for (int i = 0; i < kRowsPerLane; ++i)
+#pragma unroll
+    for (int j = 0; j < kNJ; ++j) acc[i][j] = f32x16{};
+
+  auto load_b = [&](int stage, int ks, int slot) {
+    load_b_frags(smem + stage * kStageElems, frow, fhalf, ks, fb[slot]);
+  };
+  auto mfma_block = [&](int slot) {
+#pragma unroll
+    for (int j = 0; j < kNJ; ++j)
+#pragma unroll
+      for (int i = 0; i < kRowsPerLane; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][j], fa[slot][i],
+                                                            acc[i][j], 0, 0, 0);
+  };
+
+  // Iteration kt of the current tile multiplies stage kt % 2 (j = kt % 8
+  // fixes the register sets at compile time, as in q2k_tile):
+  //  - at kt % 4 == 0 the blocks of column (kt / 4 + 1) % cols are requested
+  //    (12 loads); after a tile's last column that is column 0 of the next
+  //    tile, whose ids are in ids_lds by then;
+  //  - the barrier waits for the B slice of this stage (requested one
+  //    iteration earlier) and lets only those 12 block loads stay in flight;
+  //  - right after it, stage kt % 2, which no wave reads any more, gets the
+  //    slice `fill_slice` of resource rb_fill (slice kt + 2, or one of the
+  //    next tile's first two slices).
+  auto iteration = [&](int kt, const int j, __amdgpu_buffer_rsrc_t rb_fill, int fill_slice) {
+    const int stage = j & 1;
+    const int set = (j >> 2) & 1, qs = j & 3;
+    __builtin_amdgcn_sched_barrier(0);
+    if (qs == 0) {
+      const int col = kt / 4 + 1;
+      load_block(set ^ 1, col == cols ? 0 : col);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(stage, 1, 1);
+    decode_a(set, qs, 1, 1);
+    mfma_block(0);
+    sched_step();
+    load_b(stage, 2, 0);
+    decode_a(set, qs, 2, 0);
+    mfma_block(1);
+    sched_step();
+    load_b(stage, 3, 1);
+    decode_a(set, qs, 3, 1);
+    mfma_block(0);
+    sched_step();
+    if (qs == 0) stage_barrier<waitcnt(6 * kRowsPerLane, 0)>();
+    else stage_barrier<waitcnt(0, 0)>();
+    __builtin_amdgcn_sched_barrier(0);
+    dma_b(rb_fill, stage, fill_slice);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(stage ^ 1, 0, 0);
+    decode_a(((j + 1) >> 2) & 1, (j + 1) & 3, 0, 0);
+    mfma_block(1);
+    sched_step();
+  };
+
+  // Prologue of the first tile: its ids, the blocks of column 0 and B
+  // slice 0, then slice 1 in flight.
+  int tm, tn;
+  tile_coords(lid, tiles_m, tiles_n, tm, tn);
+  __amdgpu_buffer_rsrc_t rb = b_rsrc(B, N, K, tn);
+  dma_ids(tm);
+  __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
+  load_block(0, 0);
+  dma_b(rb, 0, 0);
+  stage_barrier<waitcnt(0, 0)>();
+  dma_b(rb, 1, 1);
+  load_b(0, 0, 0);
+  decode_a(0, 0, 0, 0);
+
+  const bool vec = (N % 8) == 0;
+  for (;;) {
+    const int next = lid + int(gridDim.x);
+    const bool has_next = next < tiles;
+    int tm2 = tm, tn2 = tn;
+    if (has_next) tile_coords(next, tiles_m, tiles_n, tm2, tn2);
+    const __amdgpu_buffer_rsrc_t rb2 = b_rsrc(B, N, K, tn2);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // Two columns per trip (cols is even).  In the last trip, iterations 6
+    // and 7 fill the stages with the next tile's slices 0 and 1 (or, after
+    // the last tile, reload slice nk - 1, which nothing reads).
+    for (int kt = 0; kt < nk; kt += 8) {
+      const bool last = kt + 8 == nk;
+      iteration(kt + 0, 0, rb, kt + 2);
+      // This tile's ids were last read just above (the blocks of column
+      // cols - 1); the next tile's replace them and land by the next
+      // barrier, whose vmcnt is 0.
+      if (last && has_next) dma_ids(tm2);
+      iteration(kt + 1, 1, rb, kt + 3);
+      iteration(kt + 2, 2, rb, kt + 4);
+      iteration(kt + 3, 3, rb, kt + 5);
+      iteration(kt + 4, 4, rb, kt + 6);
+      iteration(kt + 5, 5, rb, kt + 7);
+      iteration(kt + 6, 6, last ? rb2 : rb, last ? (has_next ? 0 : nk - 1) : kt + 8);
+      iteration(kt + 7, 7, last ? rb2 : rb, last ? (has_next ? 1 : nk - 1) : kt + 9);
+    }
+
+    // Epilogue, per wave: its 64 rows in 4 chunks of 64 columns.  A lane
+    // packs its 4 consecutive columns of a block row into 8 bytes of the
+    // staging area; the wave then reads back 16-byte row pieces and stores
+    // 128-byte row segments.  A wave's LDS accesses complete in order, so
+    // neither step needs a barrier.
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+#pragma unroll
+      for (int i = 0; i < kRowsPerLane; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x16 &a = acc[i][2 * c4 + jj];
+            const u32x2 v = {pack_bf16x2(a[4 * g], a[4 * g + 1]),
+                             pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
+            *reinterpret_cast<u32x2 *>(stg + (i * 32 + frow) * kStgStride + jj * 32 + 8 * g +
+                                       4 * fhalf) = v;
+          }
+#pragma unroll
+      for (int r8 = 0; r8 < 8; ++r8) {
+        const int row = r8 * 8 + (lane >> 3), c8 = (lane & 7) * 8;
+        const int grow = m0 + wave * 64 + row, gcol = n0 + c4 * 64 + c8;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + row * kStgStride + c8);
+        if (grow < M && gcol < N) {
+          uint16_t *dst = C + int64_t(grow) * N + gcol;
+          if (vec) {
+            *reinterpret_cast<u32x4 *>(dst) = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (gcol + e < N) dst[e] = uint16_t(v[e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kRowsPerLane; ++i)
+#pragma unroll
+      for (int j = 0; j < kNJ; ++j) acc[i][j] = f32x16{};
+    if (!has_next) break;
+    lid = next;
+    tm = tm2;
+    tn = tn2;
+    rb = rb2;
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));       // the last, unread B reload
+}
+
+// Runs after the tiles on the same stream.  Workgroup (tm, g) checks the
+// d/dmin of every block of M-tile tm (the g == 0 workgroups also count the
+// ids outside the table, once per (token, column)); if any block lies
+// outside the one-fma range (q2k_fp32_exact), it recomputes tiles (tm, g),
+// (tm, g + split), ... with the exact group decode, overwriting what the
+// first launch stored.  Otherwise it exits after the check.
 __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_exact_kernel(
     const uint8_t *__restrict__ table, int64_t num_rows, const int32_t *__restrict__ ids,
     int64_t ids_stride, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
-    int M, int N, int K, int tiles_n, int split) {
+    int M, int N, int K, int tiles_n, int split, int32_t *__restrict__ bad_ids) {
   extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
   // Workgroups are dealt round-robin to the 8 XCDs: with tm = id % tiles_m,
   // the `split` workgroups of an M-tile share an XCD (when tiles_m % 8 == 0)
@@ -297,20 +551,40 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_exact_kernel(
 #pragma unroll
   for (int c = 0; c < ENGRAM_Q2K_FUSED_MAX_COLS; ++c) idv[c] = row_ok && c < cols ? id_ptr[c] : -1;
   uint32_t ddv[ENGRAM_Q2K_FUSED_MAX_COLS];
+  int bad = 0;
 #pragma unroll
   for (int c = 0; c < ENGRAM_Q2K_FUSED_MAX_COLS; ++c) {
     const bool ok = idv[c] >= 0 && idv[c] < num_rows;
+    bad += row_ok && c < cols && !ok;
     ddv[c] = __builtin_amdgcn_raw_buffer_load_b32(
         rt, (ok ? uint32_t(idv[c]) * ENGRAM_Q2K_ROW_BYTES : kNoRow) + 80, 0, 0);
   }
+  if (bad && g == 0 && bad_ids) atomicAdd(bad_ids, bad);
   bool fast = true;
 #pragma unroll
   for (int c = 0; c < ENGRAM_Q2K_FUSED_MAX_COLS; ++c) fast &= q2k_fp32_exact(ddv[c]);
   if (__syncthreads_and(fast)) return;
   for (int tn = g; tn < tiles_n; tn += split) {
     __syncthreads();                               // the previous tile is done with the LDS
-    q2k_tile<true>(table, num_rows, ids, ids_stride, B, C, M, N, K, tm, tn, nullptr, smem);
+    q2k_tile<true>(table, num_rows, ids, ids_stride, B, C, M, N, K, tm, tn, smem);
   }
+}
+
+// Compute units of each device (the persistent grid), read once.
+int num_cus(hipStream_t stream) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= 64) {
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  }
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 }  // namespace
@@ -332,25 +606,45 @@ hipError_t launch_project_q2k(const uint8_t *table, int64_t num_rows, const int3
                                      bad_ids, stream);
   const int K = cols * ENGRAM_HEAD_DIM;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const size_t lds_loop = size_t(2) * BN * 64 * sizeof(uint16_t) +
+  // Per-tile kernels (odd column counts, the exact recompute): the two B
+  // stages and the block offsets, or the output tile in the epilogue.
+  const size_t lds_loop = size_t(2) * kStageElems * sizeof(uint16_t) +
                          size_t(cols) * kThreads * sizeof(uint32_t);
   const size_t lds_epilogue = size_t(BM) * BN * sizeof(uint16_t);
   const size_t lds = lds_loop > lds_epilogue ? lds_loop : lds_epilogue;
-  for (const void *fn : {reinterpret_cast<const void *>(&gemm_q2k_kernel),
-                         reinterpret_cast<const void *>(&gemm_q2k_exact_kernel)}) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return e;
+  // Persistent kernel: the two B stages, the ids and 4 staging areas.
+  const size_t lds_pers = size_t(2) * kStageElems * sizeof(uint16_t) +
+                          size_t(cols) * kThreads * sizeof(int32_t) +
+                          size_t(kWaves) * 64 * kStgStride * sizeof(uint16_t);
+  const bool persistent = cols % 2 == 0;
+  const void *tile_fn = persistent ? reinterpret_cast<const void *>(&gemm_q2k_persistent_kernel)
+                                   : reinterpret_cast<const void *>(&gemm_q2k_kernel);
+  hipError_t e = hipFuncSetAttribute(tile_fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     int(persistent ? lds_pers : lds));
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_q2k_exact_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (e != hipSuccess) return e;
+  const int tiles = tiles_m * tiles_n;
+  if (persistent) {
+    // One workgroup per CU; when a workgroup gets several tiles the grid is a
+    // multiple of 8, so that they all lie in its XCD's run of tile_coords.
+    const int cus = num_cus(stream);
+    const int grid = tiles <= cus ? tiles : std::max(8, cus / 8 * 8);
+    hipLaunchKernelGGL(gemm_q2k_persistent_kernel, dim3(grid), dim3(kThreads), lds_pers, stream,
+                       table, num_rows, ids, ids_token_stride, w, c, M, N, K, tiles_m, tiles_n);
+  } else {
+    hipLaunchKernelGGL(gemm_q2k_kernel, dim3(tiles), dim3(kThreads), lds, stream, table,
+                       num_rows, ids, ids_token_stride, w, c, M, N, K, tiles_m, tiles_n);
   }
-  hipLaunchKernelGGL(gemm_q2k_kernel, dim3(tiles_m * tiles_n), dim3(kThreads), lds, stream,
-                     table, num_rows, ids, ids_token_stride, w, c, M, N, K, tiles_m, tiles_n,
-                     bad_ids);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   // About one checking workgroup per CU; each recomputes every split-th tile
   // of its M-tile when that M-tile needs the exact decode.
   const int split = std::max(1, std::min(tiles_n, (256 + tiles_m - 1) / tiles_m));
   hipLaunchKernelGGL(gemm_q2k_exact_kernel, dim3(tiles_m * split), dim3(kThreads), lds, stream,
-                     table, num_rows, ids, ids_token_stride, w, c, M, N, K, tiles_n, split);
+                     table, num_rows, ids, ids_token_stride, w, c, M, N, K, tiles_n, split,
+                     bad_ids);
   return hipGetLastError();
 }
 

@@ -416,10 +416,12 @@ def test_project_q2k_bit_identical_to_rows_then_project(eg, c):
                                       (300, 24, 4096), (513, 2, 1000),
                                       (1, 4, 64), (64, 8, 1000), (100, 4, 520), (128, 12, 4096),
                                       (37, 32, 300), (129, 8, 256), (65, 24, 20480),
-                                      (96, 32, 1000)])
+                                      (96, 32, 1000), (1800, 4, 8200), (1500, 2, 16390)])
 def test_project_q2k_ragged_and_bad_ids(eg, T, cols, N):
-    # Ragged tiles in M and N, an odd column count (the 256 x 256 kernel's
-    # half-unrolled tail), few tokens with whole-column K quarters (the
+    # Ragged tiles in M and N, an odd column count (the one-tile-per-workgroup
+    # kernel and its half-unrolled tail), more tiles than compute units (the
+    # persistent kernel's workgroups take several tiles, N not a multiple of
+    # 8 included), few tokens with whole-column K quarters (the
     # weight-streaming form with 64- and 128-token tiles, one or several
     # columns per quarter, an odd number included, the widest column tiles at
     # N = 20480), and ids outside the table: zero rows, counted once per
