@@ -29,8 +29,8 @@
 //    walks its share of the tiles.  The next tile's ids, its first blocks and
 //    its first two B slices are fetched during the current tile's last
 //    column, so the K loop runs on from tile to tile; each B slice is
-//    requested right after the barrier that frees its stage, a whole stage
-//    ahead of its use.  The MFMAs take wkv as their first operand, so a lane
+//    requested in the k-step after the barrier that frees its stage, a whole
+//    stage ahead of its use.  The MFMAs take wkv as their first operand, so a lane
 //    ends with 4 consecutive output columns per block row and writes them to
 //    a wave-private LDS staging area as 8 bytes; the wave then stores whole
 //    128-byte row segments.  No workgroup barrier sits in the epilogue.
@@ -397,9 +397,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_persistent_kernel(
   //    tile, whose ids are in ids_lds by then;
   //  - the barrier waits for the B slice of this stage (requested one
   //    iteration earlier) and lets only those 12 block loads stay in flight;
-  //  - right after it, stage kt % 2, which no wave reads any more, gets the
-  //    slice `fill_slice` of resource rb_fill (slice kt + 2, or one of the
-  //    next tile's first two slices).
+  //  - after it, stage kt % 2, which no wave reads any more, gets the slice
+  //    `fill_slice` of resource rb_fill (slice kt + 2, or one of the next
+  //    tile's first two slices), its DMA spread over the last k-step.
   auto iteration = [&](int kt, const int j, __amdgpu_buffer_rsrc_t rb_fill, int fill_slice) {
     const int stage = j & 1;
     const int set = (j >> 2) & 1, qs = j & 3;
@@ -424,12 +424,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_persistent_kernel(
     if (qs == 0) stage_barrier<waitcnt(6 * kRowsPerLane, 0)>();
     else stage_barrier<waitcnt(0, 0)>();
     __builtin_amdgcn_sched_barrier(0);
-    dma_b(rb_fill, stage, fill_slice);
-    __builtin_amdgcn_sched_barrier(0);
     load_b(stage ^ 1, 0, 0);
     decode_a(((j + 1) >> 2) & 1, (j + 1) & 3, 0, 0);
+    dma_b(rb_fill, stage, fill_slice);
     mfma_block(1);
-    sched_step();
+    // The 8 DMA instructions go one after each of the first 8 MFMAs (issued
+    // together they hold up the matrix core while the address unit takes
+    // the requests of all four waves).
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (r < kSegs) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+      if (r % 2 == 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+    }
   };
 
   // Prologue of the first tile: its ids, the blocks of column 0 and B
