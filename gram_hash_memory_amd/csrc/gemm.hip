@@ -11,11 +11,17 @@
 // Tiling (gfx950: 160 KB LDS per CU, 4 SIMDs): a 256 x 256 output tile per
 // workgroup of 4 waves in a 2 x 2 grid.  Each wave owns 128 x 128 = 4 x 4
 // MFMA tiles, whose 256 fp32 accumulators live in AGPRs.  A and B tiles
-// stream through two LDS stages, each filled from global memory through
-// VGPRs (raw buffer loads, then ds_write_b128) with its loads issued two
-// iterations ahead of the matrix cores.  Fragment reads from LDS are
-// interleaved one-for-two with the MFMAs, and the chunk swizzle keeps them
-// free of bank conflicts.
+// stream through two LDS stages.  Fragment reads from LDS are interleaved
+// one-for-two with the MFMAs, and the chunk swizzle keeps them free of bank
+// conflicts.  Two forms:
+//  - gemm_nt_persistent_kernel (K a multiple of 128, the usual case): one
+//    workgroup per CU walks its tiles; the stages are filled by LDS-DMA a
+//    whole stage ahead, and the next tile's first slices are fetched during
+//    the current tile's last iterations;
+//  - gemm_nt_kernel (one tile per workgroup, any K % 64 == 0): each stage is
+//    filled from global memory through VGPRs (raw buffer loads, then
+//    ds_write_b128), its loads issued two iterations ahead of the matrix
+//    cores.
 //
 // Tile order: the hardware deals workgroups round-robin to the 8 XCDs, each of
 // which has its own L2.  The block id is remapped so that every XCD gets a
@@ -191,19 +197,194 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   store_tile(acc, smem, C, M, N, m0, n0, wm, wn, lane, tid);
 }
 
+// The persistent form (K a multiple of 128), one workgroup per CU walking
+// the tiles b, b + G, b + 2 G, ... of the XCD-aware order.  Both operands
+// come into LDS by LDS-DMA (buffer_load ... lds, 16 bytes per lane), in the
+// same swizzled layout as above.  Iteration kt multiplies stage kt % 2; its
+// barrier waits for stage (kt + 1) % 2, and right after it stage kt % 2,
+// which no wave reads any more, gets slice kt + 2 (in the tile's last two
+// iterations, the next tile's slices 0 and 1), the 16 DMA instructions
+// spread over the MFMAs of the k-step that follows.  The MFMAs take the
+// weight as their first operand, so each output block comes out transposed
+// and the epilogue is wave-private (store_wave_transposed); the same
+// products are summed in the same order, so C is bit-identical to
+// gemm_nt_kernel's.
+__global__ __launch_bounds__(kThreads, 1) void gemm_nt_persistent_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
+    int M, int N, int K, int tiles_m, int tiles_n) {
+  constexpr int BK = 64;
+  constexpr int kOpElems = BM * BK;
+  constexpr int kStageElems = 2 * kOpElems;          // A + B: 64 KB
+  constexpr int kSegs = kOpElems * 2 / 1024 / kWaves; // 1 KB segments per wave per operand
+  extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nk = K / BK;
+  const int tiles = tiles_m * tiles_n;
+  int lid = blockIdx.x;
+  if (lid >= tiles) return;
+  uint16_t *const stg = smem + 2 * kStageElems + wave * 32 * kStgStride;
+
+  // One DMA instruction fills a 1 KB segment (8 tile rows): lane L lands at
+  // byte 16 L (row L / 8, physical chunk L % 8) and fetches the logical chunk
+  // the swizzle keeps there; for segment s the row's key is (L / 8) ^ (s & 1).
+  // The row goes into the VGPR offset (the range-checked part), so rows past
+  // M or N read as zeros; the SGPR offset carries the K position.
+  const int seg_row = lane >> 3;
+  const uint32_t voff_even = uint32_t(seg_row * K + ((lane & 7) ^ seg_row) * 8) * 2;
+  const uint32_t voff_odd = uint32_t(seg_row * K + ((lane & 7) ^ seg_row ^ 1) * 8) * 2;
+  const uint32_t seg_stride = uint32_t(8 * K) * 2;
+  auto rsrc_a = [&](int tm_) {
+    const int m0_ = tm_ * BM;
+    return make_rsrc(A + int64_t(m0_) * K, int64_t(M - m0_) * K * 2);
+  };
+  auto rsrc_b = [&](int tn_) {
+    const int n0_ = tn_ * BN;
+    return make_rsrc(B + int64_t(n0_) * K, int64_t(N - n0_) * K * 2);
+  };
+  auto dma = [&](__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int stage, int slice) {
+    uint16_t *sa = smem + stage * kStageElems;
+    uint16_t *sb = sa + kOpElems;
+#pragma unroll
+    for (int i = 0; i < kSegs; ++i) {
+      const int seg = wave * kSegs + i;
+      const uint32_t v = ((i & 1) ? voff_odd : voff_even) + seg * seg_stride;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, sa + seg * 512, 16, v, slice * BK * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, sb + seg * 512, 16, v, slice * BK * 2, 0, 0);
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  const int frow = lane & 31, fhalf = lane >> 5;
+  bf16x8 fa[2][4], fb[2][4];
+  auto load_frags = [&](int stage, int ks, int slot) {
+    const uint16_t *sa = smem + stage * kStageElems;
+    const uint16_t *sb = sa + kOpElems;
+    const int chunk = 2 * ks + fhalf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      fa[slot][i] =
+          *reinterpret_cast<const bf16x8 *>(sa + swz<BK>(wm * 128 + i * 32 + frow, chunk));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      fb[slot][j] =
+          *reinterpret_cast<const bf16x8 *>(sb + swz<BK>(wn * 128 + j * 32 + frow, chunk));
+  };
+  auto mfma_block = [&](int slot) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][j], fa[slot][i],
+                                                            acc[i][j], 0, 0, 0);
+  };
+  auto sched_reads = [&]() {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+    }
+  };
+  auto sched_reads_dma = [&]() {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+    }
+  };
+  auto iteration = [&](const int stage, __amdgpu_buffer_rsrc_t ra_f, __amdgpu_buffer_rsrc_t rb_f,
+                       int fill_slice) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(stage, 1, 1);
+    mfma_block(0);
+    sched_reads();
+    load_frags(stage, 2, 0);
+    mfma_block(1);
+    sched_reads();
+    load_frags(stage, 3, 1);
+    mfma_block(0);
+    sched_reads();
+    stage_barrier<waitcnt(0, 0)>();
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(stage ^ 1, 0, 0);
+    dma(ra_f, rb_f, stage, fill_slice);
+    mfma_block(1);
+    sched_reads_dma();
+  };
+
+  int tm, tn;
+  tile_coords(lid, tiles_m, tiles_n, tm, tn);
+  __amdgpu_buffer_rsrc_t ra = rsrc_a(tm), rb = rsrc_b(tn);
+  dma(ra, rb, 0, 0);
+  stage_barrier<waitcnt(0, 0)>();
+  dma(ra, rb, 1, 1);
+  load_frags(0, 0, 0);
+
+  for (;;) {
+    const int next = lid + int(gridDim.x);
+    const bool has_next = next < tiles;
+    int tm2 = tm, tn2 = tn;
+    if (has_next) tile_coords(next, tiles_m, tiles_n, tm2, tn2);
+    const __amdgpu_buffer_rsrc_t ra2 = rsrc_a(tm2), rb2 = rsrc_b(tn2);
+    // After the last tile, the final iterations reload slice nk - 1, which
+    // nothing reads.
+    for (int kt = 0; kt < nk; kt += 2) {
+      const bool last = kt + 2 == nk;
+      iteration(0, last ? ra2 : ra, last ? rb2 : rb, last ? (has_next ? 0 : nk - 1) : kt + 2);
+      iteration(1, last ? ra2 : ra, last ? rb2 : rb, last ? (has_next ? 1 : nk - 1) : kt + 3);
+    }
+    store_wave_transposed<4, 4, 1>(acc, stg, C, M, N, tm * BM + wm * 128, tn * BN + wn * 128,
+                                   lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    if (!has_next) break;
+    lid = next;
+    tm = tm2;
+    tn = tn2;
+    ra = ra2;
+    rb = rb2;
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));       // the last, unread reloads
+}
+
 }  // namespace
 
 hipError_t launch_project(const uint16_t *a, const uint16_t *w, uint16_t *c, int32_t M,
                           int32_t K, int32_t N, hipStream_t stream) {
   if (project_uses_skinny(M)) return launch_project_skinny(a, w, c, M, K, N, stream);
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const size_t lds = size_t(2) * (BM + BN) * 64 * sizeof(uint16_t);
+  const int tiles = tiles_m * tiles_n;
+  const size_t lds_stages = size_t(2) * (BM + BN) * 64 * sizeof(uint16_t);
+  // K % 128 == 0: the persistent form (two stages per unrolled step, so the
+  // stage of a tile's first slice is always 0); else one tile per workgroup.
+  if (K % 128 == 0) {
+    const size_t lds = lds_stages + size_t(kWaves) * 32 * kStgStride * sizeof(uint16_t);
+    const void *fn = reinterpret_cast<const void *>(&gemm_nt_persistent_kernel);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gemm_nt_persistent_kernel, dim3(persistent_grid(tiles, stream)),
+                       dim3(kThreads), lds, stream, a, w, c, M, N, K, tiles_m, tiles_n);
+    return hipGetLastError();
+  }
   const void *fn = reinterpret_cast<const void *>(&gemm_nt_kernel);
   // Set on every call: the attribute is per device, and the call is cheap.
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  hipError_t e =
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_stages));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gemm_nt_kernel, dim3(tiles_m * tiles_n), dim3(kThreads), lds, stream, a,
-                     w, c, M, N, K, tiles_m, tiles_n);
+  hipLaunchKernelGGL(gemm_nt_kernel, dim3(tiles), dim3(kThreads), lds_stages, stream, a, w, c, M,
+                     N, K, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

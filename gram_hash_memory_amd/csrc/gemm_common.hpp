@@ -3,6 +3,8 @@
 // XCD-aware tile order, buffer resources and the pipeline barrier.
 #pragma once
 
+#include <atomic>
+
 #include "common.hpp"
 
 namespace engram {
@@ -121,11 +123,88 @@ __device__ __forceinline__ void store_tile_blocks(const f32x16 (&acc)[NI][NJ], u
   }
 }
 
+// Epilogue of one wave whose MFMAs took the weight as first operand, so that
+// each 32 x 32 block comes out transposed: register r of lane (t, h) in
+// acc[i][j] is row row0 + 32 i + t, column col0 + 32 j + 8 (r / 4) + 4 h +
+// r % 4.  The wave packs a lane's 4 consecutive columns into 8 bytes of its
+// own LDS staging area `stg` (32 kCI rows of kStgStride bf16), a chunk of kCI
+// row blocks x 2 column blocks at a time, then reads back 16-byte row pieces
+// and stores 128-byte row segments.  A wave's LDS accesses complete in order,
+// so no barrier is needed; no other wave touches `stg`.
+constexpr int kStgStride = 72;   // 144-byte rows: 16-byte aligned, rows 16 apart on other banks
+template <int NI, int NJ, int kCI>
+__device__ __forceinline__ void store_wave_transposed(const f32x16 (&acc)[NI][NJ], uint16_t *stg,
+                                                      uint16_t *__restrict__ C, int M, int N,
+                                                      int row0, int col0, int lane) {
+  static_assert(NI % kCI == 0 && NJ % 2 == 0, "whole chunks");
+  const int frow = lane & 31, fhalf = lane >> 5;
+  const bool vec = (N % 8) == 0;
+#pragma unroll
+  for (int ci = 0; ci < NI / kCI; ++ci)
+#pragma unroll
+    for (int cj = 0; cj < NJ / 2; ++cj) {
+#pragma unroll
+      for (int ii = 0; ii < kCI; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x16 &a = acc[ci * kCI + ii][2 * cj + jj];
+            const u32x2 v = {pack_bf16x2(a[4 * g], a[4 * g + 1]),
+                             pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
+            *reinterpret_cast<u32x2 *>(stg + (ii * 32 + frow) * kStgStride + jj * 32 + 8 * g +
+                                       4 * fhalf) = v;
+          }
+#pragma unroll
+      for (int r8 = 0; r8 < 4 * kCI; ++r8) {
+        const int row = r8 * 8 + (lane >> 3), c8 = (lane & 7) * 8;
+        const int grow = row0 + ci * kCI * 32 + row, gcol = col0 + cj * 64 + c8;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + row * kStgStride + c8);
+        if (grow < M && gcol < N) {
+          uint16_t *dst = C + int64_t(grow) * N + gcol;
+          if (vec) {
+            *reinterpret_cast<u32x4 *>(dst) = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (gcol + e < N) dst[e] = uint16_t(v[e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      }
+    }
+}
+
 // The 2 x 2 wave layout of 128 x 128 per wave (wave (wm, wn)).
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], uint16_t *smem,
                                            uint16_t *__restrict__ C, int M, int N, int m0,
                                            int n0, int wm, int wn, int lane, int tid) {
   store_tile_blocks<4, 4>(acc, smem, C, M, N, m0, n0, wm * 128, wn * 128, lane, tid);
+}
+
+// Compute units of the stream's device (the grid of the persistent kernels),
+// read once per device.
+inline int num_cus(hipStream_t stream) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= 64) {
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  }
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Grid of a persistent kernel over `tiles` tiles: one workgroup per CU, and,
+// when a workgroup gets several tiles, a multiple of 8 so that tile ids b,
+// b + grid, ... all lie in workgroup b's XCD run of tile_coords.
+inline int persistent_grid(int tiles, hipStream_t stream) {
+  const int cus = num_cus(stream);
+  return tiles <= cus ? tiles : (cus / 8 * 8 > 8 ? cus / 8 * 8 : 8);
 }
 
 }  // namespace gemm

@@ -47,7 +47,6 @@
 // group decode, the tiles of any M-tile that has such a block
 // (gemm_q2k_exact_kernel).
 #include <algorithm>
-#include <atomic>
 
 #include "gemm_common.hpp"
 #include "q2k_decode.hpp"
@@ -307,11 +306,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
   q2k_tile<false>(table, num_rows, ids, ids_stride, B, C, M, N, K, tm, tn, smem);
 }
 
-// Staging row stride of the persistent kernel's epilogue, in bf16: 144 bytes
-// keeps 16-byte alignment and puts rows 16 apart on other banks than rows
-// 0..15 (a 2-way conflict at most for the 8-byte writes).
-constexpr int kStgStride = 72;
-
 // The persistent form (cols even).  Workgroup b runs the tiles whose ids in
 // the XCD-aware order (tile_coords) are b, b + G, b + 2 G, ... (G = grid
 // size, a multiple of 8 when a workgroup has more than one tile, so all of
@@ -454,7 +448,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_persistent_kernel(
   load_b(0, 0, 0);
   decode_a(0, 0, 0, 0);
 
-  const bool vec = (N % 8) == 0;
   for (;;) {
     const int next = lid + int(gridDim.x);
     const bool has_next = next < tiles;
@@ -482,42 +475,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_persistent_kernel(
       iteration(kt + 7, 7, last ? rb2 : rb, last ? (has_next ? 1 : nk - 1) : kt + 9);
     }
 
-    // Epilogue, per wave: its 64 rows in 4 chunks of 64 columns.  A lane
-    // packs its 4 consecutive columns of a block row into 8 bytes of the
-    // staging area; the wave then reads back 16-byte row pieces and stores
-    // 128-byte row segments.  A wave's LDS accesses complete in order, so
-    // neither step needs a barrier.
-#pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
-#pragma unroll
-      for (int i = 0; i < kRowsPerLane; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x16 &a = acc[i][2 * c4 + jj];
-            const u32x2 v = {pack_bf16x2(a[4 * g], a[4 * g + 1]),
-                             pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
-            *reinterpret_cast<u32x2 *>(stg + (i * 32 + frow) * kStgStride + jj * 32 + 8 * g +
-                                       4 * fhalf) = v;
-          }
-#pragma unroll
-      for (int r8 = 0; r8 < 8; ++r8) {
-        const int row = r8 * 8 + (lane >> 3), c8 = (lane & 7) * 8;
-        const int grow = m0 + wave * 64 + row, gcol = n0 + c4 * 64 + c8;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + row * kStgStride + c8);
-        if (grow < M && gcol < N) {
-          uint16_t *dst = C + int64_t(grow) * N + gcol;
-          if (vec) {
-            *reinterpret_cast<u32x4 *>(dst) = v;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (gcol + e < N) dst[e] = uint16_t(v[e >> 1] >> (16 * (e & 1)));
-          }
-        }
-      }
-    }
+    // Epilogue, per wave: its 64 rows in 4 chunks of 64 columns.
+    store_wave_transposed<kRowsPerLane, kNJ, kRowsPerLane>(acc, stg, C, M, N, m0 + wave * 64, n0,
+                                                           lane);
 #pragma unroll
     for (int i = 0; i < kRowsPerLane; ++i)
 #pragma unroll
@@ -578,23 +538,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_exact_kernel(
   }
 }
 
-// Compute units of each device (the persistent grid), read once.
-int num_cus(hipStream_t stream) {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= 64) {
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  }
-  int n = cache[dev].load(std::memory_order_relaxed);
-  if (n <= 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cache[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 }  // namespace
 
 static_assert(ENGRAM_Q2K_FUSED_MAX_BYTES + 128 <= int64_t(kNoRow),
@@ -635,12 +578,9 @@ hipError_t launch_project_q2k(const uint8_t *table, int64_t num_rows, const int3
   if (e != hipSuccess) return e;
   const int tiles = tiles_m * tiles_n;
   if (persistent) {
-    // One workgroup per CU; when a workgroup gets several tiles the grid is a
-    // multiple of 8, so that they all lie in its XCD's run of tile_coords.
-    const int cus = num_cus(stream);
-    const int grid = tiles <= cus ? tiles : std::max(8, cus / 8 * 8);
-    hipLaunchKernelGGL(gemm_q2k_persistent_kernel, dim3(grid), dim3(kThreads), lds_pers, stream,
-                       table, num_rows, ids, ids_token_stride, w, c, M, N, K, tiles_m, tiles_n);
+    hipLaunchKernelGGL(gemm_q2k_persistent_kernel, dim3(persistent_grid(tiles, stream)),
+                       dim3(kThreads), lds_pers, stream, table, num_rows, ids, ids_token_stride, w,
+                       c, M, N, K, tiles_m, tiles_n);
   } else {
     hipLaunchKernelGGL(gemm_q2k_kernel, dim3(tiles), dim3(kThreads), lds, stream, table,
                        num_rows, ids, ids_token_stride, w, c, M, N, K, tiles_m, tiles_n);

@@ -324,11 +324,13 @@ def _check_kv(got_bits, rows_bits, wkv_bits):
 
 
 # Few tokens (<= 128) take the weight-streaming kernel (64- or 128-token tiles), more the
-# 256 x 256 tiles.
+# 256 x 256 tiles: the persistent form when K % 128 == 0 (more tiles than compute units
+# in the last two shapes, N % 8 != 0 in the last), one tile per workgroup otherwise.
 @pytest.mark.parametrize("M,N,K", [(1, 64, 64), (300, 520, 512), (257, 256, 1536),
                                    (512, 768, 192), (3, 16, 128), (17, 80, 6144),
                                    (64, 20480, 6144), (65, 1000, 1536), (100, 300, 320),
-                                   (128, 384, 256), (129, 384, 256), (96, 20480, 6144)])
+                                   (128, 384, 256), (129, 384, 256), (96, 20480, 6144),
+                                   (700, 300, 64), (1800, 8200, 256), (1500, 16390, 128)])
 def test_project_ragged_shapes_full_compare(eg, M, N, K):
     rng = np.random.default_rng(M + N + K)
     a = oracle.bf16_bits(oracle.bf16_round(rng.standard_normal((M, K))))
