@@ -283,6 +283,233 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
   store_tile(acc, reinterpret_cast<uint16_t *>(smem), C, M, N, m0, n0, wm, wn, lane, tid);
 }
 
+// The persistent form (cols >= 2): one workgroup per CU walks the tiles b,
+// b + G, b + 2 G, ... of the XCD-aware order with the K loop above, which
+// runs on from tile to tile: the ids two columns ahead, the resolved A
+// addresses and the DMA of the stage after next simply continue into the
+// next tile's first columns (with its rows, its B resources), so the next
+// tile's first stages are in LDS when the current tile ends.  The MFMAs take
+// the weight as their first operand, so each output block comes out
+// transposed and the epilogue is wave-private (store_wave_transposed).  Ids
+// outside the table are counted as their column's addresses are resolved,
+// for the tiles of the first column of tiles.
+__global__ __launch_bounds__(kThreads, 1) void gemm_mx_persistent_kernel(
+    const uint8_t *__restrict__ table, const uint8_t *__restrict__ tscales, int64_t num_rows,
+    const int32_t *__restrict__ ids, int64_t ids_stride, const uint8_t *__restrict__ W,
+    const uint8_t *__restrict__ WS, uint16_t *__restrict__ C, int M, int N, int K,
+    int tiles_m, int tiles_n, int32_t *__restrict__ bad_ids) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int cols = K / ENGRAM_HEAD_DIM;
+  const int nk = K / kBK;                            // 2 stages per table column
+  const int ks = K / 32;                             // scale bytes per row
+  const int tiles = tiles_m * tiles_n;
+  int lid = blockIdx.x;
+  if (lid >= tiles) return;
+  uint16_t *const stg =
+      reinterpret_cast<uint16_t *>(smem + 2 * kStageBytes) + wave * 32 * kStgStride;
+
+  // B codes and scales as in gemm_mx_kernel, per tile column tn.
+  const int seg_row = lane >> 3;
+  const uint32_t voff_even = uint32_t(seg_row * K + ((lane & 7) ^ seg_row) * 16);
+  const uint32_t voff_odd = uint32_t(seg_row * K + ((lane & 7) ^ seg_row ^ 1) * 16);
+  const uint32_t voff_bs = uint32_t((wave * 64 + lane) * ks);
+  auto rsrc_b = [&](int tn_) {
+    const int n0_ = tn_ * BN;
+    return make_rsrc(W + int64_t(n0_) * K, int64_t(N - n0_) * K);
+  };
+  auto rsrc_bs = [&](int tn_) {
+    const int n0_ = tn_ * BN;
+    return make_rsrc(WS + int64_t(n0_) * ks, int64_t(N - n0_) * ks);
+  };
+
+  // A: the ids of one column of one tile (rows row0 .. row0 + 63 of this
+  // wave) and their resolved addresses, as in gemm_mx_kernel.
+  const __amdgpu_buffer_rsrc_t rid = make_rsrc(ids, int64_t(M) * ids_stride * 4);
+  const int chunk_even = ((lane & 7) ^ seg_row) * 16, chunk_odd = chunk_even ^ 16;
+  int32_t idn[kIdsPerLane];
+  int idn_row0 = 0;
+  bool idn_count = false;
+  int bad = 0;
+  const uint8_t *a_src[kSegs];
+  const uint8_t *as_src;
+  auto load_ids = [&](int tm_, int c, bool count) {
+    const int row0 = tm_ * BM + wave * 64;
+    const uint32_t voff_id = uint32_t((row0 + seg_row) * ids_stride * 4);
+    const uint32_t voff_ids = uint32_t((row0 + lane) * ids_stride * 4);
+#pragma unroll
+    for (int k = 0; k < kSegs; ++k)
+      idn[k] = __builtin_amdgcn_raw_buffer_load_b32(
+          rid, voff_id + uint32_t(8 * k * ids_stride * 4), c * 4, 0);
+    idn[kSegs] = __builtin_amdgcn_raw_buffer_load_b32(rid, voff_ids, c * 4, 0);
+    idn_row0 = row0;
+    idn_count = count;
+  };
+  auto resolve = [&]() {
+#pragma unroll
+    for (int k = 0; k < kSegs; ++k) {
+      const bool ok = idn_row0 + 8 * k + seg_row < M && idn[k] >= 0 && idn[k] < num_rows;
+      a_src[k] = (ok ? table + int64_t(idn[k]) * ENGRAM_HEAD_DIM : kZeroRow) +
+                 ((k & 1) ? chunk_odd : chunk_even);
+    }
+    const bool row_ok = idn_row0 + lane < M;
+    const bool ok = row_ok && idn[kSegs] >= 0 && idn[kSegs] < num_rows;
+    as_src = ok ? tscales + int64_t(idn[kSegs]) * (ENGRAM_HEAD_DIM / 32) : kZeroRow;
+    bad += idn_count && row_ok && !ok;
+  };
+  // Stage of B slice kb (K positions 128 kb ..) and A half `half` of the
+  // resolved column into LDS buffer `buf`.
+  auto dma = [&](int buf, __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rbs, int kb,
+                 const int half) {
+    uint8_t *st = smem + buf * kStageBytes;
+#pragma unroll
+    for (int i = 0; i < kSegs; ++i) {
+      const int seg = wave * kSegs + i;
+      __builtin_amdgcn_global_load_lds(a_src[i] + half * kBK, lds_ptr(st + seg * 1024), 16, 0,
+                                       0);
+    }
+#pragma unroll
+    for (int i = 0; i < kSegs; ++i) {
+      const int seg = wave * kSegs + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, lds_ptr(st + kTileBytes + seg * 1024), 16,
+                                               ((i & 1) ? voff_odd : voff_even) + seg * 8 * K,
+                                               kb * kBK, 0, 0);
+    }
+    __builtin_amdgcn_global_load_lds(as_src + half * 4,
+                                     lds_ptr(st + 2 * kTileBytes + wave * 256), 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rbs, lds_ptr(st + 2 * kTileBytes + kScaleBytes + wave * 256), 4, voff_bs, kb * 4, 0, 0);
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  const int frow = lane & 31, fhalf = lane >> 5;
+  const int fkey = swz_key<64>(frow);
+  const int a_frag = (wm * 128 + frow) * kBK, b_frag = kTileBytes + (wn * 128 + frow) * kBK;
+  i32x8 fa[2][4], fb[2][4];
+  uint32_t sca[2][4], scb[2][4];
+  auto read_frag = [&](int buf, int base, int f, const int s) {
+    const uint8_t *p = smem + buf * kStageBytes + base + f * 32 * kBK;
+    const u32x4 lo = *reinterpret_cast<const u32x4 *>(p + (((4 * s + fhalf) ^ fkey) << 4));
+    const u32x4 hi = *reinterpret_cast<const u32x4 *>(p + (((4 * s + 2 + fhalf) ^ fkey) << 4));
+    return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto load_scales = [&](int buf, const int set) {
+    const uint32_t *ss = reinterpret_cast<const uint32_t *>(smem + buf * kStageBytes +
+                                                            2 * kTileBytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sca[set][i] = ss[wm * 128 + i * 32 + frow] >> (8 * fhalf);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) scb[set][j] = ss[BM + wn * 128 + j * 32 + frow] >> (8 * fhalf);
+  };
+  auto load_frags = [&](int buf, const int s, const int slot) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      fa[slot][f] = read_frag(buf, a_frag, f, s);
+      fb[slot][f] = read_frag(buf, b_frag, f, s);
+    }
+  };
+  auto mfma_block = [&](const int slot, const int set, const int s) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (s == 0)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fb[slot][j], fa[slot][i], acc[i][j], 0, 0, 0, scb[set][j], 0, sca[set][i]);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fb[slot][j], fa[slot][i], acc[i][j], 0, 0, 2, scb[set][j], 2, sca[set][i]);
+      }
+  };
+
+  // Iteration kt (j = kt % 2) as in gemm_mx_kernel; the ids requested at
+  // even kt are those of sequence column kt / 2 + 2 (the next tile's column
+  // kt / 2 + 2 - cols past this tile's last), and the stage filled after the
+  // middle barrier is the sequence's stage kt + 2.
+  auto iteration = [&](const int j, int ids_tm, int ids_col, bool ids_count,
+                       __amdgpu_buffer_rsrc_t rb_f, __amdgpu_buffer_rsrc_t rbs_f, int fill_kb) {
+    const int b = j;
+    __builtin_amdgcn_sched_barrier(0);
+    if (j == 0) load_ids(ids_tm, ids_col, ids_count);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(b, 1, 1);
+    mfma_block(0, j, 0);
+    sched_substep<16>();
+    if (j == 0) stage_barrier<waitcnt(kIdsPerLane, 0)>();
+    else stage_barrier<waitcnt(0, 0)>();
+    dma(b, rb_f, rbs_f, fill_kb, j);
+    if (j == 1) resolve();
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(b ^ 1, 0, 0);
+    load_scales(b ^ 1, j ^ 1);
+    mfma_block(1, j, 1);
+    sched_substep<24>();
+  };
+
+  // Prologue: the first tile's stages 0 and 1 (column 0) in flight, then
+  // column 1's addresses.
+  int tm, tn;
+  tile_coords(lid, tiles_m, tiles_n, tm, tn);
+  __amdgpu_buffer_rsrc_t rb = rsrc_b(tn), rbs = rsrc_bs(tn);
+  const bool counting = bad_ids != nullptr;
+  load_ids(tm, 0, counting && tn == 0);
+  resolve();
+  dma(0, rb, rbs, 0, 0);
+  dma(1, rb, rbs, 1, 1);
+  load_ids(tm, 1, counting && tn == 0);
+  resolve();
+  stage_barrier<waitcnt(0, 0)>();
+  load_frags(0, 0, 0);
+  load_scales(0, 0);
+
+  for (;;) {
+    const int next = lid + int(gridDim.x);
+    const bool has_next = next < tiles;
+    int tm2 = tm, tn2 = tn;
+    if (has_next) tile_coords(next, tiles_m, tiles_n, tm2, tn2);
+    const __amdgpu_buffer_rsrc_t rb2 = rsrc_b(tn2), rbs2 = rsrc_bs(tn2);
+    for (int kt = 0; kt < nk; kt += 2) {
+      // Sequence column c + 2 for the ids, stages kt + 2 and kt + 3 for the
+      // DMA; after the last tile they repeat this tile's last column and
+      // stage, which nothing reads.
+      const int c2 = kt / 2 + 2;
+      const bool nxt = c2 >= cols;
+      const int ids_tm = nxt && has_next ? tm2 : tm;
+      const int ids_col = nxt ? (has_next ? c2 - cols : cols - 1) : c2;
+      const bool ids_count = counting && (nxt ? has_next && tn2 == 0 : tn == 0);
+      const bool fill_next = kt + 2 >= nk;
+      const __amdgpu_buffer_rsrc_t rbf = fill_next && has_next ? rb2 : rb;
+      const __amdgpu_buffer_rsrc_t rbsf = fill_next && has_next ? rbs2 : rbs;
+      const int kb0 = fill_next ? (has_next ? kt + 2 - nk : nk - 1) : kt + 2;
+      const int kb1 = fill_next ? (has_next ? kt + 3 - nk : nk - 1) : kt + 3;
+      iteration(0, ids_tm, ids_col, ids_count, rbf, rbsf, kb0);
+      iteration(1, ids_tm, ids_col, ids_count, rbf, rbsf, kb1);
+    }
+    store_wave_transposed<4, 4, 1>(acc, stg, C, M, N, tm * BM + wm * 128, tn * BN + wn * 128,
+                                   lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    if (!has_next) break;
+    lid = next;
+    tm = tm2;
+    tn = tn2;
+    rb = rb2;
+    rbs = rbs2;
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));        // the last, unread reloads
+  if (bad) atomicAdd(bad_ids, bad);
+}
+
 }  // namespace
 
 bool project_mx_supported(int32_t N, int32_t K) {
@@ -298,6 +525,17 @@ hipError_t launch_project_mx(const uint8_t *table, const uint8_t *scales, int64_
                                     w_codes, w_scales, c, M, N, bad_ids, stream);
   const int K = cols * ENGRAM_HEAD_DIM;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  if (cols >= 2) {
+    const size_t lds = size_t(2) * kStageBytes + size_t(kWaves) * 32 * kStgStride * 2;
+    const void *fn = reinterpret_cast<const void *>(&gemm_mx_persistent_kernel);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gemm_mx_persistent_kernel, dim3(persistent_grid(tiles_m * tiles_n, stream)),
+                       dim3(kThreads), lds, stream, table, scales, num_rows, ids,
+                       ids_token_stride, w_codes, w_scales, c, M, N, K, tiles_m, tiles_n,
+                       bad_ids);
+    return hipGetLastError();
+  }
   const size_t lds = size_t(2) * kStageBytes;
   const void *fn = reinterpret_cast<const void *>(&gemm_mx_kernel);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
