@@ -13,7 +13,8 @@ from ._binding import (  # noqa: F401
     ENGRAM_OK, ENGRAM_ERR_ARG, ENGRAM_ERR_UNSUPPORTED, ENGRAM_ERR_HIP,
     ENGRAM_ROWS_Q2K, ENGRAM_ROWS_FP8_E4M3_E8M0, HEAD_DIM, Q2K_ROW_BYTES, FP8_ROW_BYTES,
     FP8_SCALE_BYTES, EXPORTS, LIB_PATH, EngramError, HashParams, Tokens, Layer,
-    engram_hash, engram_history_update, engram_rows, engram_project, engram_project_q2k, engram_quantize_mxfp8,
+    engram_hash, engram_history_update, engram_rows, engram_project, engram_project_q2k,
+    engram_project_fp8, engram_quantize_mxfp8,
     engram_project_mxfp8, engram_gate, engram_gate_layers, engram_workspace_bytes, engram_forward, engram_last_error,
     engram_build_id, BUILD_ID, engram_forward_noalloc, FORWARD_NOALLOC_MAX_BYTES,
 )

@@ -29,7 +29,7 @@ ENGRAM_ROWS_Q2K, ENGRAM_ROWS_FP8_E4M3_E8M0 = 0, 1
 HEAD_DIM, Q2K_ROW_BYTES, FP8_ROW_BYTES, FP8_SCALE_BYTES = 256, 84, 256, 8
 
 EXPORTS = ("engram_hash", "engram_history_update", "engram_rows", "engram_project", "engram_project_q2k",
-           "engram_quantize_mxfp8", "engram_project_mxfp8", "engram_gate",
+           "engram_project_fp8", "engram_quantize_mxfp8", "engram_project_mxfp8", "engram_gate",
            "engram_gate_layers", "engram_workspace_bytes", "engram_forward", "engram_last_error",
            "engram_build_id", "engram_forward_noalloc")
 
@@ -85,6 +85,8 @@ _lib.engram_project.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, 
                                 c_void_p]
 _lib.engram_project_q2k.argtypes = [c_void_p, c_int64, c_void_p, c_int64, c_int32, c_void_p,
                                     c_void_p, c_int32, c_int32, c_void_p, c_void_p]
+_lib.engram_project_fp8.argtypes = [c_void_p, c_void_p, c_int64, c_void_p, c_int64, c_int32,
+                                   c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p]
 _lib.engram_quantize_mxfp8.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
 _lib.engram_project_mxfp8.argtypes = [c_void_p, c_void_p, c_int64, c_void_p, c_int64, c_int32,
                                       c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
@@ -242,6 +244,20 @@ def engram_project_q2k(table, num_rows: int, ids, ids_token_stride: int, cols: i
     need_ids = 0 if T <= 0 else (T - 1) * ids_token_stride + cols
     _check(_lib.engram_project_q2k(
         _dptr(table, torch.uint8, num_rows * Q2K_ROW_BYTES, "table"), int(num_rows),
+        _dptr(ids, torch.int32, need_ids, "ids"), int(ids_token_stride), int(cols),
+        _dptr(wkv, torch.int16, N * K, "wkv"), _dptr(kv, torch.int16, T * N, "kv"), int(T),
+        int(N), _dptr(bad_ids, torch.int32, 1, "bad_ids"), _stream(stream)))
+
+
+def engram_project_fp8(table, scales, num_rows: int, ids, ids_token_stride: int, cols: int, wkv,
+                       kv, T: int, N: int, bad_ids=None, stream=None) -> None:
+    """Stages 2 + 3 fused for an FP8 table with the bf16 weight: kv [T, N] from
+    ids, bit-identical to engram_rows followed by engram_project."""
+    K = cols * HEAD_DIM
+    need_ids = 0 if T <= 0 else (T - 1) * ids_token_stride + cols
+    _check(_lib.engram_project_fp8(
+        _dptr(table, torch.uint8, num_rows * FP8_ROW_BYTES, "table"),
+        _dptr(scales, torch.uint8, num_rows * FP8_SCALE_BYTES, "scales"), int(num_rows),
         _dptr(ids, torch.int32, need_ids, "ids"), int(ids_token_stride), int(cols),
         _dptr(wkv, torch.int16, N * K, "wkv"), _dptr(kv, torch.int16, T * N, "kv"), int(T),
         int(N), _dptr(bad_ids, torch.int32, 1, "bad_ids"), _stream(stream)))

@@ -24,7 +24,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libengram.so")
 SOURCES = ["api.cpp", "hash.hip", "rows.hip", "gemm.hip", "gemm_skinny.hip", "gemm_q2k.hip",
-           "gemm_mx.hip", "mx_quant.hip", "gate.hip"]
+           "gemm_fp8.hip", "gemm_mx.hip", "mx_quant.hip", "gate.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

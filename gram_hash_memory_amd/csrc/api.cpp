@@ -284,6 +284,30 @@ engram_status check_project_mx(const uint8_t *table, const uint8_t *scales, int6
 }
 }  // namespace
 
+engram_status engram_project_fp8(const uint8_t *table, const uint8_t *scales, int64_t num_rows,
+                                 const int32_t *ids, int64_t ids_token_stride, int32_t cols,
+                                 const uint16_t *wkv, uint16_t *kv, int32_t T, int32_t N,
+                                 int32_t *bad_ids, hipStream_t stream) {
+  engram_status st =
+      check_rows_shape(ENGRAM_ROWS_FP8_E4M3_E8M0, num_rows, ids_token_stride, cols, T);
+  if (st != ENGRAM_OK) return st;
+  REQUIRE(int64_t(cols) * ENGRAM_HEAD_DIM <= kInt32Max, "cols=%d too large", cols);
+  const int32_t K = cols * ENGRAM_HEAD_DIM;
+  if ((st = check_project_shape(T, K, N)) != ENGRAM_OK) return st;
+  REQUIRE_SUP(int64_t(T) * ids_token_stride * 4 <= ENGRAM_FP8_FUSED_MAX_ID_BYTES,
+              "T * ids_token_stride * 4 exceeds %lld", (long long)ENGRAM_FP8_FUSED_MAX_ID_BYTES);
+  if (T == 0) return ENGRAM_OK;
+  REQUIRE(table && aligned(table, 16), "table is NULL or not 16-byte aligned");
+  REQUIRE(scales && aligned(scales, 4), "scales is NULL or not 4-byte aligned");
+  REQUIRE(ids && aligned(ids, 4), "ids is NULL or misaligned");
+  REQUIRE(!bad_ids || aligned(bad_ids, 4), "bad_ids misaligned");
+  REQUIRE(wkv && kv && aligned(wkv, 16) && aligned(kv, 16),
+          "wkv or kv is NULL or not 16-byte aligned");
+  return hip_status(engram::launch_project_fp8(table, scales, num_rows, ids, ids_token_stride,
+                                               cols, wkv, kv, T, N, bad_ids, stream),
+                    "engram_project_fp8 launch");
+}
+
 engram_status engram_project_mxfp8(const uint8_t *table, const uint8_t *scales,
                                    int64_t num_rows, const int32_t *ids,
                                    int64_t ids_token_stride, int32_t cols,
@@ -420,7 +444,10 @@ engram_status forward_impl(const engram_hash_params *params, const engram_tokens
     gl.kw[l] = ly.k_weight;
     // Q2_K: the fused rows + projection (its weight-streaming form for few
     // tokens).  Few tokens with cols % 4 != 0: rows -> the weight-streaming
-    // projection, which beats the fused 256 x 256 tiles there.
+    // projection, which beats the fused 256 x 256 tiles there.  FP8 without
+    // an MXFP8 weight: rows -> projection, which measures faster than
+    // engram_project_fp8 (the rows kernel gathers whole rows once; the fused
+    // kernel gathers 128-byte pieces of random rows for every tile column).
     if (ly.wkv_mx) {
       if ((st = hip_status(engram::launch_project_mx(ly.table, ly.scales, ly.num_rows,
                                                      ids + l * cols, int64_t(L) * cols, cols,

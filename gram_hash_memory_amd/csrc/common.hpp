@@ -31,6 +31,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// OCP FP8 E4M3 (fn) code -> fp32, from the format's fields (code 0x7F / 0xFF:
+// the quiet NaN of that sign).
+__device__ __forceinline__ float e4m3fn_to_float(uint32_t b) {
+  const uint32_t sign = (b & 0x80u) << 24;
+  const uint32_t e = (b >> 3) & 0xFu, m = b & 0x7u;
+  if (e == 0) return __uint_as_float(sign | __float_as_uint(float(m) * 0x1p-9f));
+  if (e == 15 && m == 7) return __uint_as_float(0x7FC00000u | sign);
+  return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
+}
+
+// An E8M0 scale byte as fp32: the byte in the binary32 exponent field (0 gives
+// 0, 255 gives inf).
+__device__ __forceinline__ float e8m0_to_float(uint32_t b) { return __uint_as_float(b << 23); }
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -79,6 +93,13 @@ hipError_t launch_project_q2k(const uint8_t *table, int64_t num_rows, const int3
                               int64_t ids_token_stride, int32_t cols, const uint16_t *w,
                               uint16_t *c, int32_t M, int32_t N, int32_t *bad_ids,
                               hipStream_t stream);
+
+// Rows + bf16 projection fused for FP8 tables (gemm_fp8.hip; kv bit-identical
+// to rows -> project), for more than 128 tokens.
+hipError_t launch_project_fp8(const uint8_t *table, const uint8_t *scales, int64_t num_rows,
+                              const int32_t *ids, int64_t ids_token_stride, int32_t cols,
+                              const uint16_t *w, uint16_t *c, int32_t M, int32_t N,
+                              int32_t *bad_ids, hipStream_t stream);
 
 // MXFP8 projection for FP8 tables (gemm_mx.hip) and its weight prep (mx_quant.hip).
 // launch_project_mx runs the weight-streaming form (gemm_skinny.hip) where

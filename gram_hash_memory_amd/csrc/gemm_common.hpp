@@ -181,6 +181,70 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], uint16_t *
   store_tile_blocks<4, 4>(acc, smem, C, M, N, m0, n0, wm * 128, wn * 128, lane, tid);
 }
 
+// The fused projections' layout (gemm_q2k.hip, gemm_fp8.hip): 4 x 1 waves,
+// each wave 64 tile rows x all 256 columns (2 x 8 blocks of 32 x 32), K in
+// stages of 64, only B (bf16) in shared LDS stages.
+namespace wide {
+
+constexpr int kRowsPerLane = 2;            // tile rows w * 64 + 32 i + (lane % 32), i = 0, 1
+constexpr int kNJ = BN / 32;               // 8 column blocks per wave
+constexpr int BK = 64;
+constexpr int kStageElems = BN * BK;                 // one B stage: 32 KB
+constexpr int kSegs = BN * BK * 2 / 1024 / kWaves;   // 1 KB B segments per wave per stage: 8
+
+// ---- B: global -> LDS by LDS-DMA.  One instruction fills a 1 KB segment (8
+// tile rows); lane L lands at byte 16 L, i.e. row L / 8 of the segment,
+// physical chunk L % 8, and fetches the logical chunk the swizzle keeps
+// there.  For segment s the swizzle key of that row is (L / 8) ^ (s & 1).
+// Rows past N read as zeros (the resource starts at the tile's first row, and
+// the row is part of the VGPR offset, the range-checked part; the SGPR offset
+// only carries the K position).
+struct BSegs {
+  uint32_t voff_even, voff_odd, seg_stride;
+};
+__device__ __forceinline__ BSegs b_segs(int lane, int K) {
+  const int seg_row = lane >> 3;
+  return {uint32_t(seg_row * K + ((lane & 7) ^ seg_row) * 8) * 2,
+          uint32_t(seg_row * K + ((lane & 7) ^ seg_row ^ 1) * 8) * 2, uint32_t(8 * K) * 2};
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t b_rsrc(const uint16_t *B, int N, int K, int tn) {
+  const int n0 = tn * BN;
+  return make_rsrc(B + int64_t(n0) * K, int64_t(N - n0) * K * 2);
+}
+// B slice `slice` (K positions 64 slice ..) of the tile into LDS stage sb.
+__device__ __forceinline__ void dma_b_slice(__amdgpu_buffer_rsrc_t rb, uint16_t *sb,
+                                            const BSegs &g, int wave, int slice) {
+#pragma unroll
+  for (int i = 0; i < kSegs; ++i) {
+    const int seg = wave * kSegs + i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, sb + seg * 512, 16,
+                                             ((i & 1) ? g.voff_odd : g.voff_even) +
+                                                 seg * g.seg_stride,
+                                             slice * BK * 2, 0, 0);
+  }
+}
+// The 8 B fragments of k-step ks of an LDS stage (block j: columns 32 j ..).
+__device__ __forceinline__ void load_b_frags(const uint16_t *sb, int frow, int fhalf, int ks,
+                                             bf16x8 (&fb)[kNJ]) {
+  const int chunk = 2 * ks + fhalf;
+#pragma unroll
+  for (int j = 0; j < kNJ; ++j)
+    fb[j] = *reinterpret_cast<const bf16x8 *>(sb + swz<BK>(j * 32 + frow, chunk));
+}
+// One k-step: 16 MFMAs (32 cycles of matrix core each), the next step's 8 B
+// fragment reads and kValu VALU ops (the A decode) after each MFMA.
+template <int kValu>
+__device__ __forceinline__ void sched_step_valu() {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (r % 2 == 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, kValu, 0);
+  }
+}
+
+}  // namespace wide
+
 // Compute units of the stream's device (the grid of the persistent kernels),
 // read once per device.
 inline int num_cus(hipStream_t stream) {

@@ -55,10 +55,9 @@ namespace engram {
 namespace {
 
 using namespace gemm;
+using namespace gemm::wide;
 
 constexpr uint32_t kNoRow = 0x7FFFFFF0u;   // block offset past the table: loads read 0
-constexpr int kRowsPerLane = 2;            // tile rows w * 64 + 32 i + (lane % 32), i = 0, 1
-constexpr int kNJ = BN / 32;               // 8 column blocks per wave
 
 // The register copy of the block parts one lane needs for one row.
 struct Q2kPart {
@@ -67,49 +66,6 @@ struct Q2kPart {
   uint32_t dd;       // fp16 d | fp16 dmin << 16
 };
 
-constexpr int BK = 64;
-constexpr int kStageElems = BN * BK;                 // one B stage: 32 KB
-constexpr int kSegs = BN * BK * 2 / 1024 / kWaves;   // 1 KB B segments per wave per stage: 8
-
-// ---- B: global -> LDS by LDS-DMA.  One instruction fills a 1 KB segment (8
-// tile rows); lane L lands at byte 16 L, i.e. row L / 8 of the segment,
-// physical chunk L % 8, and fetches the logical chunk the swizzle keeps
-// there.  For segment s the swizzle key of that row is (L / 8) ^ (s & 1).
-// Rows past N read as zeros (the resource starts at the tile's first row, and
-// the row is part of the VGPR offset, the range-checked part; the SGPR offset
-// only carries the K position).
-struct BSegs {
-  uint32_t voff_even, voff_odd, seg_stride;
-};
-__device__ __forceinline__ BSegs b_segs(int lane, int K) {
-  const int seg_row = lane >> 3;
-  return {uint32_t(seg_row * K + ((lane & 7) ^ seg_row) * 8) * 2,
-          uint32_t(seg_row * K + ((lane & 7) ^ seg_row ^ 1) * 8) * 2, uint32_t(8 * K) * 2};
-}
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t b_rsrc(const uint16_t *B, int N, int K, int tn) {
-  const int n0 = tn * BN;
-  return make_rsrc(B + int64_t(n0) * K, int64_t(N - n0) * K * 2);
-}
-// B slice `slice` (K positions 64 slice ..) of the tile into LDS stage sb.
-__device__ __forceinline__ void dma_b_slice(__amdgpu_buffer_rsrc_t rb, uint16_t *sb,
-                                            const BSegs &g, int wave, int slice) {
-#pragma unroll
-  for (int i = 0; i < kSegs; ++i) {
-    const int seg = wave * kSegs + i;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, sb + seg * 512, 16,
-                                             ((i & 1) ? g.voff_odd : g.voff_even) +
-                                                 seg * g.seg_stride,
-                                             slice * BK * 2, 0, 0);
-  }
-}
-// The 8 B fragments of k-step ks of an LDS stage (block j: columns 32 j ..).
-__device__ __forceinline__ void load_b_frags(const uint16_t *sb, int frow, int fhalf, int ks,
-                                             bf16x8 (&fb)[kNJ]) {
-  const int chunk = 2 * ks + fhalf;
-#pragma unroll
-  for (int j = 0; j < kNJ; ++j)
-    fb[j] = *reinterpret_cast<const bf16x8 *>(sb + swz<BK>(j * 32 + frow, chunk));
-}
 // A lane's parts of the block at byte offset `off` of the table.
 __device__ __forceinline__ void load_part(__amdgpu_buffer_rsrc_t rt, uint32_t off, int fhalf,
                                           Q2kPart &p) {
@@ -130,16 +86,9 @@ __device__ __forceinline__ bf16x8 decode_frag(const Q2kPart &b, const int qs, co
   const Q2kPlanes pl = kExact ? q2k_group_planes_exact(b.dd, sm) : q2k_group_planes(b.dd, sm);
   return __builtin_bit_cast(bf16x8, q2k_expand8(pl, b.q[p][0], b.q[p][1], shift));
 }
-// One k-step: 16 MFMAs (32 cycles of matrix core each), the next step's 8 B
-// fragment reads and its A decode (about 56 VALU ops) spread between them.
-__device__ __forceinline__ void sched_step() {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    if (r % 2 == 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
-  }
-}
+// One k-step: 16 MFMAs, the next step's 8 B fragment reads and its A decode
+// (about 56 VALU ops) spread between them.
+__device__ __forceinline__ void sched_step() { sched_step_valu<4>(); }
 
 // One 256 x 256 output tile (tm, tn) per call; kExact picks the group decode.
 template <bool kExact>

@@ -30,15 +30,6 @@ __device__ __forceinline__ float half_to_float(uint32_t h16) {
   return float(__builtin_bit_cast(_Float16, uint16_t(h16)));
 }
 
-// OCP FP8 E4M3 (fn) code -> fp32, from the format's fields.
-__device__ __forceinline__ float e4m3fn_to_float(uint32_t b) {
-  const uint32_t sign = (b & 0x80u) << 24;
-  const uint32_t e = (b >> 3) & 0xFu, m = b & 0x7u;
-  if (e == 0) return __uint_as_float(sign | __float_as_uint(float(m) * 0x1p-9f));
-  if (e == 15 && m == 7) return __uint_as_float(0x7FC00000u | sign);
-  return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
-}
-
 __device__ __forceinline__ void count_bad(int32_t *bad_ids, bool bad, int lane32) {
   if (bad && bad_ids && lane32 == 0) atomicAdd(bad_ids, 1);
 }

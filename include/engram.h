@@ -255,6 +255,36 @@ ENGRAM_API engram_status engram_project_q2k(const uint8_t *table, int64_t num_ro
                                  const uint16_t *wkv, uint16_t *kv, int32_t T, int32_t N,
                                  int32_t *bad_ids, hipStream_t stream);
 
+/* Stages 2 + 3 fused for FP8 tables with the bf16 weight ([vLLM]
+ * _engram_lookup_kernel, bf16 mode, then [spark] overview stage 3): kv =
+ * bf16(dequant(table[ids])) x wkv^T without writing the bf16 rows to memory.
+ * The projection reads each row's 256 codes and 8 scale bytes and converts
+ * them on chip to the values engram_rows gives (e4m3fn code x 2^(byte -
+ * 127), rounded to bf16; NaN codes and scale bytes 0 and 255 included), and
+ * sums the same products in the same fp32 order as engram_project, so kv is
+ * bit for bit what engram_rows followed by engram_project gives.  It runs
+ * 256 x 256 output tiles whatever T is and needs no rows buffer (T * cols *
+ * 512 bytes for engram_rows); it is about 4 % slower than engram_rows
+ * followed by engram_project (measured at 16384 tokens: the fused kernel
+ * gathers 128-byte pieces of random table rows for every column of tiles),
+ * so engram_forward runs rows -> projection for FP8 layers.
+ *   table DEVICE [num_rows][256] e4m3fn codes, 16-byte aligned; scales DEVICE
+ *   [num_rows][8] e8m0, 4-byte aligned; ids, ids_token_stride, cols, bad_ids
+ *   as for engram_rows (K = cols * 256; an id outside the table gives a zero
+ *   row); wkv DEVICE bf16 [N][K]; kv DEVICE bf16 [T][N], 16-byte aligned,
+ *   fully overwritten.
+ *   Limit: T * ids_token_stride * 4 <= ENGRAM_FP8_FUSED_MAX_ID_BYTES (the ids
+ *   are read through a 32-bit-offset buffer descriptor), else
+ *   ENGRAM_ERR_UNSUPPORTED.  The table has no size limit (its rows are read
+ *   through 64-bit addresses).
+ */
+#define ENGRAM_FP8_FUSED_MAX_ID_BYTES 2147483632LL
+ENGRAM_API engram_status engram_project_fp8(const uint8_t *table, const uint8_t *scales,
+                                            int64_t num_rows, const int32_t *ids,
+                                            int64_t ids_token_stride, int32_t cols,
+                                            const uint16_t *wkv, uint16_t *kv, int32_t T,
+                                            int32_t N, int32_t *bad_ids, hipStream_t stream);
+
 /* MXFP8 copy of a bf16 weight, for engram_project_mxfp8 ([vLLM] EngramBatch:
  * the WKV GEMM there takes MXFP8 operands, in the OCP MX v1.0 format).
  *   w DEVICE bf16 [N][K], K % 32 == 0; codes DEVICE [N][K] e4m3fn, 16-byte

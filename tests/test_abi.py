@@ -55,7 +55,7 @@ def declared_functions():
 def test_header_declares_the_five_calls_and_helpers():
     names = declared_functions()
     for want in ("engram_hash", "engram_history_update", "engram_rows", "engram_project", "engram_project_q2k",
-                 "engram_quantize_mxfp8", "engram_project_mxfp8", "engram_gate",
+                 "engram_project_fp8", "engram_quantize_mxfp8", "engram_project_mxfp8", "engram_gate",
                  "engram_gate_layers", "engram_forward", "engram_workspace_bytes", "engram_last_error"):
         assert want in names
 
@@ -130,6 +130,10 @@ def _raw(eg):
                                        ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_void_p, ctypes.c_void_p]
+    lib.engram_project_fp8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     lib.engram_gate_layers.argtypes = ([ctypes.c_void_p] * 4 + [ctypes.c_int32, ctypes.c_void_p] +
                                        [ctypes.c_int32] * 3 + [ctypes.c_float] * 3 +
                                        [ctypes.c_void_p])
@@ -312,6 +316,27 @@ class TestValidation:
         # a table of 2^32 bytes and more is fine (64-bit row addresses)
         assert call(nrows=2**25, T=0, table=None, ids=None, wc=None, ws=None,
                     kv=None) == eg.ENGRAM_OK
+
+    def test_project_fp8_rejects(self, eg):
+        lib = _raw(eg)
+        ok = dict(table=FAKE, scales=FAKE, nrows=100, ids=FAKE, stride=24, cols=24, wkv=FAKE,
+                  kv=FAKE, T=300, N=512, bad=None)
+
+        def call(**kw):
+            a = dict(ok, **kw)
+            return lib.engram_project_fp8(a["table"], a["scales"], a["nrows"], a["ids"],
+                                          a["stride"], a["cols"], a["wkv"], a["kv"], a["T"],
+                                          a["N"], a["bad"], None)
+        for kw in (dict(nrows=0), dict(cols=0), dict(stride=23), dict(T=-1), dict(N=0),
+                   dict(table=None), dict(table=FAKE + 4), dict(scales=None),
+                   dict(scales=FAKE + 2), dict(ids=None), dict(ids=FAKE + 1), dict(wkv=None),
+                   dict(wkv=FAKE + 8), dict(kv=None), dict(kv=FAKE + 8), dict(bad=FAKE + 2)):
+            assert call(**kw) == eg.ENGRAM_ERR_ARG, kw
+        # the ids are read through a 32-bit-offset buffer descriptor
+        assert call(T=2147483632 // (24 * 4) + 1) == eg.ENGRAM_ERR_UNSUPPORTED
+        assert "exceeds" in lib.engram_last_error().decode()
+        # a table of 2^32 bytes and more is fine (64-bit row addresses)
+        assert call(nrows=2**25, T=0, table=None, ids=None, wkv=None, kv=None) == eg.ENGRAM_OK
 
     def test_forward_mx_layer_rejects(self, eg):
         lib = _raw(eg)

@@ -728,6 +728,105 @@ def test_binding_rejects_short_buffers(eg):
         eg.engram_hash(params, tokens, short)
 
 
+# --------------------------------- FP8 rows fused into the bf16 projection
+
+@pytest.mark.parametrize("c", [c for c in CONFIGS if workloads.SPECS[c].fmt == "fp8"])
+def test_project_fp8_bit_identical_to_rows_then_project(eg, c):
+    # The fused FP8 projection converts each code to the rows kernel's bf16
+    # value and sums in engram_project's order: kv equal bit for bit on the
+    # whole output at the full size, and the oracle's projection bar.
+    wl = host(c)
+    s = wl.spec
+    for layer in range(len(s.layer_ids)):
+        ids, rows = gpu_rows(eg, c, layer, eg.ENGRAM_ROWS_FP8_E4M3_E8M0)
+        L = dev(c).layers[layer]
+        kv_two = torch.empty((s.T, s.N), dtype=torch.int16, device="cuda")
+        eg.engram_project(rows, L.wkv, kv_two, s.T, s.K, s.N)
+        g = Guarded((s.T, s.N), torch.int16, 0x7777)
+        bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+        eg.engram_project_fp8(L.table, L.scales, L.table.numel() // 256,
+                              ids.view(-1)[layer * s.cols:], len(s.layer_ids) * s.cols, s.cols,
+                              L.wkv, g.t, s.T, s.N, bad)
+        g.check()
+        assert bad.item() == 0
+        diff = int((g.t != kv_two).sum().item())
+        assert diff == 0, f"layer {layer}: {diff} kv values differ"
+        check_kv_full(c, layer, g.t.cpu().numpy().view(np.uint16))
+
+
+@pytest.mark.parametrize("T,cols,N,stride", [(1, 1, 64, 1), (37, 3, 256, 3), (255, 5, 520, 5),
+                                             (300, 24, 4096, 48), (513, 2, 1000, 2),
+                                             (129, 8, 256, 16), (1800, 4, 8200, 4),
+                                             (1500, 2, 16390, 6)])
+def test_project_fp8_ragged_and_bad_ids(eg, T, cols, N, stride):
+    # Ragged tiles in M and N (N % 8 != 0 included), one column and many,
+    # more tiles than compute units (persistent workgroups with several
+    # tiles), ids read with a stride, and ids outside the table: zero rows,
+    # counted once per (token, column) -- exactly as engram_rows does.
+    rng = np.random.default_rng(13 * T + cols)
+    R = 777
+    table_np, scales_np = workloads.fp8_table(4, 0, R)
+    ids_full = rng.integers(0, R, (T, stride)).astype(np.int32)
+    bad_mask = rng.random((T, stride)) < 0.05
+    ids_full[bad_mask] = rng.choice([-1, R, R + 5, 2**31 - 1, -(2**31)], int(bad_mask.sum()))
+    off = stride - cols
+    ids_np = ids_full[:, off:]
+    K = cols * 256
+    wkv_np = oracle.bf16_bits(oracle.bf16_round(0.05 * rng.standard_normal((N, K))))
+    table, tscales, wkv = tensor(table_np, "cuda"), tensor(scales_np, "cuda"), tensor(wkv_np, "cuda")
+    ids = tensor(ids_full, "cuda")
+    g = Guarded((T, N), torch.int16, 0x7777)
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    eg.engram_project_fp8(table, tscales, R, ids.view(-1)[off:], stride, cols, wkv, g.t, T, N,
+                          bad)
+    g.check()
+    assert bad.item() == int(bad_mask[:, off:].sum())
+    rows = torch.empty((T, K), dtype=torch.int16, device="cuda")
+    eg.engram_rows(eg.ENGRAM_ROWS_FP8_E4M3_E8M0, table, tscales, R, ids.view(-1)[off:], stride,
+                   cols, T, rows)
+    kv_two = torch.empty((T, N), dtype=torch.int16, device="cuda")
+    eg.engram_project(rows, wkv, kv_two, T, K, N)
+    if T > SKINNY_MAX_TOKENS:             # engram_project's tiles: the same order
+        assert torch.equal(g.t, kv_two)
+    _check_kv(g.t.cpu().numpy().view(np.uint16), oracle.rows_fp8(table_np, scales_np, ids_np),
+              wkv_np)
+
+
+def test_project_fp8_nan_codes_and_edge_scale_bytes(eg):
+    # Codes 0x7F / 0xFF (NaN) and scale bytes 0 and 255 (0 and inf in the
+    # binary32 exponent field): the fused kernel's exact conversion must give
+    # the rows kernel's values, so kv equals rows -> projection bit for bit
+    # (NaN and inf outputs included), and the rows equal the oracle's.
+    T, cols, N, R = 300, 4, 512, 500
+    rng = np.random.default_rng(5)
+    table_np, scales_np = workloads.fp8_table(4, 1, R)
+    table_np = table_np.copy()
+    scales_np = scales_np.copy()
+    table_np[rng.choice(R, 20, replace=False), rng.integers(0, 256, 20)] = 0x7F
+    table_np[rng.choice(R, 20, replace=False), rng.integers(0, 256, 20)] = 0xFF
+    scales_np[rng.choice(R, 30, replace=False), rng.integers(0, 8, 30)] = 0
+    scales_np[rng.choice(R, 10, replace=False), rng.integers(0, 8, 10)] = 255
+    ids_np = rng.integers(0, R, (T, cols)).astype(np.int32)
+    K = cols * 256
+    wkv_np = oracle.bf16_bits(oracle.bf16_round(0.05 * rng.standard_normal((N, K))))
+    table, tscales, wkv = tensor(table_np, "cuda"), tensor(scales_np, "cuda"), tensor(wkv_np, "cuda")
+    ids = tensor(ids_np, "cuda")
+    rows = torch.empty((T, K), dtype=torch.int16, device="cuda")
+    eg.engram_rows(eg.ENGRAM_ROWS_FP8_E4M3_E8M0, table, tscales, R, ids, cols, cols, T, rows)
+    want = oracle.rows_fp8(table_np, scales_np, ids_np)
+    got_rows = rows.cpu().numpy().view(np.uint16)
+    nan_g, nan_w = (got_rows & 0x7FFF) > 0x7F80, (want & 0x7FFF) > 0x7F80
+    assert nan_w.any() and np.array_equal(nan_g, nan_w)       # the oracle's NaN carries no sign
+    assert np.array_equal(got_rows[~nan_g], want[~nan_w])
+    kv_two = torch.empty((T, N), dtype=torch.int16, device="cuda")
+    eg.engram_project(rows, wkv, kv_two, T, K, N)
+    kv = torch.full((T, N), 0x7777, dtype=torch.int16, device="cuda")
+    eg.engram_project_fp8(table, tscales, R, ids, cols, cols, wkv, kv, T, N)
+    assert torch.equal(kv, kv_two)
+    got = kv.cpu().numpy().view(np.uint16)
+    assert ((got & 0x7F80) == 0x7F80).any()          # the crafted rows do reach the output
+
+
 # ------------------------------------------------ MXFP8 projection (FP8 tables)
 
 FP8_CONFIGS = [c for c in CONFIGS if workloads.SPECS[c].fmt == "fp8"]
