@@ -372,7 +372,9 @@ def main() -> int:
         return profiled_traffic(name + suffix) if suffix else None
 
     if mx:
-        dom_name, dom_kernel = "rows_project", "gemm_mx_kernel (engram_project_mxfp8)"
+        dom_name, dom_kernel = "rows_project", (
+            "gemm_mx_persistent_kernel" if s.cols >= 2 else "gemm_mx_kernel") + \
+            " (engram_project_mxfp8)"
         dom_prof = "gemm_mx"
     elif fused:
         dom_name, dom_kernel = "rows_project", (
@@ -380,7 +382,9 @@ def main() -> int:
             " + gemm_q2k_exact_kernel (engram_project_q2k)"
         dom_prof = "gemm_q2k"
     else:
-        dom_name, dom_kernel = "project", "gemm_nt_kernel (engram_project)"
+        dom_name, dom_kernel = "project", (
+            "gemm_nt_persistent_kernel" if s.K % 128 == 0 else "gemm_nt_kernel") + \
+            " (engram_project)"
         dom_prof = "gemm_nt"
     dom_tf = tflops(per_launch_ms[dom_name])
     dom_peak = FP8_PEAK_TFLOPS if mx else BF16_PEAK_TFLOPS
