@@ -929,14 +929,17 @@ def test_quantize_mxfp8_workload_weight_sampled(eg, c):
                                              (257, 6, 256, 12), (300, 24, 4096, 24),
                                              (513, 2, 1000, 2), (600, 24, 700, 48),
                                              (1, 4, 64, 4), (64, 4, 20480, 8), (37, 8, 300, 8),
-                                             (100, 24, 2048, 48), (128, 12, 1000, 12)])
+                                             (100, 24, 2048, 48), (128, 12, 1000, 12),
+                                             (300, 1, 520, 1), (1500, 2, 16390, 2)])
 def test_project_mxfp8_ragged_and_bad_ids(eg, T, cols, N, stride):
     # Ragged tiles in M and N, few and many columns, ids read with a stride
     # (as for one layer of several), and ids outside the table (zero rows,
     # counted once per (token, column)).  Up to 64 tokens with cols % 4 == 0
     # the weight-streaming form runs (one or several columns per K quarter,
     # the widest column tiles at N = 20480, a ragged token tile); 100 and 128
-    # tokens with cols % 4 == 0 stay on the 256 x 256 tiles.
+    # tokens with cols % 4 == 0 stay on the 256 x 256 tiles: one tile per
+    # workgroup for a single column, the persistent form otherwise (with
+    # several tiles per workgroup and N % 8 != 0 in the last shape).
     rng = np.random.default_rng(11 * T + cols)
     R = 777
     table_np, scales_np = workloads.fp8_table(4, 0, R)
