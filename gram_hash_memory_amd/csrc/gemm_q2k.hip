@@ -8,16 +8,18 @@
 // engram_rows produces, and every output sums the same MFMAs in the same K
 // order as gemm.hip, so kv is bit-identical to rows -> project.
 //
-// Tile 256 x 256, 4 waves, each wave 64 rows x 256 columns (2 x 8 blocks of
-// v_mfma_f32_32x32x16_bf16, accumulators in AGPRs), K in stages of BK = 64.
+// Tile 256 x 256, each wave a band of tile rows x all 256 columns (blocks of
+// v_mfma_f32_32x32x16_bf16), K in stages of BK = 64.
 //  - B goes straight from global memory into its LDS stage (buffer_load ...
 //    lds); every wave reads the whole B stage as fragments.
-//  - A never touches LDS.  A wave owns 64 tile rows, so each row is needed by
-//    exactly one wave, and every lane decodes its own A fragments from the
-//    Q2_K block in registers: lane (r, h) of the 32 x 16 fragment holds row r,
-//    values 8h .. 8h + 7 of the 16-value k-step.  Decoding into LDS instead
-//    would add a 32 KB LDS write per stage next to the fragment reads, and LDS
-//    traffic is what bounds this kernel.
+//  - A never touches LDS.  Each tile row is needed by exactly one wave, and
+//    every lane decodes its own A fragments from the Q2_K block in
+//    registers: lane (r, h) of the 32 x 16 fragment holds row r, values
+//    8h .. 8h + 7 of the 16-value k-step.  Decoding into LDS instead would
+//    add a 32 KB LDS write per stage next to the fragment reads.
+//  - The persistent form runs 8 waves of 32 rows (two waves per SIMD, 128
+//    accumulators each); the one-tile form 4 waves of 64 rows (256
+//    accumulators in AGPRs).
 // Per lane and table column (256 values = 4 stages) a row needs the block's
 // 16 scale/min bytes, d/dmin, and 32 of its 64 quant bytes: value v's quant
 // is byte 32 (v / 128) + v % 32 at bit 2 ((v % 128) / 32), and the lane's
@@ -25,8 +27,8 @@
 // bytes 16 p + 8 h, p = 0..3.  The blocks of a column are loaded one column
 // ahead.
 // Two forms of the same K loop:
-//  - gemm_q2k_persistent_kernel (even column counts): one workgroup per CU
-//    walks its share of the tiles.  The next tile's ids, its first blocks and
+//  - gemm_q2k_persistent_kernel (even column counts): one workgroup of 8
+//    waves per CU walks its share of the tiles.  The next tile's ids, its first blocks and
 //    its first two B slices are fetched during the current tile's last
 //    column, so the K loop runs on from tile to tile; each B slice is
 //    requested in the k-step after the barrier that frees its stage, a whole
@@ -255,13 +257,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
   q2k_tile<false>(table, num_rows, ids, ids_stride, B, C, M, N, K, tm, tn, smem);
 }
 
-// The persistent form (cols even).  Workgroup b runs the tiles whose ids in
-// the XCD-aware order (tile_coords) are b, b + G, b + 2 G, ... (G = grid
-// size, a multiple of 8 when a workgroup has more than one tile, so all of
-// them lie in its XCD's run).  LDS: the two B stages (64 KB), the current
-// tile's ids (cols x 256 int32: each wave's 64 rows are written and read only
-// by that wave), and a 9 KB staging area per wave.
-__global__ __launch_bounds__(kThreads, 1) void gemm_q2k_persistent_kernel(
+// The persistent form (cols even): one workgroup of 8 waves (two per SIMD)
+// per CU.  Workgroup b runs the tiles whose ids in the XCD-aware order
+// (tile_coords) are b, b + G, b + 2 G, ... (G = grid size, a multiple of 8
+// when a workgroup has more than one tile, so all of them lie in its XCD's
+// run).  Wave w owns tile rows 32 w .. 32 w + 31 and all 256 columns: it
+// decodes one A fragment per k-step (the same VALU work per MFMA as the
+// 4-wave form) and reads all 8 B fragments, and while one wave of a SIMD
+// waits on its reads, its DMA issue or the barrier, the other's MFMAs go on.
+// LDS: the two B stages (64 KB), the current tile's ids (cols x 256 int32,
+// brought in by waves 0-3 and read by every wave after the next barrier), and
+// a 4.5 KB staging area per wave.
+constexpr int kPersThreads = 512;
+constexpr int kPersWaves = kPersThreads / 64;
+constexpr int kPersSegs = kStageElems * 2 / 1024 / kPersWaves;   // B segments per wave: 4
+
+__global__ __launch_bounds__(kPersThreads, 1) void gemm_q2k_persistent_kernel(
     const uint8_t *__restrict__ table, int64_t num_rows, const int32_t *__restrict__ ids,
     int64_t ids_stride, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
     int M, int N, int K, int tiles_m, int tiles_n) {
@@ -277,49 +288,55 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_persistent_kernel(
   if (lid >= tiles) return;
 
   int32_t *const ids_lds = reinterpret_cast<int32_t *>(smem + 2 * kStageElems);
-  uint16_t *const stg = smem + 2 * kStageElems + cols * kThreads * 2 + wave * 64 * kStgStride;
+  uint16_t *const stg = smem + 2 * kStageElems + cols * BM * 2 + wave * 32 * kStgStride;
+  // B slice `slice` into stage `stage`: this wave's 4 segments of 1 KB (8
+  // rows each; segment 4 w + i, whose swizzle key parity is i & 1).
   const BSegs segs = b_segs(lane, K);
   auto dma_b = [&](__amdgpu_buffer_rsrc_t rb, int stage, int slice) {
-    dma_b_slice(rb, smem + stage * kStageElems, segs, wave, slice);
+    uint16_t *sb = smem + stage * kStageElems;
+#pragma unroll
+    for (int i = 0; i < kPersSegs; ++i) {
+      const int seg = wave * kPersSegs + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, sb + seg * 512, 16, ((i & 1) ? segs.voff_odd : segs.voff_even) + seg * segs.seg_stride,
+          slice * BK * 2, 0, 0);
+    }
   };
-  // The ids of tile row m0 + 64 wave + lane, all columns, into ids_lds (one
-  // LDS-DMA instruction per column; rows past M read 0 and are never stored).
+  // The ids of tile rows 64 w + lane, all columns, into ids_lds (waves 0-3,
+  // one LDS-DMA instruction per column; rows past M read 0 and are never
+  // stored).  The other waves see them after the issuing waves' next
+  // barrier with vmcnt 0.
   auto dma_ids = [&](int tm_) {
+    if (wave >= 4) return;
     const int m0_ = tm_ * BM;
     const __amdgpu_buffer_rsrc_t ri =
         make_rsrc(ids + int64_t(m0_) * ids_stride, int64_t(min(BM, M - m0_)) * ids_stride * 4);
     const uint32_t voff = uint32_t((wave * 64 + lane) * ids_stride) * 4;
     for (int c = 0; c < cols; ++c)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ri, ids_lds + c * kThreads + wave * 64, 4,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ri, ids_lds + c * BM + wave * 64, 4,
                                                voff + uint32_t(c) * 4, 0, 0, 0);
   };
 
   const __amdgpu_buffer_rsrc_t rt = make_rsrc(table, num_rows * ENGRAM_Q2K_ROW_BYTES);
-  Q2kPart blk[2][kRowsPerLane];
+  Q2kPart blk[2];
   // An id outside the table reads the bytes past it: zeros.
   auto load_block = [&](int set, int col) {
-#pragma unroll
-    for (int i = 0; i < kRowsPerLane; ++i) {
-      const int32_t id = ids_lds[col * kThreads + wave * 64 + 32 * i + frow];
-      const uint32_t off =
-          (id >= 0 && id < num_rows) ? uint32_t(id) * ENGRAM_Q2K_ROW_BYTES : kNoRow;
-      load_part(rt, off, fhalf, blk[set][i]);
-    }
+    const int32_t id = ids_lds[col * BM + wave * 32 + frow];
+    const uint32_t off =
+        (id >= 0 && id < num_rows) ? uint32_t(id) * ENGRAM_Q2K_ROW_BYTES : kNoRow;
+    load_part(rt, off, fhalf, blk[set]);
   };
 
-  bf16x8 fa[2][kRowsPerLane], fb[2][kNJ];
+  bf16x8 fa[2], fb[2][kNJ];
   auto decode_a = [&](int set, const int qs, const int ks, int slot) {
-#pragma unroll
-    for (int i = 0; i < kRowsPerLane; ++i) fa[slot][i] = decode_frag<false>(blk[set][i], qs, ks);
+    fa[slot] = decode_frag<false>(blk[set], qs, ks);
   };
 
-  // acc[i][j] holds the transposed 32 x 32 output block: accumulator r of
-  // lane (t, h) is tile row 32 i + t, column 32 j + 8 (r / 4) + 4 h + r % 4.
-  f32x16 acc[kRowsPerLane][kNJ];
+  // acc[0][j] holds the transposed 32 x 32 output block: accumulator r of
+  // lane (t, h) is tile row 32 w + t, column 32 j + 8 (r / 4) + 4 h + r % 4.
+  f32x16 acc[1][kNJ];
 #pragma unroll
-  for (int i = 0; i < kRowsPerLane; ++i)
-#pragma unroll
-    for (int j = 0; j < kNJ; ++j) acc[i][j] = f32x16{};
+  for (int j = 0; j < kNJ; ++j) acc[0][j] = f32x16{};
 
   auto load_b = [&](int stage, int ks, int slot) {
     load_b_frags(smem + stage * kStageElems, frow, fhalf, ks, fb[slot]);
@@ -327,22 +344,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_persistent_kernel(
   auto mfma_block = [&](int slot) {
 #pragma unroll
     for (int j = 0; j < kNJ; ++j)
+      acc[0][j] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][j], fa[slot], acc[0][j], 0, 0, 0);
+  };
+  // One k-step: 8 MFMAs, each followed by one of the next step's 8 B
+  // fragment reads and 4 VALU ops of its A decode (about 28).
+  auto sched_step = [&]() {
 #pragma unroll
-      for (int i = 0; i < kRowsPerLane; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][j], fa[slot][i],
-                                                            acc[i][j], 0, 0, 0);
+    for (int r = 0; r < kNJ; ++r) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+    }
   };
 
   // Iteration kt of the current tile multiplies stage kt % 2 (j = kt % 8
   // fixes the register sets at compile time, as in q2k_tile):
-  //  - at kt % 4 == 0 the blocks of column (kt / 4 + 1) % cols are requested
-  //    (12 loads); after a tile's last column that is column 0 of the next
+  //  - at kt % 4 == 0 the block of column (kt / 4 + 1) % cols is requested
+  //    (6 loads); after a tile's last column that is column 0 of the next
   //    tile, whose ids are in ids_lds by then;
   //  - the barrier waits for the B slice of this stage (requested one
-  //    iteration earlier) and lets only those 12 block loads stay in flight;
+  //    iteration earlier) and lets only those 6 block loads stay in flight;
   //  - after it, stage kt % 2, which no wave reads any more, gets the slice
   //    `fill_slice` of resource rb_fill (slice kt + 2, or one of the next
-  //    tile's first two slices), its DMA spread over the last k-step.
+  //    tile's first two slices), its 4 DMA instructions spread over the last
+  //    k-step.
   auto iteration = [&](int kt, const int j, __amdgpu_buffer_rsrc_t rb_fill, int fill_slice) {
     const int stage = j & 1;
     const int set = (j >> 2) & 1, qs = j & 3;
@@ -364,21 +390,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_persistent_kernel(
     decode_a(set, qs, 3, 1);
     mfma_block(0);
     sched_step();
-    if (qs == 0) stage_barrier<waitcnt(6 * kRowsPerLane, 0)>();
+    if (qs == 0) stage_barrier<waitcnt(6, 0)>();
     else stage_barrier<waitcnt(0, 0)>();
     __builtin_amdgcn_sched_barrier(0);
     load_b(stage ^ 1, 0, 0);
     decode_a(((j + 1) >> 2) & 1, (j + 1) & 3, 0, 0);
     dma_b(rb_fill, stage, fill_slice);
     mfma_block(1);
-    // The 8 DMA instructions go one after each of the first 8 MFMAs (issued
-    // together they hold up the matrix core while the address unit takes
-    // the requests of all four waves).
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < kNJ; ++r) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      if (r < kSegs) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-      if (r % 2 == 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      if (r < kPersSegs) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
     }
   };
@@ -389,7 +412,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_persistent_kernel(
   tile_coords(lid, tiles_m, tiles_n, tm, tn);
   __amdgpu_buffer_rsrc_t rb = b_rsrc(B, N, K, tn);
   dma_ids(tm);
-  __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
+  stage_barrier<waitcnt(0, 0)>();
   load_block(0, 0);
   dma_b(rb, 0, 0);
   stage_barrier<waitcnt(0, 0)>();
@@ -411,9 +434,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_persistent_kernel(
     for (int kt = 0; kt < nk; kt += 8) {
       const bool last = kt + 8 == nk;
       iteration(kt + 0, 0, rb, kt + 2);
-      // This tile's ids were last read just above (the blocks of column
-      // cols - 1); the next tile's replace them and land by the next
-      // barrier, whose vmcnt is 0.
+      // Every wave read this tile's ids for the last time before the barrier
+      // just passed (the blocks of column cols - 1); the next tile's replace
+      // them and are visible after the next barrier, whose vmcnt is 0.
       if (last && has_next) dma_ids(tm2);
       iteration(kt + 1, 1, rb, kt + 3);
       iteration(kt + 2, 2, rb, kt + 4);
@@ -424,13 +447,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_persistent_kernel(
       iteration(kt + 7, 7, last ? rb2 : rb, last ? (has_next ? 1 : nk - 1) : kt + 9);
     }
 
-    // Epilogue, per wave: its 64 rows in 4 chunks of 64 columns.
-    store_wave_transposed<kRowsPerLane, kNJ, kRowsPerLane>(acc, stg, C, M, N, m0 + wave * 64, n0,
-                                                           lane);
+    // Epilogue, per wave: its 32 rows in 4 chunks of 64 columns.
+    store_wave_transposed<1, kNJ, 1>(acc, stg, C, M, N, m0 + wave * 32, n0, lane);
 #pragma unroll
-    for (int i = 0; i < kRowsPerLane; ++i)
-#pragma unroll
-      for (int j = 0; j < kNJ; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < kNJ; ++j) acc[0][j] = f32x16{};
     if (!has_next) break;
     lid = next;
     tm = tm2;
@@ -512,10 +532,10 @@ hipError_t launch_project_q2k(const uint8_t *table, int64_t num_rows, const int3
                          size_t(cols) * kThreads * sizeof(uint32_t);
   const size_t lds_epilogue = size_t(BM) * BN * sizeof(uint16_t);
   const size_t lds = lds_loop > lds_epilogue ? lds_loop : lds_epilogue;
-  // Persistent kernel: the two B stages, the ids and 4 staging areas.
+  // Persistent kernel: the two B stages, the ids and 8 staging areas.
   const size_t lds_pers = size_t(2) * kStageElems * sizeof(uint16_t) +
-                          size_t(cols) * kThreads * sizeof(int32_t) +
-                          size_t(kWaves) * 64 * kStgStride * sizeof(uint16_t);
+                          size_t(cols) * BM * sizeof(int32_t) +
+                          size_t(kPersWaves) * 32 * kStgStride * sizeof(uint16_t);
   const bool persistent = cols % 2 == 0;
   const void *tile_fn = persistent ? reinterpret_cast<const void *>(&gemm_q2k_persistent_kernel)
                                    : reinterpret_cast<const void *>(&gemm_q2k_kernel);
@@ -528,7 +548,7 @@ hipError_t launch_project_q2k(const uint8_t *table, int64_t num_rows, const int3
   const int tiles = tiles_m * tiles_n;
   if (persistent) {
     hipLaunchKernelGGL(gemm_q2k_persistent_kernel, dim3(persistent_grid(tiles, stream)),
-                       dim3(kThreads), lds_pers, stream, table, num_rows, ids, ids_token_stride, w,
+                       dim3(kPersThreads), lds_pers, stream, table, num_rows, ids, ids_token_stride, w,
                        c, M, N, K, tiles_m, tiles_n);
   } else {
     hipLaunchKernelGGL(gemm_q2k_kernel, dim3(tiles), dim3(kThreads), lds, stream, table,
