@@ -91,8 +91,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 // (row-major, 512 B per row) so that global memory sees 16-byte stores of
 // whole row segments instead of 2-byte stores scattered over rows.  `smem`
 // needs 128 KB that no wave reads any more; the caller's barrier before this
-// call guarantees that.
-template <int NI, int NJ>
+// call guarantees that.  kNThreads: the workgroup's thread count; kCols: the
+// tile columns stored (those of the blocks, col0 = 0).
+template <int NI, int NJ, int kNThreads = kThreads, int kCols = BN>
 __device__ __forceinline__ void store_tile_blocks(const f32x16 (&acc)[NI][NJ], uint16_t *smem,
                                                   uint16_t *__restrict__ C, int M, int N,
                                                   int m0, int n0, int row0, int col0, int lane,
@@ -109,8 +110,8 @@ __device__ __forceinline__ void store_tile_blocks(const f32x16 (&acc)[NI][NJ], u
       }
   __syncthreads();
   const bool vec = (N % 8) == 0;
-  for (int idx = tid; idx < BM * BN / 8; idx += kThreads) {
-    const int row = idx / (BN / 8), c8 = (idx % (BN / 8)) * 8;
+  for (int idx = tid; idx < BM * kCols / 8; idx += kNThreads) {
+    const int row = idx / (kCols / 8), c8 = (idx % (kCols / 8)) * 8;
     const int grow = m0 + row, gcol = n0 + c8;
     if (grow >= M || gcol >= N) continue;
     uint16_t *dst = C + int64_t(grow) * N + gcol;

@@ -88,17 +88,33 @@ __device__ __forceinline__ bf16x8 decode_frag(const Q2kPart &b, const int qs, co
   const Q2kPlanes pl = kExact ? q2k_group_planes_exact(b.dd, sm) : q2k_group_planes(b.dd, sm);
   return __builtin_bit_cast(bf16x8, q2k_expand8(pl, b.q[p][0], b.q[p][1], shift));
 }
-// One k-step: 16 MFMAs, the next step's 8 B fragment reads and its A decode
-// (about 56 VALU ops) spread between them.
-__device__ __forceinline__ void sched_step() { sched_step_valu<4>(); }
 
-// One 256 x 256 output tile (tm, tn) per call; kExact picks the group decode.
-template <bool kExact>
+// One k-step of a wave with 2 x kJ blocks: 2 kJ MFMAs, the next step's kJ
+// B fragment reads and 4 VALU ops (the A decode) after each MFMA.
+template <int kJ>
+__device__ __forceinline__ void sched_step_cols() {
+#pragma unroll
+  for (int r = 0; r < 2 * kJ; ++r) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (r % 2 == 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+  }
+}
+
+// Columns 32 kJ part .. 32 kJ part + 32 kJ - 1 of the 256 x 256 output tile
+// (tm, tn), by 4 waves of 64 rows, each with 2 x kJ blocks of accumulators
+// (kJ = 8: the whole tile, 256 accumulators in AGPRs; kJ = 4: half of it,
+// which leaves the registers the exact decode needs).  kExact picks the
+// group decode.  Returns at once if the part lies past N.
+template <bool kExact, int kJ>
 __device__ __forceinline__ void q2k_tile(
     const uint8_t *__restrict__ table, int64_t num_rows, const int32_t *__restrict__ ids,
     int64_t ids_stride, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
-    int M, int N, int K, int tm, int tn, uint16_t *smem) {
-  const int m0 = tm * BM, n0 = tn * BN;
+    int M, int N, int K, int tm, int tn, int part, uint16_t *smem) {
+  constexpr int kR = kRowsPerLane;                 // 32-row blocks per wave
+  constexpr int kSegW = kJ * 4 / kWaves;           // B segments (8 rows) per wave per stage
+  const int m0 = tm * BM, n0 = tn * BN + part * 32 * kJ;
+  if (n0 >= N) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -106,10 +122,17 @@ __device__ __forceinline__ void q2k_tile(
   const int cols = K / ENGRAM_HEAD_DIM;
   const int nk = K / BK;
 
-  const __amdgpu_buffer_rsrc_t rb = b_rsrc(B, N, K, tn);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + int64_t(n0) * K, int64_t(N - n0) * K * 2);
   const BSegs segs = b_segs(lane, K);
   auto dma_b = [&](int stage, int slice) {
-    dma_b_slice(rb, smem + stage * kStageElems, segs, wave, min(slice, nk - 1));
+    uint16_t *sb = smem + stage * kStageElems;
+#pragma unroll
+    for (int i = 0; i < kSegW; ++i) {
+      const int seg = wave * kSegW + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, sb + seg * 512, 16, ((i & 1) ? segs.voff_odd : segs.voff_even) + seg * segs.seg_stride,
+          min(slice, nk - 1) * BK * 2, 0, 0);
+    }
   };
 
   // ---- A: byte offsets of every (row, column) block, in LDS behind the two
@@ -127,44 +150,47 @@ __device__ __forceinline__ void q2k_tile(
     for (int c = 0; c < ENGRAM_Q2K_FUSED_MAX_COLS; ++c) {
       if (c < cols) {
         const bool ok = idv[c] >= 0 && idv[c] < num_rows;
-        offs[c * kThreads + tid] =
-            row_ok && ok ? uint32_t(idv[c]) * ENGRAM_Q2K_ROW_BYTES : kNoRow;
+        offs[c * BM + tid] = row_ok && ok ? uint32_t(idv[c]) * ENGRAM_Q2K_ROW_BYTES : kNoRow;
       }
     }
   }
   __syncthreads();                                  // offsets of other lanes' rows
 
-  Q2kPart blk[2][kRowsPerLane];
+  Q2kPart blk[2][kR];
   auto load_block = [&](int set, int col) {
 #pragma unroll
-    for (int i = 0; i < kRowsPerLane; ++i)
-      load_part(rt, offs[min(col, cols - 1) * kThreads + wave * 64 + 32 * i + frow], fhalf,
+    for (int i = 0; i < kR; ++i)
+      load_part(rt, offs[min(col, cols - 1) * BM + wave * 32 * kR + 32 * i + frow], fhalf,
                 blk[set][i]);
   };
 
-  bf16x8 fa[2][kRowsPerLane], fb[2][kNJ];
+  bf16x8 fa[2][kR], fb[2][kJ];
   auto decode_a = [&](int set, const int qs, const int ks, int slot) {
 #pragma unroll
-    for (int i = 0; i < kRowsPerLane; ++i) fa[slot][i] = decode_frag<kExact>(blk[set][i], qs, ks);
+    for (int i = 0; i < kR; ++i) fa[slot][i] = decode_frag<kExact>(blk[set][i], qs, ks);
   };
 
-  f32x16 acc[kRowsPerLane][kNJ];
+  f32x16 acc[kR][kJ];
 #pragma unroll
-  for (int i = 0; i < kRowsPerLane; ++i)
+  for (int i = 0; i < kR; ++i)
 #pragma unroll
-    for (int j = 0; j < kNJ; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < kJ; ++j) acc[i][j] = f32x16{};
 
   auto load_b = [&](int stage, int ks, int slot) {
-    load_b_frags(smem + stage * kStageElems, frow, fhalf, ks, fb[slot]);
+    const uint16_t *sb = smem + stage * kStageElems;
+    const int chunk = 2 * ks + fhalf;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+      fb[slot][j] = *reinterpret_cast<const bf16x8 *>(sb + swz<BK>(j * 32 + frow, chunk));
   };
   // Column-block-major: B fragment j, read during the previous k-step in
   // order j, is first used 2 j MFMAs into this one, so every read gets the
   // same 16-MFMA lead (row-major order would give fragment 7 only 9).
   auto mfma_block = [&](int slot) {
 #pragma unroll
-    for (int j = 0; j < kNJ; ++j)
+    for (int j = 0; j < kJ; ++j)
 #pragma unroll
-      for (int i = 0; i < kRowsPerLane; ++i)
+      for (int i = 0; i < kR; ++i)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j],
                                                             acc[i][j], 0, 0, 0);
   };
@@ -199,21 +225,21 @@ __device__ __forceinline__ void q2k_tile(
     load_b(stage, 1, 1);
     decode_a(set, qs, 1, 1);
     mfma_block(0);
-    sched_step();
+    sched_step_cols<kJ>();
     load_b(stage, 2, 0);
     decode_a(set, qs, 2, 0);
     mfma_block(1);
-    sched_step();
+    sched_step_cols<kJ>();
     load_b(stage, 3, 1);
     decode_a(set, qs, 3, 1);
     mfma_block(0);
-    sched_step();
-    if (qs == 0 && prefetch) stage_barrier<waitcnt(6 * kRowsPerLane, 0)>();
+    sched_step_cols<kJ>();
+    if (qs == 0 && prefetch) stage_barrier<waitcnt(6 * kR, 0)>();
     else stage_barrier<waitcnt(0, 0)>();
     load_b(stage ^ 1, 0, 0);
     decode_a(((j + 1) >> 2) & 1, (j + 1) & 3, 0, 0);
     mfma_block(1);
-    sched_step();
+    sched_step_cols<kJ>();
   };
 
   // Prologue: stage 0 gets B slice 0, the lanes the blocks of column 0 and
@@ -244,7 +270,8 @@ __device__ __forceinline__ void q2k_tile(
   }
   __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
   __syncthreads();                                 // every wave is done with the stages
-  store_tile_blocks<kRowsPerLane, kNJ>(acc, smem, C, M, N, m0, n0, wave * 64, 0, lane, tid);
+  store_tile_blocks<kR, kJ, kThreads, 32 * kJ>(acc, smem, C, M, N, m0, n0, wave * 64, 0, lane,
+                                              tid);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
@@ -254,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_kernel(
   extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  q2k_tile<false>(table, num_rows, ids, ids_stride, B, C, M, N, K, tm, tn, smem);
+  q2k_tile<false, kNJ>(table, num_rows, ids, ids_stride, B, C, M, N, K, tm, tn, 0, smem);
 }
 
 // The persistent form (cols even): one workgroup of 8 waves (two per SIMD)
@@ -465,7 +492,9 @@ __global__ __launch_bounds__(kPersThreads, 1) void gemm_q2k_persistent_kernel(
 // ids outside the table, once per (token, column)); if any block lies
 // outside the one-fma range (q2k_fp32_exact), it recomputes tiles (tm, g),
 // (tm, g + split), ... with the exact group decode, overwriting what the
-// first launch stored.  Otherwise it exits after the check.
+// first launch stored, one half of the tile's columns at a time (the exact
+// decode needs more registers than the one-fma decode; 128 accumulators per
+// wave leave room for them).  Otherwise it exits after the check.
 __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_exact_kernel(
     const uint8_t *__restrict__ table, int64_t num_rows, const int32_t *__restrict__ ids,
     int64_t ids_stride, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
@@ -501,10 +530,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_exact_kernel(
 #pragma unroll
   for (int c = 0; c < ENGRAM_Q2K_FUSED_MAX_COLS; ++c) fast &= q2k_fp32_exact(ddv[c]);
   if (__syncthreads_and(fast)) return;
-  for (int tn = g; tn < tiles_n; tn += split) {
-    __syncthreads();                               // the previous tile is done with the LDS
-    q2k_tile<true>(table, num_rows, ids, ids_stride, B, C, M, N, K, tm, tn, smem);
-  }
+  for (int tn = g; tn < tiles_n; tn += split)
+    for (int part = 0; part < 2; ++part) {
+      __syncthreads();                             // the previous part is done with the LDS
+      q2k_tile<true, kNJ / 2>(table, num_rows, ids, ids_stride, B, C, M, N, K, tm, tn, part,
+                              smem);
+    }
 }
 
 }  // namespace
