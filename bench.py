@@ -13,9 +13,11 @@ the timed run itself.  For Q2_K tables that is engram_project_q2k (row gather
 and projection fused into one kernel); the two-kernel path it replaces
 (engram_rows, engram_project) is timed after the steps for comparison, as is
 engram_forward itself.  With --mxfp8 (FP8 tables only) the layers carry an
-MXFP8 copy of wkv, made once before timing, and the step runs
-engram_project_mxfp8 (raw FP8 rows on the block-scaled matrix cores) in place
-of rows -> projection.  With --overlap (several layers) the layers after the
+MXFP8 copy of wkv, made once before timing, and the step runs the MXFP8
+projection in place of rows -> projection, as engram_forward picks it:
+engram_stage_mxfp8 (the raw FP8 rows copied into an MXFP8 activation) then
+engram_project_mxfp8_staged (block-scaled matrix cores), or, for up to 64
+tokens, engram_project_mxfp8's weight-streaming form.  With --overlap (several layers) the layers after the
 first are projected on a second stream beside the first layer's projection
 and gate, each later gate waiting for its layer (a comparison schedule).
 
@@ -42,6 +44,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published (no sparsity)
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published (no sparsity)
 Q2K_FUSED_MAX_BYTES = 2147483504   # engram.h: ENGRAM_Q2K_FUSED_MAX_BYTES
+MX_MAX_BYTES = 2147483632          # engram.h: ENGRAM_MX_MAX_WEIGHT_BYTES
 SKINNY_MAX_TOKENS = 128            # engram_project streams wkv at or below this many tokens
 CPU_SAMPLE_TOKENS = 8192       # whole sequences of the workload, up to this many tokens
 CPU_MIN_SECONDS = 10.0         # the CPU baseline repeats its sample at least this long
@@ -91,6 +94,8 @@ def algorithmic(spec, token_mask) -> dict:
         "rows": T * per_tok_rows,                 # per layer
         "project": 2.0 * T * spec.K * spec.N,     # FLOP per layer
         "gate": live * per_live_gate + mask_bytes,  # per layer
+        # the MXFP8 staging: ids, then each row's 256 codes + 8 scale bytes read and written
+        "stage_mx": T * cols * (4 + 2 * (256 + 8)),
         "rows_per_token": per_tok_rows,
         "gate_per_token": per_live_gate,
     }
@@ -221,6 +226,14 @@ def main() -> int:
     fused = (fmt == eg.ENGRAM_ROWS_Q2K and s.cols <= 32 and
              (s.T > SKINNY_MAX_TOKENS or s.cols % 4 == 0) and
              all(n * 84 <= Q2K_FUSED_MAX_BYTES for n in num_rows))
+    # MXFP8 as engram_forward runs it: the weight-streaming form for up to 64
+    # tokens (cols % 4 == 0, cols <= 64), else the rows staged into an MXFP8
+    # activation and the 256 x 256 tiles on it.
+    mx_staged = mx and not (s.T <= 64 and s.cols % 4 == 0 and s.cols <= 64) and \
+        s.T * s.K <= MX_MAX_BYTES
+    if mx_staged:
+        a_codes = torch.empty((s.T, s.K), dtype=torch.uint8, device="cuda")
+        a_scales = torch.empty((s.T, s.K // 32), dtype=torch.uint8, device="cuda")
 
     def layer_ids(l):
         return ids.view(-1)[l * s.cols:]
@@ -241,7 +254,16 @@ def main() -> int:
     def mx_call(l):
         dl = dw.layers[l]
         eg.engram_project_mxfp8(dl.table, dl.scales, num_rows[l], layer_ids(l), L * s.cols,
-                                s.cols, wmx[l][0], wmx[l][1], kv, s.T, s.N, None, stream)
+                                s.cols, wmx[l][0], wmx[l][1], kvs[l], s.T, s.N, None, stream)
+
+    def stage_call(l):
+        dl = dw.layers[l]
+        eg.engram_stage_mxfp8(dl.table, dl.scales, num_rows[l], layer_ids(l), L * s.cols,
+                              s.cols, s.T, a_codes, a_scales, None, stream)
+
+    def mx_staged_call(l):
+        eg.engram_project_mxfp8_staged(a_codes, a_scales, s.cols, wmx[l][0], wmx[l][1], kvs[l],
+                                       s.T, s.N, stream)
 
     def gate_pass_call():
         eg.engram_gate_layers(h, kvs, [dl.q_weight for dl in dw.layers],
@@ -280,7 +302,10 @@ def main() -> int:
         for l in range(1, L):
             plan.append(("gate", lambda l=l: gate_after(l)))
     for l in range(L if not overlap else 0):
-        if mx:
+        if mx_staged:
+            plan += [("stage_mx", lambda l=l: stage_call(l)),
+                     ("project_mx", lambda l=l: mx_staged_call(l))]
+        elif mx:
             plan.append(("rows_project", lambda l=l: mx_call(l)))
         elif fused:
             plan.append(("rows_project", lambda l=l: fused_call(l)))
@@ -371,7 +396,11 @@ def main() -> int:
                   4: "_fp8_T16384.md"}.get(args.config)
         return profiled_traffic(name + suffix) if suffix else None
 
-    if mx:
+    if mx_staged:
+        dom_name = "project_mx"
+        dom_kernel = "gemm_mx_persistent_kernel<true> (engram_project_mxfp8_staged)"
+        dom_prof = "gemm_mx"
+    elif mx:
         dom_name, dom_kernel = "rows_project", (
             "gemm_mx_persistent_kernel" if s.cols >= 2 else "gemm_mx_kernel") + \
             " (engram_project_mxfp8)"
@@ -415,7 +444,17 @@ def main() -> int:
                  "hbm_gbs": round(gbs(alg["hash"], per_launch_ms["hash"]), 1),
                  "traffic": prof("hash")},
     }
-    if (fused or mx) and skinny:
+    if mx_staged:
+        stage_gbs = gbs(alg["stage_mx"], per_launch_ms["stage_mx"])
+        stages["stage_mx"] = {
+            "ms": round(per_launch_ms["stage_mx"], 4), "bound": "hbm",
+            "achieved_gbs": round(stage_gbs, 1), "frac": round(stage_gbs / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": alg["stage_mx"], "traffic": prof("stage_mx")}
+        stages["project_mx"] = {
+            "ms": round(per_launch_ms["project_mx"], 4), "bound": "mfma",
+            "achieved_tflops": round(dom_tf, 1), "frac": round(dom_tf / dom_peak, 4),
+            "traffic": prof(dom_prof)}
+    elif (fused or mx) and skinny:
         stages["rows_project"] = {
             "ms": round(per_launch_ms["rows_project"], 4), "bound": "hbm",
             "achieved_gbs": round(dom_gbs, 1), "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
@@ -450,7 +489,17 @@ def main() -> int:
           "frac": round(gg_gbs / HBM_PEAK_GBS, 4),
           "kernels": "engram_rows + engram_gate" +
                      (" (one gate pass for all layers)" if gate_pass else "")}
-    if fused or mx:
+    if mx_staged:
+        # The step's gather is the MXFP8 staging kernel, HBM-bound like the gate.
+        sg_ms = L * per_launch_ms["stage_mx"] + per_launch_ms["gate"] * (
+            1 if gate_pass or L == 1 else L)
+        sg_bytes = L * alg["stage_mx"] + (gate_bytes if gate_pass or L == 1 else L * alg["gate"])
+        stages["gather_plus_gate"] = {
+            "in_step": True, "ms": round(sg_ms, 4), "achieved_gbs": round(gbs(sg_bytes, sg_ms), 1),
+            "frac": round(gbs(sg_bytes, sg_ms) / HBM_PEAK_GBS, 4),
+            "kernels": "engram_stage_mxfp8 + engram_gate"}
+        stages["gather_plus_gate_standalone"] = dict(gg, in_step=False)
+    elif fused or mx:
         # The step gathers inside the fused projection (MFMA-bound, timed
         # above as rows_project); its only HBM-bound kernel is the gate.
         stages["gather_plus_gate"] = {

@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     FP8_SCALE_BYTES, EXPORTS, LIB_PATH, EngramError, HashParams, Tokens, Layer,
     engram_hash, engram_history_update, engram_rows, engram_project, engram_project_q2k,
     engram_project_fp8, engram_quantize_mxfp8,
-    engram_project_mxfp8, engram_gate, engram_gate_layers, engram_workspace_bytes, engram_forward, engram_last_error,
+    engram_project_mxfp8, engram_stage_mxfp8, engram_project_mxfp8_staged, engram_gate,
+    engram_gate_layers, engram_workspace_bytes, engram_forward, engram_last_error,
     engram_build_id, BUILD_ID, engram_forward_noalloc, FORWARD_NOALLOC_MAX_BYTES,
 )

@@ -29,7 +29,8 @@ ENGRAM_ROWS_Q2K, ENGRAM_ROWS_FP8_E4M3_E8M0 = 0, 1
 HEAD_DIM, Q2K_ROW_BYTES, FP8_ROW_BYTES, FP8_SCALE_BYTES = 256, 84, 256, 8
 
 EXPORTS = ("engram_hash", "engram_history_update", "engram_rows", "engram_project", "engram_project_q2k",
-           "engram_project_fp8", "engram_quantize_mxfp8", "engram_project_mxfp8", "engram_gate",
+           "engram_project_fp8", "engram_quantize_mxfp8", "engram_project_mxfp8",
+           "engram_stage_mxfp8", "engram_project_mxfp8_staged", "engram_gate",
            "engram_gate_layers", "engram_workspace_bytes", "engram_forward", "engram_last_error",
            "engram_build_id", "engram_forward_noalloc")
 
@@ -91,6 +92,10 @@ _lib.engram_quantize_mxfp8.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_v
 _lib.engram_project_mxfp8.argtypes = [c_void_p, c_void_p, c_int64, c_void_p, c_int64, c_int32,
                                       c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
                                       c_void_p]
+_lib.engram_stage_mxfp8.argtypes = [c_void_p, c_void_p, c_int64, c_void_p, c_int64, c_int32,
+                                    c_int32, c_void_p, c_void_p, c_void_p, c_void_p]
+_lib.engram_project_mxfp8_staged.argtypes = [c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+                                             c_void_p, c_int32, c_int32, c_void_p]
 _lib.engram_gate.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                              c_int32, c_int32, c_float, c_float, c_float, c_void_p]
 _lib.engram_gate_layers.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
@@ -106,8 +111,9 @@ _lib.engram_forward_noalloc.argtypes = [_P(_HashParams), _P(_Tokens), _P(_Layer)
                                         c_void_p]
 _lib.engram_last_error.restype = c_char_p
 for _name in ("engram_hash", "engram_history_update", "engram_rows", "engram_project", "engram_project_q2k",
-              "engram_quantize_mxfp8", "engram_project_mxfp8", "engram_gate", "engram_gate_layers",
-              "engram_forward", "engram_forward_noalloc"):
+              "engram_project_fp8", "engram_quantize_mxfp8", "engram_project_mxfp8",
+              "engram_stage_mxfp8", "engram_project_mxfp8_staged", "engram_gate",
+              "engram_gate_layers", "engram_forward", "engram_forward_noalloc"):
     getattr(_lib, _name).restype = c_int
 
 
@@ -285,6 +291,31 @@ def engram_project_mxfp8(table, scales, num_rows: int, ids, ids_token_stride: in
         _dptr(wkv_scales, torch.uint8, N * (K // 32), "wkv_scales"),
         _dptr(kv, torch.int16, T * N, "kv"), int(T), int(N),
         _dptr(bad_ids, torch.int32, 1, "bad_ids"), _stream(stream)))
+
+
+def engram_stage_mxfp8(table, scales, num_rows: int, ids, ids_token_stride: int, cols: int,
+                       T: int, a_codes, a_scales, bad_ids=None, stream=None) -> None:
+    """The MXFP8 activation of FP8 rows: codes [T, cols*256] and scales [T, cols*8]."""
+    need_ids = 0 if T <= 0 else (T - 1) * ids_token_stride + cols
+    _check(_lib.engram_stage_mxfp8(
+        _dptr(table, torch.uint8, num_rows * FP8_ROW_BYTES, "table"),
+        _dptr(scales, torch.uint8, num_rows * FP8_SCALE_BYTES, "scales"), int(num_rows),
+        _dptr(ids, torch.int32, need_ids, "ids"), int(ids_token_stride), int(cols), int(T),
+        _dptr(a_codes, torch.uint8, T * cols * HEAD_DIM, "a_codes"),
+        _dptr(a_scales, torch.uint8, T * cols * FP8_SCALE_BYTES, "a_scales"),
+        _dptr(bad_ids, torch.int32, 1, "bad_ids"), _stream(stream)))
+
+
+def engram_project_mxfp8_staged(a_codes, a_scales, cols: int, wkv_codes, wkv_scales, kv, T: int,
+                                N: int, stream=None) -> None:
+    """kv [T, N] from a staged MXFP8 activation and the MXFP8 wkv."""
+    K = cols * HEAD_DIM
+    _check(_lib.engram_project_mxfp8_staged(
+        _dptr(a_codes, torch.uint8, T * K, "a_codes"),
+        _dptr(a_scales, torch.uint8, T * (K // 32), "a_scales"), int(cols),
+        _dptr(wkv_codes, torch.uint8, N * K, "wkv_codes"),
+        _dptr(wkv_scales, torch.uint8, N * (K // 32), "wkv_scales"),
+        _dptr(kv, torch.int16, T * N, "kv"), int(T), int(N), _stream(stream)))
 
 
 def engram_gate(h, kv, q_weight, k_weight, token_mask, T: int, hc: int, dim: int, eps: float,

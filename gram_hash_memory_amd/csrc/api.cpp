@@ -323,6 +323,63 @@ engram_status engram_project_mxfp8(const uint8_t *table, const uint8_t *scales,
                     "engram_project_mxfp8 launch");
 }
 
+engram_status engram_stage_mxfp8(const uint8_t *table, const uint8_t *scales, int64_t num_rows,
+                                 const int32_t *ids, int64_t ids_token_stride, int32_t cols,
+                                 int32_t T, uint8_t *a_codes, uint8_t *a_scales,
+                                 int32_t *bad_ids, hipStream_t stream) {
+  engram_status st =
+      check_rows_shape(ENGRAM_ROWS_FP8_E4M3_E8M0, num_rows, ids_token_stride, cols, T);
+  if (st != ENGRAM_OK) return st;
+  REQUIRE(int64_t(cols) * ENGRAM_HEAD_DIM <= kInt32Max, "cols=%d too large", cols);
+  if (T == 0) return ENGRAM_OK;
+  REQUIRE(table && aligned(table, 16), "table is NULL or not 16-byte aligned");
+  REQUIRE(scales && aligned(scales, 4), "scales is NULL or not 4-byte aligned");
+  REQUIRE(ids && aligned(ids, 4), "ids is NULL or misaligned");
+  REQUIRE(!bad_ids || aligned(bad_ids, 4), "bad_ids misaligned");
+  REQUIRE(a_codes && aligned(a_codes, 16), "a_codes is NULL or not 16-byte aligned");
+  REQUIRE(a_scales && aligned(a_scales, 4), "a_scales is NULL or not 4-byte aligned");
+  return hip_status(engram::launch_stage_mx(table, scales, num_rows, ids, ids_token_stride, cols,
+                                            T, a_codes, a_scales, bad_ids, stream),
+                    "engram_stage_mxfp8 launch");
+}
+
+namespace {
+engram_status check_project_mx_staged(const uint8_t *a_codes, const uint8_t *a_scales,
+                                      int32_t cols, const uint8_t *wc, const uint8_t *ws,
+                                      const uint16_t *kv, int32_t T, int32_t N) {
+  REQUIRE(cols >= 1 && int64_t(cols) * ENGRAM_HEAD_DIM <= kInt32Max, "cols=%d out of range",
+          cols);
+  const int32_t K = cols * ENGRAM_HEAD_DIM;
+  engram_status st = check_project_shape(T, K, N);
+  if (st != ENGRAM_OK) return st;
+  REQUIRE_SUP(engram::project_mx_supported(N, K),
+              "MXFP8 weight of %d x %d bytes exceeds %lld", N, K,
+              (long long)ENGRAM_MX_MAX_WEIGHT_BYTES);
+  REQUIRE_SUP(int64_t(T) * K <= ENGRAM_MX_MAX_WEIGHT_BYTES,
+              "MXFP8 activation of %d x %d bytes exceeds %lld", T, K,
+              (long long)ENGRAM_MX_MAX_WEIGHT_BYTES);
+  if (T == 0) return ENGRAM_OK;
+  REQUIRE(a_codes && aligned(a_codes, 16), "a_codes is NULL or not 16-byte aligned");
+  REQUIRE(a_scales && aligned(a_scales, 4), "a_scales is NULL or not 4-byte aligned");
+  REQUIRE(wc && aligned(wc, 16), "wkv codes are NULL or not 16-byte aligned");
+  REQUIRE(ws && aligned(ws, 4), "wkv scales are NULL or not 4-byte aligned");
+  REQUIRE(kv && aligned(kv, 16), "kv is NULL or not 16-byte aligned");
+  return ENGRAM_OK;
+}
+}  // namespace
+
+engram_status engram_project_mxfp8_staged(const uint8_t *a_codes, const uint8_t *a_scales,
+                                          int32_t cols, const uint8_t *wkv_codes,
+                                          const uint8_t *wkv_scales, uint16_t *kv, int32_t T,
+                                          int32_t N, hipStream_t stream) {
+  engram_status st =
+      check_project_mx_staged(a_codes, a_scales, cols, wkv_codes, wkv_scales, kv, T, N);
+  if (st != ENGRAM_OK || T == 0) return st;
+  return hip_status(engram::launch_project_mx_staged(a_codes, a_scales, cols, wkv_codes,
+                                                     wkv_scales, kv, T, N, stream),
+                    "engram_project_mxfp8_staged launch");
+}
+
 engram_status engram_gate(float *h, const uint16_t *kv, const uint16_t *q_weight,
                           const uint16_t *k_weight, const uint8_t *token_mask, int32_t T,
                           int32_t hc, int32_t dim, float eps, float clamp, float dot_scale,
@@ -412,6 +469,12 @@ engram_status forward_impl(const engram_hash_params *params, const engram_tokens
   ws += align256(size_t(T) * L * cols * sizeof(int32_t));
   uint16_t *rows = reinterpret_cast<uint16_t *>(ws);
   ws += align256(size_t(T) * K * sizeof(uint16_t));
+  // MXFP8 layers beyond the weight-streaming form's token count stage their
+  // rows in the same buffer: codes [T][K], then scales [T][K / 32].
+  uint8_t *const mx_codes = reinterpret_cast<uint8_t *>(rows);
+  uint8_t *const mx_scales = mx_codes + align256(size_t(T) * K);
+  const bool mx_staged = !engram::project_mx_skinny_supported(T, cols) &&
+                         int64_t(T) * K <= ENGRAM_MX_MAX_WEIGHT_BYTES;
   // one kv per layer: every projection runs before the one gate pass
   uint16_t *kv_all = reinterpret_cast<uint16_t *>(ws);
   const size_t kv_elems = align256(size_t(T) * N * sizeof(uint16_t)) / sizeof(uint16_t);
@@ -448,7 +511,20 @@ engram_status forward_impl(const engram_hash_params *params, const engram_tokens
     // an MXFP8 weight: rows -> projection, which measures faster than
     // engram_project_fp8 (the rows kernel gathers whole rows once; the fused
     // kernel gathers 128-byte pieces of random rows for every tile column).
-    if (ly.wkv_mx) {
+    if (ly.wkv_mx && mx_staged) {
+      // MXFP8 with the 256 x 256 tiles: the rows are first staged into an
+      // MXFP8 activation in the rows buffer, which the tiles then read as
+      // they read the weight (the same kv bits as the gather form).
+      if ((st = hip_status(engram::launch_stage_mx(ly.table, ly.scales, ly.num_rows,
+                                                   ids + l * cols, int64_t(L) * cols, cols, T,
+                                                   mx_codes, mx_scales, bad_ids, stream),
+                           "MXFP8 staging launch")) != ENGRAM_OK)
+        return st;
+      if ((st = hip_status(engram::launch_project_mx_staged(mx_codes, mx_scales, cols, ly.wkv_mx,
+                                                            ly.wkv_mx_scales, kv, T, N, stream),
+                           "MXFP8 project launch")) != ENGRAM_OK)
+        return st;
+    } else if (ly.wkv_mx) {
       if ((st = hip_status(engram::launch_project_mx(ly.table, ly.scales, ly.num_rows,
                                                      ids + l * cols, int64_t(L) * cols, cols,
                                                      ly.wkv_mx, ly.wkv_mx_scales, kv, T, N,

@@ -115,6 +115,17 @@ hipError_t launch_project_mx(const uint8_t *table, const uint8_t *scales, int64_
                              const int32_t *ids, int64_t ids_token_stride, int32_t cols,
                              const uint8_t *w_codes, const uint8_t *w_scales, uint16_t *c,
                              int32_t M, int32_t N, int32_t *bad_ids, hipStream_t stream);
+// The MXFP8 activation of FP8 rows (codes [M][cols*256], scales [M][cols*8])
+// and the 256 x 256 MXFP8 tiles on it (gemm_mx.hip); for cols >= 2, the same
+// kv bits as launch_project_mx's tile form.
+hipError_t launch_stage_mx(const uint8_t *table, const uint8_t *scales, int64_t num_rows,
+                           const int32_t *ids, int64_t ids_token_stride, int32_t cols, int32_t M,
+                           uint8_t *a_codes, uint8_t *a_scales, int32_t *bad_ids,
+                           hipStream_t stream);
+hipError_t launch_project_mx_staged(const uint8_t *a_codes, const uint8_t *a_scales,
+                                    int32_t cols, const uint8_t *w_codes,
+                                    const uint8_t *w_scales, uint16_t *c, int32_t M, int32_t N,
+                                    hipStream_t stream);
 hipError_t launch_quantize_mx(const uint16_t *w, int32_t N, int32_t K, uint8_t *codes,
                               uint8_t *scales, hipStream_t stream);
 

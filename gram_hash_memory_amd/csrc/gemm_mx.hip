@@ -293,6 +293,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
 // transposed and the epilogue is wave-private (store_wave_transposed).  Ids
 // outside the table are counted as their column's addresses are resolved,
 // for the tiles of the first column of tiles.
+// kStaged: A is an MXFP8 activation staged by stage_mx_kernel (`table` =
+// codes [M][K], `tscales` = scales [M][K/32], row-major like W and WS), read
+// exactly like B; ids, num_rows and bad_ids are unused.  The MFMAs and their
+// order are the same, so kv is bit-identical to the gather form's.
+template <bool kStaged>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mx_persistent_kernel(
     const uint8_t *__restrict__ table, const uint8_t *__restrict__ tscales, int64_t num_rows,
     const int32_t *__restrict__ ids, int64_t ids_stride, const uint8_t *__restrict__ W,
@@ -325,6 +330,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_persistent_kernel(
     const int n0_ = tn_ * BN;
     return make_rsrc(WS + int64_t(n0_) * ks, int64_t(N - n0_) * ks);
   };
+  // Staged A: the same addressing as B, over M rows.
+  auto rsrc_a = [&](int tm_) {
+    const int m0_ = tm_ * BM;
+    return make_rsrc(table + int64_t(m0_) * K, kStaged ? int64_t(M - m0_) * K : 0);
+  };
+  auto rsrc_as = [&](int tm_) {
+    const int m0_ = tm_ * BM;
+    return make_rsrc(tscales + int64_t(m0_) * ks, kStaged ? int64_t(M - m0_) * ks : 0);
+  };
 
   // A: the ids of one column of one tile (rows row0 .. row0 + 63 of this
   // wave) and their resolved addresses, as in gemm_mx_kernel.
@@ -337,6 +351,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_persistent_kernel(
   const uint8_t *a_src[kSegs];
   const uint8_t *as_src;
   auto load_ids = [&](int tm_, int c, bool count) {
+    if constexpr (kStaged) return;
     const int row0 = tm_ * BM + wave * 64;
     const uint32_t voff_id = uint32_t((row0 + seg_row) * ids_stride * 4);
     const uint32_t voff_ids = uint32_t((row0 + lane) * ids_stride * 4);
@@ -349,6 +364,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_persistent_kernel(
     idn_count = count;
   };
   auto resolve = [&]() {
+    if constexpr (kStaged) return;
 #pragma unroll
     for (int k = 0; k < kSegs; ++k) {
       const bool ok = idn_row0 + 8 * k + seg_row < M && idn[k] >= 0 && idn[k] < num_rows;
@@ -361,15 +377,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_persistent_kernel(
     bad += idn_count && row_ok && !ok;
   };
   // Stage of B slice kb (K positions 128 kb ..) and A half `half` of the
-  // resolved column into LDS buffer `buf`.
-  auto dma = [&](int buf, __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rbs, int kb,
-                 const int half) {
+  // resolved column (staged: A slice kb of resource ra) into LDS buffer `buf`.
+  auto dma = [&](int buf, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t ras,
+                 __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rbs, int kb, const int half) {
     uint8_t *st = smem + buf * kStageBytes;
 #pragma unroll
     for (int i = 0; i < kSegs; ++i) {
       const int seg = wave * kSegs + i;
-      __builtin_amdgcn_global_load_lds(a_src[i] + half * kBK, lds_ptr(st + seg * 1024), 16, 0,
-                                       0);
+      if constexpr (kStaged)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_ptr(st + seg * 1024), 16,
+                                                 ((i & 1) ? voff_odd : voff_even) + seg * 8 * K,
+                                                 kb * kBK, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(a_src[i] + half * kBK, lds_ptr(st + seg * 1024), 16, 0,
+                                         0);
     }
 #pragma unroll
     for (int i = 0; i < kSegs; ++i) {
@@ -378,8 +399,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_persistent_kernel(
                                                ((i & 1) ? voff_odd : voff_even) + seg * 8 * K,
                                                kb * kBK, 0, 0);
     }
-    __builtin_amdgcn_global_load_lds(as_src + half * 4,
-                                     lds_ptr(st + 2 * kTileBytes + wave * 256), 4, 0, 0);
+    if constexpr (kStaged)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, lds_ptr(st + 2 * kTileBytes + wave * 256), 4,
+                                               voff_bs, kb * 4, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(as_src + half * 4,
+                                       lds_ptr(st + 2 * kTileBytes + wave * 256), 4, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rbs, lds_ptr(st + 2 * kTileBytes + kScaleBytes + wave * 256), 4, voff_bs, kb * 4, 0, 0);
   };
@@ -435,6 +460,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_persistent_kernel(
   // kt / 2 + 2 - cols past this tile's last), and the stage filled after the
   // middle barrier is the sequence's stage kt + 2.
   auto iteration = [&](const int j, int ids_tm, int ids_col, bool ids_count,
+                       __amdgpu_buffer_rsrc_t ra_f, __amdgpu_buffer_rsrc_t ras_f,
                        __amdgpu_buffer_rsrc_t rb_f, __amdgpu_buffer_rsrc_t rbs_f, int fill_kb) {
     const int b = j;
     __builtin_amdgcn_sched_barrier(0);
@@ -443,9 +469,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_persistent_kernel(
     load_frags(b, 1, 1);
     mfma_block(0, j, 0);
     sched_substep<16>();
-    if (j == 0) stage_barrier<waitcnt(kIdsPerLane, 0)>();
+    // The ids requested at j == 0 may stay in flight (the gather form).
+    if (j == 0 && !kStaged) stage_barrier<waitcnt(kIdsPerLane, 0)>();
     else stage_barrier<waitcnt(0, 0)>();
-    dma(b, rb_f, rbs_f, fill_kb, j);
+    dma(b, ra_f, ras_f, rb_f, rbs_f, fill_kb, j);
     if (j == 1) resolve();
     __builtin_amdgcn_sched_barrier(0);
     load_frags(b ^ 1, 0, 0);
@@ -458,12 +485,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_persistent_kernel(
   // column 1's addresses.
   int tm, tn;
   tile_coords(lid, tiles_m, tiles_n, tm, tn);
-  __amdgpu_buffer_rsrc_t rb = rsrc_b(tn), rbs = rsrc_bs(tn);
-  const bool counting = bad_ids != nullptr;
+  __amdgpu_buffer_rsrc_t ra = rsrc_a(tm), ras = rsrc_as(tm), rb = rsrc_b(tn), rbs = rsrc_bs(tn);
+  const bool counting = !kStaged && bad_ids != nullptr;
   load_ids(tm, 0, counting && tn == 0);
   resolve();
-  dma(0, rb, rbs, 0, 0);
-  dma(1, rb, rbs, 1, 1);
+  dma(0, ra, ras, rb, rbs, 0, 0);
+  dma(1, ra, ras, rb, rbs, 1, 1);
   load_ids(tm, 1, counting && tn == 0);
   resolve();
   stage_barrier<waitcnt(0, 0)>();
@@ -475,6 +502,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_persistent_kernel(
     const bool has_next = next < tiles;
     int tm2 = tm, tn2 = tn;
     if (has_next) tile_coords(next, tiles_m, tiles_n, tm2, tn2);
+    const __amdgpu_buffer_rsrc_t ra2 = rsrc_a(tm2), ras2 = rsrc_as(tm2);
     const __amdgpu_buffer_rsrc_t rb2 = rsrc_b(tn2), rbs2 = rsrc_bs(tn2);
     for (int kt = 0; kt < nk; kt += 2) {
       // Sequence column c + 2 for the ids, stages kt + 2 and kt + 3 for the
@@ -486,12 +514,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_persistent_kernel(
       const int ids_col = nxt ? (has_next ? c2 - cols : cols - 1) : c2;
       const bool ids_count = counting && (nxt ? has_next && tn2 == 0 : tn == 0);
       const bool fill_next = kt + 2 >= nk;
+      const __amdgpu_buffer_rsrc_t raf = fill_next && has_next ? ra2 : ra;
+      const __amdgpu_buffer_rsrc_t rasf = fill_next && has_next ? ras2 : ras;
       const __amdgpu_buffer_rsrc_t rbf = fill_next && has_next ? rb2 : rb;
       const __amdgpu_buffer_rsrc_t rbsf = fill_next && has_next ? rbs2 : rbs;
       const int kb0 = fill_next ? (has_next ? kt + 2 - nk : nk - 1) : kt + 2;
       const int kb1 = fill_next ? (has_next ? kt + 3 - nk : nk - 1) : kt + 3;
-      iteration(0, ids_tm, ids_col, ids_count, rbf, rbsf, kb0);
-      iteration(1, ids_tm, ids_col, ids_count, rbf, rbsf, kb1);
+      iteration(0, ids_tm, ids_col, ids_count, raf, rasf, rbf, rbsf, kb0);
+      iteration(1, ids_tm, ids_col, ids_count, raf, rasf, rbf, rbsf, kb1);
     }
     store_wave_transposed<4, 4, 1>(acc, stg, C, M, N, tm * BM + wm * 128, tn * BN + wn * 128,
                                    lane);
@@ -503,6 +533,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_persistent_kernel(
     lid = next;
     tm = tm2;
     tn = tn2;
+    ra = ra2;
+    ras = ras2;
     rb = rb2;
     rbs = rbs2;
   }
@@ -510,6 +542,69 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_persistent_kernel(
   if (bad) atomicAdd(bad_ids, bad);
 }
 
+// The MXFP8 activation of FP8 rows: row (t, r) of the flattened [M * cols]
+// goes to codes[t][256 r ..] and scales[t][8 r ..].  16 lanes per row, each
+// a 16-byte piece of the codes (lane 0 also the 8 scale bytes, as two words:
+// the scale arrays are 4-byte aligned); each group of 16 lanes takes
+// kStageRows rows, whose ids and then codes are all requested before the
+// first store.  An id outside the table writes zero codes and scale bytes
+// 127 (2^0: the row is exactly zero) and is counted.
+constexpr int kStageRows = 4;
+constexpr int kStageRowsPerBlock = kThreads / 16 * kStageRows;
+
+__global__ __launch_bounds__(kThreads) void stage_mx_kernel(
+    const uint8_t *__restrict__ table, const uint8_t *__restrict__ tscales, int64_t num_rows,
+    const int32_t *__restrict__ ids, int64_t ids_stride, int cols, int M,
+    uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, int32_t *__restrict__ bad_ids) {
+  const int piece = threadIdx.x & 15;
+  const int64_t total = int64_t(M) * cols;
+  const int64_t first = int64_t(blockIdx.x) * kStageRowsPerBlock + (threadIdx.x >> 4);
+  int32_t id[kStageRows];
+  bool ok[kStageRows];
+#pragma unroll
+  for (int k = 0; k < kStageRows; ++k) {
+    const int64_t row = first + int64_t(k) * (kThreads / 16);
+    id[k] = -1;
+    if (row < total) {
+      const int64_t t = row / cols, r = row - t * cols;
+      id[k] = ids[t * ids_stride + r];
+    }
+    ok[k] = row < total && id[k] >= 0 && id[k] < num_rows;
+  }
+  u32x4 v[kStageRows];
+#pragma unroll
+  for (int k = 0; k < kStageRows; ++k) {
+    v[k] = u32x4{0, 0, 0, 0};
+    if (ok[k])
+      v[k] = *reinterpret_cast<const u32x4 *>(table + int64_t(id[k]) * ENGRAM_HEAD_DIM +
+                                              16 * piece);
+  }
+  int bad = 0;
+#pragma unroll
+  for (int k = 0; k < kStageRows; ++k) {
+    const int64_t row = first + int64_t(k) * (kThreads / 16);
+    if (row >= total) continue;
+    *reinterpret_cast<u32x4 *>(codes + row * ENGRAM_HEAD_DIM + 16 * piece) = v[k];
+    if (piece == 0) {
+      uint32_t s0 = 0x7F7F7F7Fu, s1 = 0x7F7F7F7Fu;
+      if (ok[k]) {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(tscales + int64_t(id[k]) * 8);
+        s0 = src[0];
+        s1 = src[1];
+      }
+      uint32_t *dst = reinterpret_cast<uint32_t *>(scales + row * 8);
+      dst[0] = s0;
+      dst[1] = s1;
+      bad += !ok[k];
+    }
+  }
+  __shared__ int n_bad;
+  if (threadIdx.x == 0) n_bad = 0;
+  __syncthreads();
+  if (bad) atomicAdd(&n_bad, bad);
+  __syncthreads();
+  if (threadIdx.x == 0 && n_bad && bad_ids) atomicAdd(bad_ids, n_bad);
+}
 }  // namespace
 
 bool project_mx_supported(int32_t N, int32_t K) {
@@ -527,13 +622,13 @@ hipError_t launch_project_mx(const uint8_t *table, const uint8_t *scales, int64_
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   if (cols >= 2) {
     const size_t lds = size_t(2) * kStageBytes + size_t(kWaves) * 32 * kStgStride * 2;
-    const void *fn = reinterpret_cast<const void *>(&gemm_mx_persistent_kernel);
+    const void *fn = reinterpret_cast<const void *>(&gemm_mx_persistent_kernel<false>);
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gemm_mx_persistent_kernel, dim3(persistent_grid(tiles_m * tiles_n, stream)),
-                       dim3(kThreads), lds, stream, table, scales, num_rows, ids,
-                       ids_token_stride, w_codes, w_scales, c, M, N, K, tiles_m, tiles_n,
-                       bad_ids);
+    hipLaunchKernelGGL(gemm_mx_persistent_kernel<false>,
+                       dim3(persistent_grid(tiles_m * tiles_n, stream)), dim3(kThreads), lds,
+                       stream, table, scales, num_rows, ids, ids_token_stride, w_codes, w_scales,
+                       c, M, N, K, tiles_m, tiles_n, bad_ids);
     return hipGetLastError();
   }
   const size_t lds = size_t(2) * kStageBytes;
@@ -543,6 +638,35 @@ hipError_t launch_project_mx(const uint8_t *table, const uint8_t *scales, int64_
   hipLaunchKernelGGL(gemm_mx_kernel, dim3(tiles_m * tiles_n), dim3(kThreads), lds, stream,
                      table, scales, num_rows, ids, ids_token_stride, w_codes, w_scales, c, M, N,
                      K, tiles_m, tiles_n, bad_ids);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_mx(const uint8_t *table, const uint8_t *scales, int64_t num_rows,
+                           const int32_t *ids, int64_t ids_token_stride, int32_t cols, int32_t M,
+                           uint8_t *a_codes, uint8_t *a_scales, int32_t *bad_ids,
+                           hipStream_t stream) {
+  const int64_t rows = int64_t(M) * cols;
+  const int64_t blocks = (rows + kStageRowsPerBlock - 1) / kStageRowsPerBlock;
+  hipLaunchKernelGGL(stage_mx_kernel, dim3(uint32_t(blocks)), dim3(kThreads), 0, stream, table,
+                     scales, num_rows, ids, ids_token_stride, cols, M, a_codes, a_scales,
+                     bad_ids);
+  return hipGetLastError();
+}
+
+hipError_t launch_project_mx_staged(const uint8_t *a_codes, const uint8_t *a_scales,
+                                    int32_t cols, const uint8_t *w_codes,
+                                    const uint8_t *w_scales, uint16_t *c, int32_t M, int32_t N,
+                                    hipStream_t stream) {
+  const int K = cols * ENGRAM_HEAD_DIM;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const size_t lds = size_t(2) * kStageBytes + size_t(kWaves) * 32 * kStgStride * 2;
+  const void *fn = reinterpret_cast<const void *>(&gemm_mx_persistent_kernel<true>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gemm_mx_persistent_kernel<true>,
+                     dim3(persistent_grid(tiles_m * tiles_n, stream)), dim3(kThreads), lds,
+                     stream, a_codes, a_scales, int64_t(0), (const int32_t *)nullptr, int64_t(0),
+                     w_codes, w_scales, c, M, N, K, tiles_m, tiles_n, (int32_t *)nullptr);
   return hipGetLastError();
 }
 

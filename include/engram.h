@@ -335,6 +335,42 @@ ENGRAM_API engram_status engram_project_mxfp8(const uint8_t *table, const uint8_
                                               int32_t T, int32_t N, int32_t *bad_ids,
                                               hipStream_t stream);
 
+/* The MXFP8 activation of FP8 rows, for engram_project_mxfp8_staged ([vLLM]
+ * EngramBatch: the FP8 rows of a batch are staged into an MXFP8 buffer that
+ * the WKV GEMM takes as its activation).  Row r of token t is copied as
+ * stored: a_codes[t][r*256 + i] = table[ids[t][r]][i], a_scales[t][r*8 + b] =
+ * scales[ids[t][r]][b].  An id outside the table gives zero codes and scale
+ * bytes 127 (2^0; the row contributes exactly 0 to any product) and is
+ * counted in bad_ids as engram_rows counts it.
+ *   table, scales, num_rows, ids, ids_token_stride, cols, T, bad_ids as for
+ *   engram_project_mxfp8; a_codes DEVICE [T][cols*256], 16-byte aligned;
+ *   a_scales DEVICE [T][cols*8], 4-byte aligned; both fully overwritten.
+ */
+ENGRAM_API engram_status engram_stage_mxfp8(const uint8_t *table, const uint8_t *scales,
+                                            int64_t num_rows, const int32_t *ids,
+                                            int64_t ids_token_stride, int32_t cols, int32_t T,
+                                            uint8_t *a_codes, uint8_t *a_scales,
+                                            int32_t *bad_ids, hipStream_t stream);
+
+/* engram_project_mxfp8 on a staged MXFP8 activation (engram_stage_mxfp8):
+ * kv[t][n] = bf16(sum_k a[t][k] * w[n][k]) with a = a_codes/a_scales and w =
+ * wkv_codes/wkv_scales as in engram_project_mxfp8.  Always the 256 x 256
+ * tiles, reading the activation as they read the weight; the same kv bits as
+ * engram_project_mxfp8's tile form on the rows that were staged (for every
+ * T > 64, and for every T when cols % 4 != 0 or cols > 64).
+ *   a_codes DEVICE [T][K], 16-byte aligned; a_scales DEVICE [T][K/32],
+ *   4-byte aligned (K = cols * 256); wkv_codes, wkv_scales, kv, N as for
+ *   engram_project_mxfp8.
+ *   Limits: N * K and T * K <= ENGRAM_MX_MAX_WEIGHT_BYTES (32-bit-offset
+ *   buffer descriptors); beyond either the call returns
+ *   ENGRAM_ERR_UNSUPPORTED.
+ */
+ENGRAM_API engram_status engram_project_mxfp8_staged(const uint8_t *a_codes,
+                                                     const uint8_t *a_scales, int32_t cols,
+                                                     const uint8_t *wkv_codes,
+                                                     const uint8_t *wkv_scales, uint16_t *kv,
+                                                     int32_t T, int32_t N, hipStream_t stream);
+
 /* Stage 4 -- gate, in place on the fp32 highway ([spark] overview stage 4;
  * [NeMo] _engram_gate_core, compile_engram_gate; [vLLM] Engram).
  *   h DEVICE fp32 [T][hc][dim], updated in place.
@@ -380,8 +416,11 @@ ENGRAM_API size_t engram_workspace_bytes(int32_t T, int32_t n_layers, int32_t co
  * Q2_K layers within the limits of engram_project_q2k run rows -> projection
  * as that fused kernel (same kv bits) when T > 128, or when T <= 128 and
  * cols % 4 == 0; other few-token Q2_K layers run rows -> the weight-streaming
- * projection.  FP8 layers that carry wkv_mx run engram_project_mxfp8 instead
- * of rows -> projection.
+ * projection.  FP8 layers that carry wkv_mx run the MXFP8 projection instead
+ * of rows -> projection: engram_project_mxfp8's weight-streaming form where
+ * it applies (T <= 64, cols % 4 == 0, cols <= 64), else engram_stage_mxfp8
+ * into the rows buffer -> engram_project_mxfp8_staged (T * K within its
+ * limit; beyond it engram_project_mxfp8's gather tiles).
  *   layers: HOST array [params->n_layers] of DEVICE-pointer descriptors.
  *   workspace: DEVICE, at least engram_workspace_bytes(...) bytes, 256-byte
  *   aligned; its contents are scratch.  Every other argument is as for the

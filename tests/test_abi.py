@@ -55,7 +55,8 @@ def declared_functions():
 def test_header_declares_the_five_calls_and_helpers():
     names = declared_functions()
     for want in ("engram_hash", "engram_history_update", "engram_rows", "engram_project", "engram_project_q2k",
-                 "engram_project_fp8", "engram_quantize_mxfp8", "engram_project_mxfp8", "engram_gate",
+                 "engram_project_fp8", "engram_quantize_mxfp8", "engram_project_mxfp8",
+                 "engram_stage_mxfp8", "engram_project_mxfp8_staged", "engram_gate",
                  "engram_gate_layers", "engram_forward", "engram_workspace_bytes", "engram_last_error"):
         assert want in names
 
@@ -146,6 +147,13 @@ def _raw(eg):
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                          ctypes.c_void_p]
+    lib.engram_stage_mxfp8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+    lib.engram_project_mxfp8_staged.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
     lib.engram_forward.argtypes = [ctypes.POINTER(_HP), ctypes.POINTER(_TK),
                                    ctypes.POINTER(_LY), ctypes.c_void_p, ctypes.c_int32,
                                    ctypes.c_int32, ctypes.c_float, ctypes.c_float,
@@ -316,6 +324,42 @@ class TestValidation:
         # a table of 2^32 bytes and more is fine (64-bit row addresses)
         assert call(nrows=2**25, T=0, table=None, ids=None, wc=None, ws=None,
                     kv=None) == eg.ENGRAM_OK
+
+    def test_stage_mxfp8_rejects(self, eg):
+        lib = _raw(eg)
+        ok = dict(table=FAKE, scales=FAKE, nrows=100, ids=FAKE, stride=24, cols=24, T=8,
+                  ac=FAKE, asc=FAKE, bad=None)
+
+        def call(**kw):
+            a = dict(ok, **kw)
+            return lib.engram_stage_mxfp8(a["table"], a["scales"], a["nrows"], a["ids"],
+                                          a["stride"], a["cols"], a["T"], a["ac"], a["asc"],
+                                          a["bad"], None)
+        for kw in (dict(nrows=0), dict(cols=0), dict(stride=23), dict(T=-1), dict(table=None),
+                   dict(table=FAKE + 4), dict(scales=None), dict(scales=FAKE + 2),
+                   dict(ids=None), dict(ids=FAKE + 1), dict(ac=None), dict(ac=FAKE + 8),
+                   dict(asc=None), dict(asc=FAKE + 2), dict(bad=FAKE + 2)):
+            assert call(**kw) == eg.ENGRAM_ERR_ARG, kw
+        assert call(T=0, table=None, ids=None, ac=None, asc=None) == eg.ENGRAM_OK
+
+    def test_project_mxfp8_staged_rejects(self, eg):
+        lib = _raw(eg)
+        ok = dict(ac=FAKE, asc=FAKE, cols=24, wc=FAKE, ws=FAKE, kv=FAKE, T=300, N=512)
+
+        def call(**kw):
+            a = dict(ok, **kw)
+            return lib.engram_project_mxfp8_staged(a["ac"], a["asc"], a["cols"], a["wc"],
+                                                   a["ws"], a["kv"], a["T"], a["N"], None)
+        for kw in (dict(cols=0), dict(T=-1), dict(N=0), dict(ac=None), dict(ac=FAKE + 8),
+                   dict(asc=None), dict(asc=FAKE + 2), dict(wc=None), dict(wc=FAKE + 8),
+                   dict(ws=None), dict(ws=FAKE + 1), dict(kv=None), dict(kv=FAKE + 8)):
+            assert call(**kw) == eg.ENGRAM_ERR_ARG, kw
+        # the weight and the activation are read through 32-bit-offset buffer descriptors
+        assert call(N=2147483632 // 6144 + 1) == eg.ENGRAM_ERR_UNSUPPORTED
+        assert "exceeds" in lib.engram_last_error().decode()
+        assert call(T=2147483632 // 6144 + 1) == eg.ENGRAM_ERR_UNSUPPORTED
+        assert "activation" in lib.engram_last_error().decode()
+        assert call(T=0, ac=None, asc=None, wc=None, ws=None, kv=None) == eg.ENGRAM_OK
 
     def test_project_fp8_rejects(self, eg):
         lib = _raw(eg)

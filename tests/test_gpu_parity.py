@@ -968,6 +968,56 @@ def test_project_mxfp8_ragged_and_bad_ids(eg, T, cols, N, stride):
     assert exact > 0.9, exact
 
 
+@pytest.mark.parametrize("T,cols,N,stride", [(1, 1, 64, 1), (3, 3, 320, 3), (255, 5, 520, 5),
+                                             (257, 6, 256, 12), (300, 24, 4096, 24),
+                                             (600, 24, 700, 48), (64, 4, 20480, 8),
+                                             (100, 24, 2048, 48), (300, 1, 520, 1),
+                                             (1500, 2, 16390, 2)])
+def test_stage_and_project_mxfp8_staged(eg, T, cols, N, stride):
+    # engram_stage_mxfp8 copies the raw rows (codes and scale bytes) by id,
+    # bit for bit as the oracle's gather gives them (an id outside the table:
+    # zero codes, scale bytes 127), with guards after both outputs and bad ids
+    # counted.  engram_project_mxfp8_staged on them equals
+    # engram_project_mxfp8 bit for bit wherever that call runs its 256 x 256
+    # tiles, and is held to the oracle's MXFP8 bar everywhere.
+    rng = np.random.default_rng(13 * T + cols)
+    R = 777
+    table_np, scales_np = workloads.fp8_table(4, 0, R)
+    ids_full = rng.integers(0, R, (T, stride)).astype(np.int32)
+    bad_mask = rng.random((T, stride)) < 0.05
+    ids_full[bad_mask] = rng.choice([-1, R, R + 5, 2**31 - 1, -(2**31)], int(bad_mask.sum()))
+    off = stride - cols
+    ids_np = ids_full[:, off:]
+    K = cols * 256
+    table, tscales = tensor(table_np, "cuda"), tensor(scales_np, "cuda")
+    ids = tensor(ids_full, "cuda")
+    g_codes = Guarded((T, K), torch.uint8, 0x55)
+    g_scales = Guarded((T, K // 32), torch.uint8, 0x55)
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    eg.engram_stage_mxfp8(table, tscales, R, ids.view(-1)[off:], stride, cols, T, g_codes.t,
+                          g_scales.t, bad)
+    g_codes.check()
+    g_scales.check()
+    assert bad.item() == int(bad_mask[:, off:].sum())
+    want_c, want_s = oracle.rows_fp8_mx(table_np, scales_np, ids_np)
+    assert np.array_equal(g_codes.t.cpu().numpy(), want_c)
+    assert np.array_equal(g_scales.t.cpu().numpy(), want_s)
+    wkv_np = oracle.bf16_bits(oracle.bf16_round(0.05 * rng.standard_normal((N, K))))
+    w_codes, w_scales = oracle.quantize_mxfp8(wkv_np)
+    wc, ws = tensor(w_codes, "cuda"), tensor(w_scales, "cuda")
+    g = Guarded((T, N), torch.int16, 0x7777)
+    eg.engram_project_mxfp8_staged(g_codes.t, g_scales.t, cols, wc, ws, g.t, T, N)
+    g.check()
+    got = g.t.cpu().numpy().view(np.uint16)
+    if T > 64 or cols % 4 != 0 or cols > 64:           # the gather call's tile form
+        kv_g = torch.empty((T, N), dtype=torch.int16, device="cuda")
+        eg.engram_project_mxfp8(table, tscales, R, ids.view(-1)[off:], stride, cols, wc, ws,
+                                kv_g, T, N)
+        assert np.array_equal(got, kv_g.cpu().numpy().view(np.uint16))
+    exact = _check_kv_mx(got, want_c, want_s, w_codes, w_scales)
+    assert exact > 0.9, exact
+
+
 def oracle_mx_weight(c, layer):
     if (c, layer) not in _omx_w:
         _omx_w[(c, layer)] = _oracle_mx_weight(host(c).layers[layer].wkv)
