@@ -67,7 +67,7 @@ extern "C" {
 typedef enum engram_status ENGRAM_ENUM_BASE {
   ENGRAM_OK = 0,
   ENGRAM_ERR_ARG = 1,          /* invalid argument: null, misaligned, bad size     */
-  ENGRAM_ERR_UNSUPPORTED = 2,  /* valid for the method, beyond this build's limits */
+  ENGRAM_ERR_UNSUPPORTED = 2,  /* valid for the method, beyond this library's limits */
   ENGRAM_ERR_HIP = 3           /* a HIP launch or runtime call failed             */
 } engram_status;
 
