@@ -331,6 +331,8 @@ engram_status engram_stage_mxfp8(const uint8_t *table, const uint8_t *scales, in
       check_rows_shape(ENGRAM_ROWS_FP8_E4M3_E8M0, num_rows, ids_token_stride, cols, T);
   if (st != ENGRAM_OK) return st;
   REQUIRE(int64_t(cols) * ENGRAM_HEAD_DIM <= kInt32Max, "cols=%d too large", cols);
+  // one workgroup per 64 rows of the flattened [T * cols]
+  REQUIRE_SUP(int64_t(T) * cols <= int64_t(kInt32Max) * 64, "T * cols too large");
   if (T == 0) return ENGRAM_OK;
   REQUIRE(table && aligned(table, 16), "table is NULL or not 16-byte aligned");
   REQUIRE(scales && aligned(scales, 4), "scales is NULL or not 4-byte aligned");
