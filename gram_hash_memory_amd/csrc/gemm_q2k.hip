@@ -28,14 +28,15 @@
 // ahead.
 // Two forms of the same K loop:
 //  - gemm_q2k_persistent_kernel (even column counts): one workgroup of 8
-//    waves per CU walks its share of the tiles.  The next tile's ids, its first blocks and
-//    its first two B slices are fetched during the current tile's last
-//    column, so the K loop runs on from tile to tile; each B slice is
-//    requested in the k-step after the barrier that frees its stage, a whole
-//    stage ahead of its use.  The MFMAs take wkv as their first operand, so a lane
-//    ends with 4 consecutive output columns per block row and writes them to
-//    a wave-private LDS staging area as 8 bytes; the wave then stores whole
-//    128-byte row segments.  No workgroup barrier sits in the epilogue.
+//    waves per CU walks its share of the tiles.  The next tile's ids, its
+//    first blocks and its first two B slices are fetched during the current
+//    tile's last column, so the K loop runs on from tile to tile; each B
+//    slice is requested in the k-step after the barrier that frees its
+//    stage, a whole stage ahead of its use.  The MFMAs take wkv as their
+//    first operand, so a lane ends with 4 consecutive output columns per
+//    block row and writes them to a wave-private LDS staging area as 8
+//    bytes; the wave then stores whole 128-byte row segments.  No workgroup
+//    barrier sits in the epilogue.
 //  - q2k_tile (one tile per workgroup): odd column counts, and the exact
 //    recompute below.
 // Both give every output the same MFMAs in the same K order as gemm.hip
