@@ -50,10 +50,20 @@ __device__ __forceinline__ void bf16x8_to_f32(const u32x4 w, float *f) {
 // blockIdx.x % hc of token blockIdx.x / hc only (HC = 1 then, hc the real
 // stream count): the value is then read once per stream, but a decode batch
 // of a few dozen tokens spreads over hc times more workgroups.
+//
+// Where a thread's slices are few (HC * NCH <= 8: the hc = 4, dim <= 4096
+// shapes), a layer's key, value and q/k weight slices are loaded into
+// registers in one batch before its sums start, and the key and value slices
+// of the next layer are requested right behind them, so that they arrive
+// while this layer reduces.  Each layer then waits on memory once, not three
+// times (keys and weights, then the value after the reduction, then the next
+// layer's keys).  Wider shapes keep the loads at their use: their streams
+// alone fill most of the registers.
 template <int HC, int NCH, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void gate_kernel(
     float *__restrict__ h, const GateLayers layers, const uint8_t *__restrict__ mask,
     int32_t dim, int32_t hc, float eps, float clamp, float dot_scale) {
+  constexpr bool kBatch = HC * NCH <= 8;
   const int64_t t = SPLIT ? blockIdx.x / hc : blockIdx.x;
   const int s0 = SPLIT ? int(blockIdx.x % hc) : 0;   // first stream of this workgroup
   const int nstreams = SPLIT ? hc : HC;
@@ -63,25 +73,71 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(
   float *ht = h + (t * nstreams + s0) * int64_t(dim);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const float inv_dim = 1.0f / float(dim);
+  auto i0_of = [&](int c) { return (int(threadIdx.x) + c * kThreads) * kVec; };
   float x[HC][NCH][kVec];
   float ssx[HC], ssk[HC], dot[HC];
 
-  // Partial sums of one chunk of one stream against layer l's key and weights.
-  auto accumulate = [&](int l, int c, int s, int i0) {
-    const uint16_t *kvt =
-        layers.kv[l] + t * (nstreams + 1) * int64_t(dim) + (s0 + s) * int64_t(dim);
-    const uint16_t *qw = layers.qw[l] + (s0 + s) * int64_t(dim);
-    const uint16_t *kw = layers.kw[l] + (s0 + s) * int64_t(dim);
-    float key[kVec], q[kVec], k[kVec];
-    bf16x8_to_f32(*reinterpret_cast<const u32x4 *>(kvt + i0), key);
-    bf16x8_to_f32(*reinterpret_cast<const u32x4 *>(qw + i0), q);
-    bf16x8_to_f32(*reinterpret_cast<const u32x4 *>(kw + i0), k);
+  // Layer l's slices: key of stream s, the shared value, q/k weights.
+  auto key_ptr = [&](int l, int s, int c) {
+    return layers.kv[l] + t * (nstreams + 1) * int64_t(dim) + (s0 + s) * int64_t(dim) + i0_of(c);
+  };
+  auto val_ptr = [&](int l, int c) {
+    return layers.kv[l] + t * (nstreams + 1) * int64_t(dim) + nstreams * int64_t(dim) + i0_of(c);
+  };
+  auto w_ptr = [&](const uint16_t *w, int s, int c) { return w + (s0 + s) * int64_t(dim) + i0_of(c); };
+  auto ld = [](const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); };
+
+  // Register copies (kBatch): this layer's operands and the next layer's
+  // key and value.
+  u32x4 key[HC][NCH], qw[HC][NCH], kw[HC][NCH], val[NCH];
+  u32x4 key_next[HC][NCH], val_next[NCH];
+  auto load_kv = [&](int l, u32x4 (&k)[HC][NCH], u32x4 (&v)[NCH]) {
 #pragma unroll
-    for (int e = 0; e < kVec; ++e) {
-      const float xv = x[s][c][e];
-      ssx[s] += xv * xv;
-      ssk[s] += key[e] * key[e];
-      dot[s] += (xv * q[e]) * (key[e] * k[e]);
+    for (int c = 0; c < NCH; ++c)
+      if (i0_of(c) < dim) {
+#pragma unroll
+        for (int s = 0; s < HC; ++s) k[s][c] = ld(key_ptr(l, s, c));
+        v[c] = ld(val_ptr(l, c));
+      }
+  };
+  auto load_weights = [&](int l) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      if (i0_of(c) < dim)
+#pragma unroll
+        for (int s = 0; s < HC; ++s) {
+          qw[s][c] = ld(w_ptr(layers.qw[l], s, c));
+          kw[s][c] = ld(w_ptr(layers.kw[l], s, c));
+        }
+  };
+  // Layer l's operands: from the registers (kBatch) or straight from memory.
+  auto key_of = [&](int l, int s, int c) { return kBatch ? key[s][c] : ld(key_ptr(l, s, c)); };
+  auto qw_of = [&](int l, int s, int c) { return kBatch ? qw[s][c] : ld(w_ptr(layers.qw[l], s, c)); };
+  auto kw_of = [&](int l, int s, int c) { return kBatch ? kw[s][c] : ld(w_ptr(layers.kw[l], s, c)); };
+  auto val_of = [&](int l, int c) { return kBatch ? val[c] : ld(val_ptr(l, c)); };
+
+  // Layer l's partial sums over this thread's slices.
+  auto accumulate = [&](int l) {
+#pragma unroll
+    for (int s = 0; s < HC; ++s) ssx[s] = ssk[s] = dot[s] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (i0_of(c) < dim) {
+#pragma unroll
+        for (int s = 0; s < HC; ++s) {
+          float kf[kVec], q[kVec], k[kVec];
+          bf16x8_to_f32(key_of(l, s, c), kf);
+          bf16x8_to_f32(qw_of(l, s, c), q);
+          bf16x8_to_f32(kw_of(l, s, c), k);
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) {
+            const float xv = x[s][c][e];
+            ssx[s] += xv * xv;
+            ssk[s] += kf[e] * kf[e];
+            dot[s] += (xv * q[e]) * (kf[e] * k[e]);
+          }
+        }
+      }
     }
   };
   // Reduce the sums over the workgroup, derive the hc gates of layer l and
@@ -114,14 +170,11 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(
       const float z = av > 0.f ? mag : (av < 0.f ? -mag : 0.f);
       g[s] = 1.0f / (1.0f + expf(-z));
     }
-    const uint16_t *vt =                           // the shared value
-        layers.kv[l] + t * (nstreams + 1) * int64_t(dim) + nstreams * int64_t(dim);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int i0 = (threadIdx.x + c * kThreads) * kVec;
-      if (i0 < dim) {
+      if (i0_of(c) < dim) {
         float v[kVec];
-        bf16x8_to_f32(*reinterpret_cast<const u32x4 *>(vt + i0), v);
+        bf16x8_to_f32(val_of(l, c), v);
 #pragma unroll
         for (int s = 0; s < HC; ++s)
 #pragma unroll
@@ -130,47 +183,55 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(
     }
   };
 
-  // Layer 0: the streams are loaded and reduced in the same pass.
-#pragma unroll
-  for (int s = 0; s < HC; ++s) ssx[s] = ssk[s] = dot[s] = 0.f;
+  // The streams, then (kBatch) layer 0's operands and layer 1's key and
+  // value.  The scheduling fences keep the three groups in this order: a
+  // wait for the first two then leaves the third in flight.
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const int i0 = (threadIdx.x + c * kThreads) * kVec;
-    if (i0 < dim) {
+    if (i0_of(c) < dim) {
 #pragma unroll
       for (int s = 0; s < HC; ++s) {
-        const f32x4 a = *reinterpret_cast<const f32x4 *>(ht + s * dim + i0);
-        const f32x4 b = *reinterpret_cast<const f32x4 *>(ht + s * dim + i0 + 4);
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(ht + s * dim + i0_of(c));
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(ht + s * dim + i0_of(c) + 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           x[s][c][e] = a[e];
           x[s][c][4 + e] = b[e];
         }
-        accumulate(0, c, s, i0);
       }
     }
   }
+  if constexpr (kBatch) {
+    load_kv(0, key, val);
+    load_weights(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (layers.n > 1) load_kv(1, key_next, val_next);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  accumulate(0);
   finish(0);
   // Later layers read the streams from registers.
   for (int l = 1; l < layers.n; ++l) {
     __syncthreads();                               // every thread is done with red
+    if constexpr (kBatch) {
 #pragma unroll
-    for (int s = 0; s < HC; ++s) ssx[s] = ssk[s] = dot[s] = 0.f;
+      for (int c = 0; c < NCH; ++c) {
+        val[c] = val_next[c];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int i0 = (threadIdx.x + c * kThreads) * kVec;
-      if (i0 < dim) {
-#pragma unroll
-        for (int s = 0; s < HC; ++s) accumulate(l, c, s, i0);
+        for (int s = 0; s < HC; ++s) key[s][c] = key_next[s][c];
       }
+      load_weights(l);
+      __builtin_amdgcn_sched_barrier(0);
+      if (l + 1 < layers.n) load_kv(l + 1, key_next, val_next);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    accumulate(l);
     finish(l);
   }
 
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const int i0 = (threadIdx.x + c * kThreads) * kVec;
-    if (i0 < dim) {
+    if (i0_of(c) < dim) {
 #pragma unroll
       for (int s = 0; s < HC; ++s) {
         f32x4 a, b;
@@ -179,8 +240,8 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(
           a[e] = x[s][c][e];
           b[e] = x[s][c][4 + e];
         }
-        *reinterpret_cast<f32x4 *>(ht + s * dim + i0) = a;
-        *reinterpret_cast<f32x4 *>(ht + s * dim + i0 + 4) = b;
+        *reinterpret_cast<f32x4 *>(ht + s * dim + i0_of(c)) = a;
+        *reinterpret_cast<f32x4 *>(ht + s * dim + i0_of(c) + 4) = b;
       }
     }
   }

@@ -1401,13 +1401,17 @@ def test_projection_at_many_columns(eg, kind, T, cols, N):
         _check_kv_mx(kv.cpu().numpy().view(np.uint16), a_c, a_s, wc, ws)
 
 
-@pytest.mark.parametrize("T,masked", [(100, False), (1500, True)])
-def test_gate_layers_equals_gate_per_layer(eg, T, masked):
+@pytest.mark.parametrize("T,masked,hc,dim", [(100, False, 4, 512), (1500, True, 4, 512),
+                                             (1030, True, 3, 4096), (1100, True, 8, 1024),
+                                             (1024, False, 5, 2056)])
+def test_gate_layers_equals_gate_per_layer(eg, T, masked, hc, dim):
     # One pass for two and three layers against engram_gate per layer, in
     # order, bit for bit (per-stream workgroups below 1024 tokens, per-token
-    # above), and against the oracle's gates in sequence.
+    # above: with the layers' operands loaded in batches where a thread holds
+    # at most 8 slices, at their use for hc = 5, dim = 2056), and against the
+    # oracle's gates in sequence.
     rng = np.random.default_rng(T)
-    hc, dim, eps, clamp, ds = 4, 512, 1e-6, 1e-6, 1 / np.sqrt(512)
+    eps, clamp, ds = 1e-6, 1e-6, 1 / np.sqrt(dim)
     h0 = rng.standard_normal((T, hc, dim)).astype(np.float32)
     mask = (rng.random(T) > 0.2).astype(np.uint8) if masked else None
     for n in (2, 3):
