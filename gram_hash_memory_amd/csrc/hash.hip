@@ -11,7 +11,12 @@
 // arguments: all lanes index them uniformly per layer, so they are read with
 // scalar loads.  Sequence boundaries are searched in an LDS copy of
 // cu_seqlens when it fits, which turns a chain of dependent global loads into
-// one cooperative load.
+// one cooperative load.  Every history entry a thread may need is loaded
+// before the walk that decides which of them count (an earlier dead or
+// foreign position blocks the later ones), so the loads travel together:
+// the positions inside the batch while cu_seqlens comes in, the lookback
+// entries after the search.  All of them lie inside the batch or the
+// sequence's lookback row whatever the walk decides.
 #include "common.hpp"
 
 namespace engram {
@@ -43,16 +48,40 @@ __global__ __launch_bounds__(kThreads) void hash_kernel(
     int32_t *__restrict__ ids) {
   __shared__ int32_t cu_lds[kCuLds];
   const bool cu_in_lds = n_seqs + 1 <= kCuLds;
-  if (cu_in_lds) {
-    for (int i = threadIdx.x; i <= n_seqs; i += kThreads) cu_lds[i] = cu[i];
-    __syncthreads();
-  }
-
   const int32_t cols = (tab.max_ngram - 1) * tab.n_heads;
   const int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-  if (g >= int64_t(T) * cols) return;
-  const int32_t t = int32_t(g / cols), c = int32_t(g % cols);
+  const bool active = g < int64_t(T) * cols;
+  const int32_t t = active ? int32_t(g / cols) : 0, c = active ? int32_t(g % cols) : 0;
   const int order = 2 + c / tab.n_heads;
+
+  // First, with no load waiting on another: this thread's first entry of
+  // the LDS copy of cu_seqlens, then the position itself and the ones
+  // before it in the batch (distance k, clamped at 0; an absent mask or
+  // document array reads stand-in bytes of cids, in bounds and unused).
+  const int32_t cu_first = cu_in_lds && int(threadIdx.x) <= n_seqs ? cu[threadIdx.x] : 0;
+  const uint8_t *mptr = mask ? mask : reinterpret_cast<const uint8_t *>(cids);
+  const int32_t *dptr = doc_ids ? doc_ids : cids;
+  const int32_t tok0 = cids[t], d0 = dptr[t];
+  int32_t tokv[ENGRAM_MAX_NGRAM], dq[ENGRAM_MAX_NGRAM];
+  uint32_t mq[ENGRAM_MAX_NGRAM];
+  bool livev[ENGRAM_MAX_NGRAM];
+#pragma unroll
+  for (int k = 1; k < ENGRAM_MAX_NGRAM; ++k) {
+    const int32_t q = max(t - k, 0);
+    tokv[k] = cids[q];
+    mq[k] = mptr[q];
+    dq[k] = dptr[q];
+  }
+  if (cu_in_lds) {
+    if (int(threadIdx.x) <= n_seqs) cu_lds[threadIdx.x] = cu_first;
+    for (int i = threadIdx.x + kThreads; i <= n_seqs; i += kThreads) cu_lds[i] = cu[i];
+    __syncthreads();
+  }
+  if (!active) return;
+  const int32_t own_doc = doc_ids ? d0 : 1;
+#pragma unroll
+  for (int k = 1; k < ENGRAM_MAX_NGRAM; ++k)
+    livev[k] = k < order && t - k >= 0 && (!mask || mq[k] != 0) && (!doc_ids || dq[k] == own_doc);
 
   // Chunk of t: the last s with cu[s] <= t (empty chunks are skipped over).
   int32_t lo = 0, hi = n_seqs - 1;
@@ -63,36 +92,43 @@ __global__ __launch_bounds__(kThreads) void hash_kernel(
   const int32_t s = lo;
   const int32_t start = max(cu_in_lds ? cu_lds[s] : cu[s], 0);
 
+  // Positions before the chunk come from the sequence's lookback row
+  // (oldest first, entry depth - (start - q)), or are absent.  The row's
+  // entries are loaded at clamped indices, then kept where they count.
+  const bool has_lookback = lookback && depth > 0;
+  const uint8_t *llptr =
+      lookback_live ? lookback_live : reinterpret_cast<const uint8_t *>(lookback);
+  int32_t lb_tok[ENGRAM_MAX_NGRAM];
+  uint32_t lb_live[ENGRAM_MAX_NGRAM];
+  if (has_lookback) {
+#pragma unroll
+    for (int k = 1; k < ENGRAM_MAX_NGRAM; ++k) {
+      const int32_t j = depth - (start - (t - k));
+      const int64_t at = int64_t(s) * depth + min(max(j, 0), depth - 1);
+      lb_tok[k] = lookback[at];
+      lb_live[k] = llptr[at];
+    }
+  }
+#pragma unroll
+  for (int k = 1; k < ENGRAM_MAX_NGRAM; ++k) {
+    if (k < order && t - k < start) {
+      const int32_t j = depth - (start - (t - k));
+      livev[k] = has_lookback && j >= 0 && (!lookback_live || lb_live[k] != 0);
+      tokv[k] = has_lookback ? lb_tok[k] : 0;
+    }
+  }
+
   // History: distance 0 is t itself; walking back, the first position that
   // is absent or not live, and everything before it, reads as pad_id.
   uint64_t hist[ENGRAM_MAX_NGRAM];
-  hist[0] = uint64_t(int64_t(cids[t]));
-  const int32_t own_doc = doc_ids ? doc_ids[t] : 1;
+  hist[0] = uint64_t(int64_t(tok0));
   bool blocked = own_doc == 0;          // a padding position has no history
   const uint64_t pad = uint64_t(int64_t(tab.pad_id));
 #pragma unroll
   for (int k = 1; k < ENGRAM_MAX_NGRAM; ++k) {
     if (k >= order) break;
-    int32_t tokv = tab.pad_id;
-    if (!blocked) {
-      const int32_t q = t - k;
-      bool live;
-      if (q >= start) {
-        live = (!mask || mask[q] != 0) && (!doc_ids || doc_ids[q] == own_doc);
-        tokv = cids[q];
-      } else {
-        const int32_t j = depth - (start - q);   // lookback is oldest first
-        if (!lookback || j < 0) {
-          live = false;
-        } else {
-          const int64_t at = int64_t(s) * depth + j;
-          live = !lookback_live || lookback_live[at] != 0;
-          tokv = lookback[at];
-        }
-      }
-      blocked = !live;
-    }
-    hist[k] = blocked ? pad : uint64_t(int64_t(tokv));
+    blocked = blocked || !livev[k];
+    hist[k] = blocked ? pad : uint64_t(int64_t(tokv[k]));
   }
 
   int32_t *out = ids + int64_t(t) * tab.n_layers * cols + c;

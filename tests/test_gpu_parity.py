@@ -1373,6 +1373,38 @@ def test_hash_at_maximum_sizes(eg):
     assert np.array_equal(ids.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("n_seqs,depth", [(300, 2), (5000, 0), (5000, 3)])
+def test_hash_many_sequences(eg, n_seqs, depth):
+    # Batches of many short sequences (empty ones included): 300 needs more
+    # than one pass to copy cu_seqlens into LDS, 5000 is past the LDS copy and
+    # searches cu_seqlens in global memory; a lookback row with depth 0 is
+    # given but never read.  Bit-exact against the oracle.
+    from oracle.layout import engram_layout, hash_multipliers
+    L, max_ngram, n_heads, V = 2, 4, 2, 5000
+    primes, offsets = engram_layout(L, max_ngram, n_heads, 4099)
+    hp = dict(multipliers=hash_multipliers([1, 14], max_ngram, V), primes=primes,
+              offsets=offsets, max_ngram=max_ngram, n_heads=n_heads, pad_id=7)
+    rng = np.random.default_rng(n_seqs + depth)
+    lens = rng.integers(0, 5, n_seqs)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    cids = rng.integers(0, V, T).astype(np.int32)
+    mask = (rng.random(T) > 0.1).astype(np.uint8)
+    lb = rng.integers(0, V, (n_seqs, max(depth, 1))).astype(np.int32)[:, :depth]
+    lb_live = (rng.random((n_seqs, depth)) > 0.2).astype(np.uint8)
+    want = oracle.hash_ids(cids, cu, hp["multipliers"], primes, offsets, max_ngram, n_heads, 7,
+                           token_mask=mask, lookback=lb if depth else None,
+                           lookback_live=lb_live if depth else None)
+    params = eg.HashParams.from_dict(hp)
+    lb_d = tensor(np.ascontiguousarray(lb) if depth else np.zeros((n_seqs, 1), np.int32), "cuda")
+    tokens = eg.Tokens(tensor(cids, "cuda"), tensor(cu, "cuda"), None, tensor(mask, "cuda"),
+                       lb_d, tensor(lb_live, "cuda") if depth else None)
+    tokens.c.lookback_depth = depth           # depth 0: the row pointer is set, nothing is read
+    ids = torch.empty((T, L, (max_ngram - 1) * n_heads), dtype=torch.int32, device="cuda")
+    eg.engram_hash(params, tokens, ids)
+    assert np.array_equal(ids.cpu().numpy(), want)
+
+
 @pytest.mark.parametrize("kind,T,cols,N", [("q2k", 300, 32, 512), ("mx", 130, 40, 300),
                                            ("mx", 64, 40, 300), ("mx", 50, 64, 200),
                                            ("mx", 64, 68, 200)])
