@@ -232,17 +232,6 @@ __device__ __forceinline__ void load_b_frags(const uint16_t *sb, int frow, int f
   for (int j = 0; j < kNJ; ++j)
     fb[j] = *reinterpret_cast<const bf16x8 *>(sb + swz<BK>(j * 32 + frow, chunk));
 }
-// One k-step: 16 MFMAs (32 cycles of matrix core each), the next step's 8 B
-// fragment reads and kValu VALU ops (the A decode) after each MFMA.
-template <int kValu>
-__device__ __forceinline__ void sched_step_valu() {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    if (r % 2 == 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedValu, kValu, 0);
-  }
-}
 
 }  // namespace wide
 

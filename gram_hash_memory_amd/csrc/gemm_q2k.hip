@@ -507,24 +507,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q2k_exact_kernel(
   const int tiles_m = int(gridDim.x) / split;
   const int tm = int(blockIdx.x) % tiles_m, g = int(blockIdx.x) / tiles_m;
   const int cols = K / ENGRAM_HEAD_DIM;
-  // Thread t checks tile row t: all its ids, then all its blocks' d/dmin
-  // words, each batch in flight at once (an id outside the table, or a row
-  // past M, reads the word past the table: 0).
-  const int row = tm * BM + int(threadIdx.x);
-  const bool row_ok = row < M;
-  const int32_t *id_ptr = ids + int64_t(row_ok ? row : 0) * ids_stride;
+  // The tile's (row, column) pairs in row-major order, thread t taking pairs
+  // t, t + 256, ... (so a wave's id loads are contiguous runs): all the ids,
+  // then all their blocks' d/dmin words, each batch in flight at once (an id
+  // outside the table, or a row past M, reads the word past the table: 0).
   const __amdgpu_buffer_rsrc_t rt = make_rsrc(table, num_rows * ENGRAM_Q2K_ROW_BYTES);
   int32_t idv[ENGRAM_Q2K_FUSED_MAX_COLS];
+  bool pair_ok[ENGRAM_Q2K_FUSED_MAX_COLS];
 #pragma unroll
-  for (int c = 0; c < ENGRAM_Q2K_FUSED_MAX_COLS; ++c) idv[c] = row_ok && c < cols ? id_ptr[c] : -1;
+  for (int i = 0; i < ENGRAM_Q2K_FUSED_MAX_COLS; ++i) {
+    const int pair = i * kThreads + int(threadIdx.x);
+    const int row = tm * BM + pair / max(cols, 1), c = pair % max(cols, 1);
+    pair_ok[i] = i < cols && row < M;
+    idv[i] = pair_ok[i] ? ids[int64_t(row) * ids_stride + c] : -1;
+  }
   uint32_t ddv[ENGRAM_Q2K_FUSED_MAX_COLS];
   int bad = 0;
 #pragma unroll
-  for (int c = 0; c < ENGRAM_Q2K_FUSED_MAX_COLS; ++c) {
-    const bool ok = idv[c] >= 0 && idv[c] < num_rows;
-    bad += row_ok && c < cols && !ok;
-    ddv[c] = __builtin_amdgcn_raw_buffer_load_b32(
-        rt, (ok ? uint32_t(idv[c]) * ENGRAM_Q2K_ROW_BYTES : kNoRow) + 80, 0, 0);
+  for (int i = 0; i < ENGRAM_Q2K_FUSED_MAX_COLS; ++i) {
+    const bool ok = idv[i] >= 0 && idv[i] < num_rows;
+    bad += pair_ok[i] && !ok;
+    ddv[i] = __builtin_amdgcn_raw_buffer_load_b32(
+        rt, (ok ? uint32_t(idv[i]) * ENGRAM_Q2K_ROW_BYTES : kNoRow) + 80, 0, 0);
   }
   if (bad && g == 0 && bad_ids) atomicAdd(bad_ids, bad);
   bool fast = true;
