@@ -704,6 +704,86 @@ def test_forward_kernel_choices_against_oracle(eg, T, max_ngram, n_heads):
     assert err.max() <= 1e-2, err.max()
 
 
+@pytest.mark.parametrize("T,n_seqs,L,depth,docs", [
+    (64, 64, 1, 3, False),      # the decode shape: one token per sequence, 3-token lookback
+    (37, 5, 2, 2, True),        # two layers, documents, a mask, dead lookback entries
+    (1, 1, 2, 0, False),        # one token, no lookback
+    (50, 9000, 1, 3, True),     # mostly empty chunks: cu_seqlens searched in global memory
+])
+def test_forward_at_decode_shapes_matches_stages(eg, T, n_seqs, L, depth, docs):
+    # engram_forward at decode sizes (every layer on the fused Q2_K
+    # weight-streaming projection) against the staged calls, engram_hash ->
+    # engram_project_q2k per layer -> engram_gate_layers, bit for bit, and
+    # against the oracle's forward within the highway bar.
+    from oracle.layout import engram_layout, hash_multipliers
+    max_ngram, n_heads, V, hc, dim = 4, 4, 3000, 2, 256
+    cols = (max_ngram - 1) * n_heads
+    layer_ids = [1, 14][:L]
+    primes, offsets = engram_layout(L, max_ngram, n_heads, 4001)
+    R = int((offsets + primes).max())
+    hp = dict(multipliers=hash_multipliers(layer_ids, max_ngram, V), primes=primes,
+              offsets=offsets, max_ngram=max_ngram, n_heads=n_heads, pad_id=5)
+    rng = np.random.default_rng(T * 7 + n_seqs)
+    lens = np.zeros(n_seqs, dtype=np.int64)
+    if n_seqs > T:                               # T one-token chunks among empty ones
+        lens[rng.choice(n_seqs, T, replace=False)] = 1
+    else:
+        lens[:] = T // n_seqs
+        lens[: T % n_seqs] += 1
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    assert cu[-1] == T
+    cids = rng.integers(0, V, T).astype(np.int32)
+    doc_ids = np.sort(rng.integers(0, 3, T)).astype(np.int32) if docs else None
+    mask = (rng.random(T) > 0.15).astype(np.uint8) if docs else None
+    lb = rng.integers(0, V, (n_seqs, depth)).astype(np.int32) if depth else None
+    lb_live = (rng.random((n_seqs, depth)) > 0.2).astype(np.uint8) if depth else None
+    K, N = cols * 256, (hc + 1) * dim
+    lay_np = []
+    for l in range(L):
+        lay_np.append(dict(
+            fmt="q2k", table=workloads.q2k_table(0, l, R), scales=None,
+            wkv=oracle.bf16_bits(oracle.bf16_round(0.02 * rng.standard_normal((N, K)))),
+            q_weight=oracle.bf16_bits(oracle.bf16_round(1 + 0.1 * rng.standard_normal((hc, dim)))),
+            k_weight=oracle.bf16_bits(oracle.bf16_round(1 + 0.1 * rng.standard_normal((hc, dim))))))
+    h0 = rng.standard_normal((T, hc, dim)).astype(np.float32)
+    eps, clamp, dot_scale = 1e-6, 1e-6, 1 / np.sqrt(dim)
+    params = eg.HashParams.from_dict(hp)
+    opt = lambda a: None if a is None else tensor(a, "cuda")
+    tokens = eg.Tokens(tensor(cids, "cuda"), tensor(cu, "cuda"), opt(doc_ids), opt(mask),
+                       opt(lb), opt(lb_live))
+    dev = [dict((k, tensor(v, "cuda") if isinstance(v, np.ndarray) else v) for k, v in d.items())
+           for d in lay_np]
+    layers = [eg.Layer(eg.ENGRAM_ROWS_Q2K, d["table"], None, d["wkv"], d["q_weight"],
+                       d["k_weight"], hc, dim, cols) for d in dev]
+    g_h = Guarded((T, hc, dim), torch.float32, 0.0)
+    g_h.t.copy_(tensor(h0, "cuda"))
+    nws = eg.engram_workspace_bytes(T, L, cols, hc, dim)
+    g_ws = Guarded((nws,), torch.uint8, 0, pad=1 << 20)
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    eg.engram_forward(params, tokens, layers, g_h.t, hc, dim, eps, clamp, dot_scale, g_ws.t, bad)
+    g_h.check()
+    g_ws.check()
+    # the staged calls
+    ids = torch.empty((T, L, cols), dtype=torch.int32, device="cuda")
+    eg.engram_hash(params, tokens, ids)
+    kvs = []
+    for l, d in enumerate(dev):
+        kv = torch.empty((T, N), dtype=torch.int16, device="cuda")
+        eg.engram_project_q2k(d["table"], R, ids.view(-1)[l * cols:], L * cols, cols, d["wkv"],
+                              kv, T, N)
+        kvs.append(kv)
+    h2 = tensor(h0, "cuda")
+    eg.engram_gate_layers(h2, kvs, [d["q_weight"] for d in dev], [d["k_weight"] for d in dev],
+                          opt(mask), T, hc, dim, eps, clamp, dot_scale)
+    torch.cuda.synchronize()
+    assert bad.item() == 0
+    assert torch.equal(g_h.t.view(torch.int32), h2.view(torch.int32))
+    want = oracle.forward(h0, cids, cu, hp, lay_np, eps, clamp, dot_scale, doc_ids=doc_ids,
+                          token_mask=mask, lookback=lb, lookback_live=lb_live)
+    err = np.abs(g_h.t.cpu().numpy() - want) / np.maximum(1.0, np.abs(want))
+    assert err.max() <= 1e-2, err.max()
+
+
 def test_forward_empty_batch(eg):
     wl = host(0)
     s = wl.spec
