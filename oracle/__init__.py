@@ -15,7 +15,7 @@ where the method stores a value); integers are exact Python integers.
 
 Every function is pinned by tests against hand-worked values, library
 decoders, closed forms or invariants.  The pins cover the oracle's readings
-of the pages and stop there.  Three things stay "parity unpinned" because
+of the pages and stop there.  Two things stay "parity unpinned" because
 neither the released model nor its files are available:
 * whether DeepSeek's own hash combines the n-gram terms by XOR (reading A1);
 * whether real GGUF Q2_K files use the quant interleave of reading A10.
